@@ -1,0 +1,148 @@
+"""CPU oracle for the tiled dense GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
+this package; the library path never imports it.  It shares no code with the
+GPU path.  The arithmetic lives in oracle.c (plain fp64 loops, own decoders);
+this module only marshals numpy arrays through ctypes.
+
+Every function is pinned by tests/test_oracle.py against identities,
+permutations, rank-1 closed forms, exact-integer brute force and NumPy's fp64
+matmul; the decoders and the rounding are pinned exhaustively against
+torch / numpy dtype conversions (tests/test_codecs.py).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "libtg_oracle.so")
+
+FMT = {"f16": 1, "bf16": 2, "e4m3fn": 3}
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile oracle.c (gcc -O2, OpenMP, no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-o", out + ".tmp", src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+class Oracle:
+    """ctypes view of one build of oracle.c (the default build, or a test build)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.tg_oracle_gemm.argtypes = [c_int, i64, i64, i64, vp, i64, i64, vp, i64, i64,
+                                       vp, i64, vp, vp]
+        lib.tg_oracle_gemm.restype = c_int
+        lib.tg_oracle_gemm_fp8_blockscaled.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64,
+                                                       vp, i64, i64, vp, i64, i64, vp, i64, vp, vp]
+        lib.tg_oracle_gemm_fp8_blockscaled.restype = c_int
+        lib.tg_oracle_round.argtypes = [c_int, vp, i64, vp]
+        lib.tg_oracle_round.restype = None
+        lib.tg_oracle_decode.argtypes = [c_int, vp, i64, vp]
+        lib.tg_oracle_decode.restype = None
+        lib.tg_oracle_init()
+        self.lib = lib
+
+    def gemm(self, fmt: str, M: int, N: int, K: int, A: np.ndarray, sam: int, sak: int,
+             B: np.ndarray, sbk: int, sbn: int, rows=None):
+        """fp64 C and S = sum |a||b| for the requested rows of C (all if None).
+
+        A and B are uint16 code buffers (fp16 or bf16) addressed with element
+        strides: A[i,k] = A.flat[i*sam + k*sak], B[k,j] = B.flat[k*sbk + j*sbn].
+        """
+        A = np.ascontiguousarray(A).view(np.uint16)
+        B = np.ascontiguousarray(B).view(np.uint16)
+        rows, nrows = _rows_arg(rows, M)
+        C = np.empty((nrows, N), np.float64)
+        S = np.empty((nrows, N), np.float64)
+        rc = self.lib.tg_oracle_gemm(FMT[fmt], M, N, K, _p(A), sam, sak, _p(B), sbk, sbn,
+                                     _p(rows), nrows, _p(C), _p(S))
+        if rc != 0:
+            raise ValueError("oracle: bad arguments")
+        return C, S
+
+    def gemm_fp8_blockscaled(self, M, N, K, QA, sam, sak, SA, ssam, ssak, QB, sbk, sbn, SB,
+                             ssbn, ssbk, rows=None):
+        """fp64 C and S for the e4m3fn block-scaled product (see oracle.c)."""
+        QA = np.ascontiguousarray(QA).view(np.uint8)
+        QB = np.ascontiguousarray(QB).view(np.uint8)
+        SA = np.ascontiguousarray(SA, dtype=np.float32)
+        SB = np.ascontiguousarray(SB, dtype=np.float32)
+        rows, nrows = _rows_arg(rows, M)
+        C = np.empty((nrows, N), np.float64)
+        S = np.empty((nrows, N), np.float64)
+        rc = self.lib.tg_oracle_gemm_fp8_blockscaled(M, N, K, _p(QA), sam, sak, _p(SA), ssam,
+                                                     ssak, _p(QB), sbk, sbn, _p(SB), ssbn, ssbk,
+                                                     _p(rows), nrows, _p(C), _p(S))
+        if rc != 0:
+            raise ValueError("oracle: bad arguments")
+        return C, S
+
+    def round_to(self, fmt: str, x: np.ndarray) -> np.ndarray:
+        """Round fp64 values to fp16 / bf16 codes, nearest-even (overflow -> inf)."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.empty(x.shape, np.uint16)
+        self.lib.tg_oracle_round(FMT[fmt], _p(x), x.size, _p(out))
+        return out
+
+    def decode(self, fmt: str, codes: np.ndarray) -> np.ndarray:
+        """Exact fp64 values of fp16 / bf16 / e4m3fn codes."""
+        dt = np.uint8 if fmt == "e4m3fn" else np.uint16
+        codes = np.ascontiguousarray(codes).view(dt)
+        out = np.empty(codes.shape, np.float64)
+        self.lib.tg_oracle_decode(FMT[fmt], _p(codes), codes.size, _p(out))
+        return out
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _rows_arg(rows, M):
+    if rows is None:
+        return None, M
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    return rows, rows.size
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB):
+            build()
+        _default = Oracle(_LIB)
+    return _default
+
+
+def gemm(*args, **kw):
+    return default().gemm(*args, **kw)
+
+
+def gemm_fp8_blockscaled(*args, **kw):
+    return default().gemm_fp8_blockscaled(*args, **kw)
+
+
+def round_to(fmt, x):
+    return default().round_to(fmt, x)
+
+
+def decode(fmt, codes):
+    return default().decode(fmt, codes)
+
+
+def bound(fmt_out: str, S: np.ndarray) -> np.ndarray:
+    """Per-element tolerance: 4*2^-8*S for bf16 output, 4*2^-11*S for fp16."""
+    return (4.0 * 2.0 ** -8 if fmt_out == "bf16" else 4.0 * 2.0 ** -11) * S

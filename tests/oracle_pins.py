@@ -1,0 +1,320 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each pin takes an `oracle.Oracle` (the default build, or a build with a
+planted mistake) and raises AssertionError if the oracle disagrees with:
+identity and selection matrices, rank-1 closed forms, exact integer / rational
+brute force, NumPy's fp64 matmul, layout (stride) invariance, the magnitude-sum
+invariants, the fp8 block-scale closed form, and exhaustive decoder tables
+from torch / numpy.  Reference values come from Python integers, fractions,
+numpy / torch dtype conversions -- never from the oracle itself.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import gen
+
+ONE = {"bf16": 0x3F80, "f16": 0x3C00}
+E4M3_ONE = 0x38
+
+
+def lib_decode(fmt: str, codes: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of codes via torch / numpy dtype conversion."""
+    codes = np.ascontiguousarray(codes)
+    if fmt == "f16":
+        return codes.view(np.float16).astype(np.float64)
+    if fmt == "bf16":
+        return torch.from_numpy(codes.view(np.int16).copy()).view(torch.bfloat16) \
+            .to(torch.float32).double().numpy()
+    return torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32) \
+        .double().numpy()
+
+
+def lib_encode(fmt: str, values: np.ndarray) -> np.ndarray:
+    """Codes of values exactly representable in fp16 / bf16 (library casts)."""
+    values = np.asarray(values, dtype=np.float64)
+    if fmt == "f16":
+        return values.astype(np.float16).view(np.uint16)
+    return torch.from_numpy(values.astype(np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def _strides(layout, N, K):
+    return (N, 1) if layout == "kn" else (1, K)
+
+
+def _store_b(bvals_kn: np.ndarray, layout: str) -> np.ndarray:
+    return np.ascontiguousarray(bvals_kn if layout == "kn" else bvals_kn.T)
+
+
+# ---------------------------------------------------------------- 16-bit GEMM
+
+def pin_identity(orc):
+    for fmt in ("bf16", "f16"):
+        for layout in ("kn", "nk"):
+            M = K = 37
+            N = 29
+            A = np.zeros((M, K), np.uint16)
+            A[np.arange(M), np.arange(K)] = ONE[fmt]
+            Bkn = gen.normal((K, N), 21, 1, fmt)
+            sbk, sbn = _strides(layout, N, K)
+            C, S = orc.gemm(fmt, M, N, K, A, K, 1, _store_b(Bkn, layout), sbk, sbn)
+            want = lib_decode(fmt, Bkn)
+            assert np.array_equal(C, want), "identity: C != B"
+            assert np.array_equal(S, np.abs(want)), "identity: S != |B|"
+
+
+def pin_selection(orc):
+    """A[i,k] = 1 iff k = pi(i) (M < K): C[i,:] = B[pi(i),:] exactly."""
+    for fmt in ("bf16", "f16"):
+        for layout in ("kn", "nk"):
+            M, N, K = 23, 31, 41
+            pi = np.random.default_rng(4).permutation(K)[:M]
+            A = np.zeros((M, K), np.uint16)
+            A[np.arange(M), pi] = ONE[fmt]
+            Bkn = gen.uniform_pm1((K, N), 22, 1, fmt)
+            sbk, sbn = _strides(layout, N, K)
+            C, _ = orc.gemm(fmt, M, N, K, A, K, 1, _store_b(Bkn, layout), sbk, sbn)
+            assert np.array_equal(C, lib_decode(fmt, Bkn)[pi, :]), "selection: wrong rows"
+
+
+def pin_rank1(orc):
+    """A = u w^T, B = w v^T with small integers: C = (w.w) u v^T exactly."""
+    rng = np.random.default_rng(5)
+    M, N, K = 19, 13, 27
+    u = rng.integers(-15, 16, M)
+    v = rng.integers(-15, 16, N)
+    w = rng.integers(-15, 16, K)
+    for fmt in ("bf16", "f16"):
+        for layout in ("kn", "nk"):
+            A = lib_encode(fmt, np.outer(u, w))
+            Bkn = lib_encode(fmt, np.outer(w, v))
+            sbk, sbn = _strides(layout, N, K)
+            C, S = orc.gemm(fmt, M, N, K, A, K, 1, _store_b(Bkn, layout), sbk, sbn)
+            ww = int(np.dot(w, w))
+            assert np.array_equal(C, (ww * np.outer(u, v)).astype(np.float64)), "rank-1"
+            assert np.array_equal(S, (ww * np.outer(np.abs(u), np.abs(v))).astype(np.float64))
+
+
+def pin_all_ones(orc):
+    for K in (1, 7, 256, 1000):
+        M, N = 3, 5
+        A = np.full((M, K), ONE["bf16"], np.uint16)
+        B = np.full((K, N), ONE["bf16"], np.uint16)
+        C, S = orc.gemm("bf16", M, N, K, A, K, 1, B, N, 1)
+        assert np.all(C == K) and np.all(S == K), "all-ones: C != K"
+    C, S = orc.gemm("bf16", 2, 3, 0, np.zeros(1, np.uint16), 0, 1, np.zeros(1, np.uint16), 3, 1)
+    assert np.all(C == 0) and np.all(S == 0), "K = 0 must give zeros"
+
+
+def pin_bruteforce_integers(orc):
+    """Tiny integer inputs: C and S equal Python exact-integer sums."""
+    rng = np.random.default_rng(6)
+    for trial in range(40):
+        M, N, K = (int(x) for x in rng.integers(1, 10, 3))
+        fmt = ("bf16", "f16")[trial % 2]
+        layout = ("kn", "nk")[(trial // 2) % 2]
+        a = rng.integers(-8, 9, (M, K))
+        b = rng.integers(-8, 9, (K, N))
+        sbk, sbn = _strides(layout, N, K)
+        C, S = orc.gemm(fmt, M, N, K, lib_encode(fmt, a), K, 1,
+                        _store_b(lib_encode(fmt, b), layout), sbk, sbn)
+        for i in range(M):
+            for j in range(N):
+                c = sum(int(a[i, k]) * int(b[k, j]) for k in range(K))
+                s = sum(abs(int(a[i, k])) * abs(int(b[k, j])) for k in range(K))
+                assert C[i, j] == c and S[i, j] == s, f"brute force ({M},{N},{K}) at {i},{j}"
+
+
+def pin_bruteforce_rationals(orc):
+    """Random (non-integer) codes: C within fp64 summation error of the exact
+    rational sum; the products of two 16-bit values are exact in fp64."""
+    for fmt in ("bf16", "f16"):
+        for layout in ("kn", "nk"):
+            M, N, K = 4, 5, 33
+            A = gen.normal((M, K), 23, 0, fmt)
+            Bkn = gen.normal((K, N), 23, 1, fmt)
+            a, b = lib_decode(fmt, A), lib_decode(fmt, Bkn)
+            sbk, sbn = _strides(layout, N, K)
+            C, S = orc.gemm(fmt, M, N, K, A, K, 1, _store_b(Bkn, layout), sbk, sbn)
+            for i in range(M):
+                for j in range(N):
+                    exact = sum(Fraction(a[i, k]) * Fraction(b[k, j]) for k in range(K))
+                    mag = sum(abs(Fraction(a[i, k]) * Fraction(b[k, j])) for k in range(K))
+                    tol = Fraction(2 * K) * Fraction(2.0 ** -53) * mag
+                    assert abs(Fraction(C[i, j]) - exact) <= tol, "rational brute force"
+                    assert abs(Fraction(S[i, j]) - mag) <= tol
+
+
+def pin_numpy_matmul(orc):
+    """Against NumPy's fp64 matmul (a library routine) on a larger shape."""
+    M, N, K = 70, 45, 300
+    for fmt in ("bf16", "f16"):
+        A = gen.normal((M, K), 24, 0, fmt)
+        Bnk = gen.normal((N, K), 24, 1, fmt)
+        a, bt = lib_decode(fmt, A), lib_decode(fmt, Bnk)
+        C, S = orc.gemm(fmt, M, N, K, A, K, 1, Bnk, 1, K)
+        ref = a @ bt.T
+        sref = np.abs(a) @ np.abs(bt).T
+        assert np.all(np.abs(C - ref) <= 1e-12 * sref), "numpy matmul"
+        assert np.all(np.abs(S - sref) <= 1e-12 * sref), "numpy |a||b|"
+        assert np.all(S >= np.abs(C)), "S >= |C|"
+
+
+def pin_layout_invariance(orc):
+    """The same logical A and B in different storage give identical bits."""
+    M, N, K = 17, 23, 29
+    A = gen.normal((M, K), 25, 0, "bf16")
+    Bkn = gen.normal((K, N), 25, 1, "bf16")
+    C0, S0 = orc.gemm("bf16", M, N, K, A, K, 1, Bkn, N, 1)
+    C1, S1 = orc.gemm("bf16", M, N, K, A, K, 1, np.ascontiguousarray(Bkn.T), 1, K)
+    # A column-major, B K x N with a padded leading stride
+    Acm = np.ascontiguousarray(A.T)
+    Bpad = np.zeros((K, N + 3), np.uint16)
+    Bpad[:, :N] = Bkn
+    C2, S2 = orc.gemm("bf16", M, N, K, Acm, 1, M, Bpad, N + 3, 1)
+    # every other column / element: non-unit strides along both k and j
+    Bwide = np.zeros((K, 2 * N), np.uint16)
+    Bwide[:, ::2] = Bkn
+    Awide = np.zeros((M, 2 * K), np.uint16)
+    Awide[:, ::2] = A
+    C3, S3 = orc.gemm("bf16", M, N, K, Awide, 2 * K, 2, Bwide, 2 * N, 2)
+    for C, S in ((C1, S1), (C2, S2), (C3, S3)):
+        assert np.array_equal(C, C0) and np.array_equal(S, S0), "layout changed the result"
+    # asymmetric check that catches swapped A strides
+    a, b = lib_decode("bf16", A), lib_decode("bf16", Bkn)
+    assert np.all(np.abs(C0 - a @ b) <= 1e-12 * (np.abs(a) @ np.abs(b))), "strided A/B"
+
+
+def pin_row_subset(orc):
+    M, N, K = 40, 11, 13
+    A = gen.normal((M, K), 26, 0, "f16")
+    B = gen.normal((K, N), 26, 1, "f16")
+    Cf, Sf = orc.gemm("f16", M, N, K, A, K, 1, B, N, 1)
+    rows = np.array([39, 0, 17, 5])
+    Cr, Sr = orc.gemm("f16", M, N, K, A, K, 1, B, N, 1, rows=rows)
+    assert np.array_equal(Cr, Cf[rows]) and np.array_equal(Sr, Sf[rows]), "row subset"
+
+
+def pin_nonnegative_s_equals_c(orc):
+    M, N, K = 9, 8, 50
+    A = gen.fill((M, K), gen.DIST_UNIFORM, 27, 0, "f64")
+    B = gen.fill((K, N), gen.DIST_UNIFORM, 27, 1, "f64")
+    A = lib_encode("bf16", np.abs(A))
+    B = lib_encode("bf16", np.abs(B))
+    C, S = orc.gemm("bf16", M, N, K, A, K, 1, B, N, 1)
+    assert np.array_equal(C, S), "S must equal C for non-negative inputs"
+
+
+# ------------------------------------------------------- fp8 block-scaled GEMM
+
+def _dyadic_scales(rng, shape):
+    """Scales m * 2^e with 6-bit m: every product and partial sum stays exact."""
+    m = rng.integers(1, 64, shape).astype(np.float64)
+    e = rng.integers(-8, 3, shape).astype(np.float64)
+    return (m * np.exp2(e)).astype(np.float32)
+
+
+def pin_fp8_unit_codes(orc):
+    """qa = qb = 1: C[i,j] = sum_kb n_kb * sa[i,kb] * sb[j/128,kb] exactly,
+    n_kb = number of k in block kb (128, or the tail length)."""
+    rng = np.random.default_rng(8)
+    M, N, K = 5, 300, 400
+    nkb, nnb = -(-K // 128), -(-N // 128)
+    QA = np.full((M, K), E4M3_ONE, np.uint8)
+    QB = np.full((N, K), E4M3_ONE, np.uint8)
+    SA = _dyadic_scales(rng, (M, nkb))
+    SB = _dyadic_scales(rng, (nnb, nkb))
+    C, S = orc.gemm_fp8_blockscaled(M, N, K, QA, K, 1, SA, nkb, 1, QB, 1, K, SB, nkb, 1)
+    for i in range(M):
+        for j in range(N):
+            want = sum(Fraction(min(128, K - 128 * kb)) * Fraction(float(SA[i, kb]))
+                       * Fraction(float(SB[j // 128, kb])) for kb in range(nkb))
+            assert Fraction(C[i, j]) == want, f"fp8 closed form at {i},{j}"
+            assert Fraction(S[i, j]) == want
+
+
+def pin_fp8_bruteforce(orc):
+    """Random codes and fp32 scales, partial blocks in K and N: C within fp64
+    rounding of the exact rational sum of (code * scale) products."""
+    rng = np.random.default_rng(9)
+    M, N, K = 3, 150, 300
+    nkb, nnb = -(-K // 128), -(-N // 128)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    QA = rng.choice(finite, (M, K)).astype(np.uint8)
+    QB = rng.choice(finite, (N, K)).astype(np.uint8)
+    SA = rng.uniform(0.001, 0.01, (M, nkb)).astype(np.float32)
+    SB = rng.uniform(0.001, 0.01, (nnb, nkb)).astype(np.float32)
+    a, b = lib_decode("e4m3fn", QA), lib_decode("e4m3fn", QB)
+    for layout in ("nk", "kn"):
+        if layout == "nk":
+            C, S = orc.gemm_fp8_blockscaled(M, N, K, QA, K, 1, SA, nkb, 1, QB, 1, K, SB, nkb, 1)
+        else:
+            QBkn = np.ascontiguousarray(QB.T)
+            C, S = orc.gemm_fp8_blockscaled(M, N, K, QA, K, 1, SA, nkb, 1, QBkn, N, 1, SB, nkb, 1)
+        for i in range(M):
+            for j in range(0, N, 7):
+                terms = [Fraction(a[i, k]) * Fraction(float(SA[i, k // 128]))
+                         * Fraction(b[j, k]) * Fraction(float(SB[j // 128, k // 128]))
+                         for k in range(K)]
+                exact = sum(terms)
+                mag = sum(abs(t) for t in terms)
+                tol = Fraction(4 * K) * Fraction(2.0 ** -53) * mag
+                assert abs(Fraction(C[i, j]) - exact) <= tol, f"fp8 brute force {layout} {i},{j}"
+                assert abs(Fraction(S[i, j]) - mag) <= tol
+
+
+def pin_fp8_layout_and_rows(orc):
+    rng = np.random.default_rng(10)
+    M, N, K = 6, 130, 260
+    nkb, nnb = -(-K // 128), -(-N // 128)
+    QA = rng.integers(0, 0x7E, (M, K)).astype(np.uint8)
+    QB = rng.integers(0x80, 0xFE, (N, K)).astype(np.uint8)
+    SA = rng.uniform(0.5, 2, (M, nkb)).astype(np.float32)
+    SB = rng.uniform(0.5, 2, (nnb, nkb)).astype(np.float32)
+    C0, S0 = orc.gemm_fp8_blockscaled(M, N, K, QA, K, 1, SA, nkb, 1, QB, 1, K, SB, nkb, 1)
+    C1, S1 = orc.gemm_fp8_blockscaled(M, N, K, QA, K, 1, SA, nkb, 1, np.ascontiguousarray(QB.T),
+                                      N, 1, SB, nkb, 1)
+    assert np.array_equal(C0, C1) and np.array_equal(S0, S1), "fp8 layout"
+    rows = np.array([5, 2])
+    Cr, _ = orc.gemm_fp8_blockscaled(M, N, K, QA, K, 1, SA, nkb, 1, QB, 1, K, SB, nkb, 1,
+                                     rows=rows)
+    assert np.array_equal(Cr, C0[rows]), "fp8 row subset"
+    assert np.all(C0 <= 0), "positive A codes times negative B codes must give C <= 0"
+
+
+# ------------------------------------------------------------------ codecs
+
+def pin_decoders(orc):
+    codes16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    codes8 = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    for fmt, codes in (("bf16", codes16), ("f16", codes16), ("e4m3fn", codes8)):
+        got, want = orc.decode(fmt, codes), lib_decode(fmt, codes)
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan], want[~nan]), \
+            f"decoder {fmt}"
+
+
+def pin_rounding(orc):
+    """RNE to the output format against library casts (single rounding) and
+    constructed ties."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(50000) * 100.0
+    assert np.array_equal(orc.round_to("f16", x), x.astype(np.float16).view(np.uint16)), "f16"
+    x32 = (rng.standard_normal(50000) * 100.0).astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.round_to("bf16", x32.astype(np.float64)), want), "bf16"
+    # ties: 257 lies halfway between 256 and 258 in bf16 -> 256 (even); 259 -> 260
+    assert orc.round_to("bf16", np.array([257.0, 259.0, -257.0])).tolist() == \
+        lib_encode("bf16", np.array([256.0, 260.0, -256.0])).tolist(), "bf16 ties"
+    assert orc.round_to("f16", np.array([2049.0, 2051.0])).tolist() == \
+        lib_encode("f16", np.array([2048.0, 2052.0])).tolist(), "f16 ties"
+
+
+ALL_PINS = [pin_identity, pin_selection, pin_rank1, pin_all_ones, pin_bruteforce_integers,
+            pin_bruteforce_rationals, pin_numpy_matmul, pin_layout_invariance, pin_row_subset,
+            pin_nonnegative_s_equals_c, pin_fp8_unit_codes, pin_fp8_bruteforce,
+            pin_fp8_layout_and_rows, pin_decoders, pin_rounding]
