@@ -1,0 +1,120 @@
+/*
+ * tg_gemm -- tiled dense matrix multiply C = A * B on AMD Instinct MI355X
+ * (gfx950), with fp32 accumulation.
+ *
+ * The operation is the one the pages build their tiled kernels around:
+ * "Getting to know TileLang", first-GEMM section: fp16 operands, an fp32
+ * fragment accumulator that is cleared, accumulated over the K loop and copied
+ * (with a cast to the output type) into C once; "TileKernels deep dive",
+ * section 3.1: the 128-tile loop computing C tile += A tile * B tile over K;
+ * section 2.1: element addressing through per-dimension strides (stride_am,
+ * stride_ak, stride_bk, stride_bn, stride_cm, stride_cn).  The same pages list
+ * FP8 GEMM and block-scaled GEMM among TileLang's examples ("Getting to know
+ * TileLang", operator-coverage section) and quantise to E4M3 with
+ * scale = amax / 448 ("TileKernels deep dive", sections 4.3 and 7.2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Matrices are addressed with ELEMENT strides:
+ *      A[i,k] = A + i*sam + k*sak      (i < M, k < K)
+ *      B[k,j] = B + k*sbk + j*sbn      (k < K, j < N)
+ *      C[i,j] = C + i*scm + j*scn      (i < M, j < N)
+ *    "B stored N x K" (each column of B contiguous) is sbk = 1, sbn = ldb;
+ *    "B stored K x N row-major" is sbk = ldb, sbn = 1.
+ *  - C = A * B overwrites C (no alpha/beta).  Accumulation is fp32; the result
+ *    is rounded once to the output type, round-to-nearest-even.
+ *  - A, B, C (and scales) are DEVICE pointers owned by the caller; they must
+ *    stay valid until the work enqueued on `stream` has completed.  The library
+ *    allocates no memory and keeps no state between calls.
+ *  - Calls are asynchronous: they enqueue on `stream` (a hipStream_t; NULL is
+ *    the null stream) and return.  They are reentrant.
+ *  - C must not overlap A, B or the scales (undefined behaviour otherwise).
+ *
+ * Errors (tg_status)
+ * ------------------
+ *  - Arguments are validated on the host BEFORE any HIP call; a failed
+ *    validation has no side effects.
+ *      TG_ERR_INVALID_VALUE: a negative dimension or stride, a NULL pointer for
+ *        an operand with a non-empty extent, C rows that overlap (M > 1 and
+ *        scm < N), or an address range that overflows 64-bit arithmetic.
+ *      TG_ERR_UNSUPPORTED: scn != 1 (C must have unit stride along n), or a
+ *        dimension of 2^31 or more.
+ *  - M == 0 or N == 0 is a successful no-op.  K == 0 writes zeros to C.
+ *  - TG_ERR_LAUNCH: the kernel launch failed (hipGetLastError after launch);
+ *    asynchronous faults surface on the stream as usual for HIP.
+ *  - Every valid call is computed: shapes, strides or alignments that the
+ *    tuned kernels do not take go to a general masked kernel.
+ */
+#ifndef TG_GEMM_H
+#define TG_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int tg_status;
+enum {
+  TG_SUCCESS = 0,
+  TG_ERR_INVALID_VALUE = 1,
+  TG_ERR_UNSUPPORTED = 2,
+  TG_ERR_LAUNCH = 3
+};
+
+/* A hipStream_t, passed as an opaque pointer; NULL = the null stream. */
+typedef void* tg_stream_t;
+
+/* Static, NUL-terminated description of a status code. */
+const char* tg_status_string(tg_status s);
+
+/* C = A * B with IEEE fp16 (binary16) A, B and C, fp32 accumulation.
+ * The first-GEMM listing of "Getting to know TileLang" (fp16 in, float32
+ * accumulator, fp16 out). */
+tg_status tg_gemm_f16(int64_t M, int64_t N, int64_t K,
+                      const void* A, int64_t sam, int64_t sak,
+                      const void* B, int64_t sbk, int64_t sbn,
+                      void* C, int64_t scm, int64_t scn, tg_stream_t stream);
+
+/* C = A * B with bfloat16 A, B and C, fp32 accumulation.  Same contract as
+ * tg_gemm_f16; bf16 is the type of the 4096 x 7168 x 16384 GEMM reported for
+ * the Ascend release in "Getting to know TileLang" (six-piece section). */
+tg_status tg_gemm_bf16(int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t sam, int64_t sak,
+                       const void* B, int64_t sbk, int64_t sbn,
+                       void* C, int64_t scm, int64_t scn, tg_stream_t stream);
+
+/* Block-scaled fp8 product with bfloat16 output:
+ *   C[i,j] = sum_k (e4m3(A[i,k]) * SA[i, k/128]) * (e4m3(B[k,j]) * SB[j/128, k/128])
+ * A and B hold OCP E4M3FN codes (1 byte; bias 7, max 448, no infinities),
+ * the format of "TileKernels deep dive" section 4.3.  Scales are fp32, one per
+ * 1 x 128 slice of each A row and one per 128 x 128 block of B (a block-scaled
+ * GEMM as listed in "Getting to know TileLang", operator-coverage section),
+ * addressed with element strides:
+ *   SA[i, kb]  = SA + i*ssam + kb*ssak      (kb < ceil(K/128))
+ *   SB[jb, kb] = SB + jb*ssbn + kb*ssbk     (jb < ceil(N/128))
+ * A trailing partial block (K or N not a multiple of 128) has its own scale.
+ * Within each 128-wide k block the code products are summed in fp32 and the
+ * block sum is scaled by SA * SB into the fp32 accumulator; C is rounded once
+ * to bf16 (nearest-even).  Errors as above; SA / SB are checked like A / B. */
+tg_status tg_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
+                                  const void* A, int64_t sam, int64_t sak,
+                                  const float* SA, int64_t ssam, int64_t ssak,
+                                  const void* B, int64_t sbk, int64_t sbn,
+                                  const float* SB, int64_t ssbn, int64_t ssbk,
+                                  void* C, int64_t scm, int64_t scn, tg_stream_t stream);
+
+/* Name of the kernel a call with these arguments would launch ("none" for a
+ * no-op, NULL if the arguments are invalid); nothing is launched.  op: 0 =
+ * tg_gemm_f16, 1 = tg_gemm_bf16, 2 = tg_gemm_fp8_blockscaled (the scale
+ * arguments do not affect the choice).  For tests and benchmarks. */
+const char* tg_gemm_plan(int op, int64_t M, int64_t N, int64_t K,
+                         const void* A, int64_t sam, int64_t sak,
+                         const void* B, int64_t sbk, int64_t sbn,
+                         void* C, int64_t scm, int64_t scn);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TG_GEMM_H */

@@ -1,0 +1,119 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every function
+include/tg_gemm.h declares, and rejects invalid arguments on the host before
+any HIP call (so no GPU is needed here).  Valid calls are never made on the
+CPU; the parity tests make them on the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_tiled_gemm_03_amd as tg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tg_gemm.h")
+
+# Distinct fake device addresses: validation must reject before touching them.
+PA, PB, PC, PS = 0x10000, 0x20000, 0x30000, 0x40000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tg.ensure_built()
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(tg_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(tg.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), f"{name} not exported"
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for code, tag in ((0, "TG_SUCCESS"), (1, "TG_ERR_INVALID_VALUE"), (2, "TG_ERR_UNSUPPORTED"),
+                      (3, "TG_ERR_LAUNCH")):
+        assert tg.tg_status_string(code).startswith(tag)
+    assert "unknown" in tg.tg_status_string(99)
+
+
+def _call16(fn, M=8, N=8, K=8, A=PA, sam=8, sak=1, B=PB, sbk=8, sbn=1, C=PC, scm=8, scn=1):
+    return fn(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, None)
+
+
+INVALID16 = [
+    dict(M=-1), dict(N=-2), dict(K=-3),
+    dict(sam=-1), dict(sak=-1), dict(sbk=-1), dict(sbn=-1), dict(scm=-1), dict(scn=-1),
+    dict(A=0), dict(B=0), dict(C=0),
+    dict(scm=7),                                   # rows of C overlap
+    dict(M=2, sam=1 << 62, K=8, sak=1 << 62),      # A extent overflows int64
+    dict(N=3, sbn=1 << 62),                        # B extent overflows
+    dict(M=1 << 40, scm=1 << 40),                  # C extent overflows
+]
+
+
+@pytest.mark.parametrize("kw", INVALID16, ids=[str(k) for k in INVALID16])
+@pytest.mark.parametrize("name", ["tg_gemm_f16", "tg_gemm_bf16"])
+def test_invalid_16bit(lib, name, kw):
+    assert _call16(getattr(lib, name), **kw) == tg.TG_ERR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("kw", [dict(scn=2), dict(scn=0), dict(M=1 << 31, scm=8),
+                                dict(K=1 << 31, sak=1, sbk=8)])
+def test_unsupported_16bit(lib, kw):
+    assert _call16(lib.tg_gemm_bf16, **kw) == tg.TG_ERR_UNSUPPORTED
+
+
+def test_empty_calls_are_noops(lib):
+    # M == 0 or N == 0: success without any HIP call (pointers may be NULL)
+    for kw in (dict(M=0), dict(N=0), dict(M=0, A=0, B=0, C=0), dict(N=0, C=0, scm=0)):
+        assert _call16(lib.tg_gemm_bf16, **kw) == tg.TG_SUCCESS
+        assert _call16(lib.tg_gemm_f16, **kw) == tg.TG_SUCCESS
+
+
+def test_k_zero_needs_no_operands(lib):
+    # K == 0 only writes C, so NULL A/B pass validation (checked via the plan)
+    assert tg.tg_gemm_plan(tg.OP_BF16, 8, 8, 0, 0, 0, 0, 0, 0, 0, PC, 8, 1) is not None
+    assert tg.tg_gemm_plan(tg.OP_BF16, 8, 8, 0, 0, 0, 0, 0, 0, 0, 0, 8, 1) is None
+
+
+def _call8(lib, M=8, N=8, K=256, A=PA, sam=256, sak=1, SA=PS, ssam=2, ssak=1, B=PB, sbk=1,
+           sbn=256, SB=PS, ssbn=2, ssbk=1, C=PC, scm=8, scn=1):
+    return lib.tg_gemm_fp8_blockscaled(M, N, K, A, sam, sak, SA, ssam, ssak, B, sbk, sbn, SB,
+                                       ssbn, ssbk, C, scm, scn, None)
+
+
+INVALID8 = [dict(M=-1), dict(K=-1), dict(ssam=-1), dict(ssak=-1), dict(ssbn=-1), dict(ssbk=-1),
+            dict(SA=0), dict(SB=0), dict(A=0), dict(B=0), dict(C=0), dict(scm=3),
+            dict(M=3, ssam=1 << 62)]
+
+
+@pytest.mark.parametrize("kw", INVALID8, ids=[str(k) for k in INVALID8])
+def test_invalid_fp8(lib, kw):
+    assert _call8(lib, **kw) == tg.TG_ERR_INVALID_VALUE
+
+
+def test_fp8_unsupported_and_noop(lib):
+    assert _call8(lib, scn=4) == tg.TG_ERR_UNSUPPORTED
+    assert _call8(lib, M=0, SA=0, SB=0, A=0, B=0, C=0) == tg.TG_SUCCESS
+
+
+def test_python_wrapper_raises(lib):
+    with pytest.raises(tg.TgError) as e:
+        tg.tg_gemm_bf16(-1, 8, 8, PA, 8, 1, PB, 8, 1, PC, 8, 1, 0)
+    assert e.value.status == tg.TG_ERR_INVALID_VALUE
+
+
+def test_plan_names(lib):
+    plan = lambda *a: tg.tg_gemm_plan(*a)  # noqa: E731
+    assert plan(tg.OP_BF16, 0, 8, 8, PA, 8, 1, PB, 8, 1, PC, 8, 1) == "none"
+    assert plan(tg.OP_BF16, -1, 8, 8, PA, 8, 1, PB, 8, 1, PC, 8, 1) is None
+    assert plan(7, 8, 8, 8, PA, 8, 1, PB, 8, 1, PC, 8, 1) is None
+    # a ragged, odd-strided call must go to the general kernel
+    assert plan(tg.OP_F16, 13, 7, 5, PA + 2, 5, 1, PB, 1, 5, PC, 7, 1).startswith("generic")
+    assert plan(tg.OP_FP8, 13, 7, 5, PA + 1, 5, 1, PB, 1, 5, PC, 7, 1).startswith("generic")

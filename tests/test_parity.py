@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle.
+
+Two acceptance modes, element by element:
+  bound mode      |C_gpu - C_ref| <= 4*2^-8 * sum_k |a||b|  (bf16 output),
+                                    4*2^-11 * sum_k |a||b| (fp16 output);
+  bit-exact mode  integer inputs with K*r^2 <= 2^24, so every fp32 partial sum
+                  is exact: C_gpu must equal round-to-nearest-even(C_ref).
+Small cases span several tiles and ragged tails and are checked in full; the
+five workloads run at their real sizes in the launch configuration the
+benchmark times, checked on sampled rows (and fully through a selection
+matrix, whose product is known without the oracle).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gen import configs
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+FULL = os.environ.get("TG_FULL_TEST") == "1"
+
+
+@pytest.fixture(autouse=True)
+def _lib(gpu_lib):
+    return gpu_lib
+
+
+# ------------------------------------------------------------ small shapes
+
+SHAPES = [(1, 1, 1), (13, 7, 5), (64, 64, 64), (65, 129, 33), (128, 256, 512), (200, 300, 170),
+          (256, 256, 256), (1, 257, 1000), (300, 1, 77), (5, 3, 0), (257, 255, 4100)]
+
+
+def _layout_args(fmt, M, N, K, layout, seed, int_r=None):
+    """Device operands for a storage layout; returns (A, sam, sak, B, sbk, sbn,
+    a_host_view, b_host_view) where the host views give A[i,k] and B[k,j]
+    through (flat array, strides) for the oracle."""
+    draw = (lambda shape, stream: gen.integers(shape, seed, stream, int_r, fmt)) if int_r \
+        else (lambda shape, stream: gen.normal(shape, seed, stream, fmt))
+    if layout == "nk":                  # A row-major, B stored N x K
+        A, B = draw((M, K), 0), draw((N, K), 1)
+        return A, K, 1, B, 1, K
+    if layout == "kn":                  # A row-major, B stored K x N
+        A, B = draw((M, K), 0), draw((K, N), 1)
+        return A, K, 1, B, N, 1
+    if layout == "padded":              # leading dimensions padded by 24 elements
+        A = np.zeros((M, K + 24), np.uint16)
+        A[:, :K] = draw((M, K), 0)
+        B = np.zeros((N, K + 24), np.uint16)
+        B[:, :K] = draw((N, K), 1)
+        return A, K + 24, 1, B, 1, K + 24
+    if layout == "colmajor":            # A stored K x M (A^T row-major), B K x N
+        A, B = draw((K, M), 0), draw((K, N), 1)
+        return A, 1, M, B, N, 1
+    raise ValueError(layout)
+
+
+def _check16(fmt, M, N, K, layout, seed, int_r=None, scm=None):
+    A, sam, sak, B, sbk, sbn = _layout_args(fmt, M, N, K, layout, seed, int_r)
+    H.log(f"gemm {fmt} M={M} N={N} K={K} layout={layout} int_r={int_r} scm={scm}")
+    c, plan = H.run16(fmt, M, N, K, H.dev(A), sam, sak, H.dev(B), sbk, sbn, scm=scm)
+    C_ref, S = oracle.gemm(fmt, M, N, K, A, sam, sak, B, sbk, sbn)
+    what = f"{fmt} {M}x{N}x{K} {layout} [{plan}]"
+    if int_r:
+        H.assert_bit_exact(fmt, c, C_ref, what)
+    else:
+        H.assert_within_bound(fmt, c, C_ref, S, what)
+    return plan
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
+@pytest.mark.parametrize("layout", ["nk", "kn", "padded", "colmajor"])
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_small_bound(fmt, layout, shape):
+    M, N, K = shape
+    _check16(fmt, M, N, K, layout, seed=100 + M + N + K)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_small_bit_exact(fmt, layout, shape):
+    M, N, K = shape
+    # K*r^2 <= 2^24 keeps every fp32 partial sum exact; fp16 output also keeps
+    # typical sums below its 65504 maximum
+    r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / max(K, 1)))))
+    _check16(fmt, M, N, K, layout, seed=200 + M + N + K, int_r=r)
+
+
+def test_padded_c_rows():
+    _check16("bf16", 100, 90, 64, "nk", seed=7, scm=96)
+    _check16("f16", 100, 90, 64, "kn", seed=8, scm=130)
+
+
+def test_rne_ties_bf16():
+    """Sums that are exact ties between bf16 neighbours round to even:
+    257 -> 256, 259 -> 260, 261 -> 260, 263 -> 264, -257 -> -256."""
+    M, N, K = 64, 64, 64
+    a = np.zeros((M, K))
+    a[:, 0] = 1.0
+    a[:, 1] = 1.0
+    b = np.zeros((K, N))
+    b[0, :] = 256.0
+    b[1, :] = np.resize([1.0, 3.0, 5.0, 7.0, -513.0], N)
+    A = gen.round_bf16(a)
+    B = gen.round_bf16(b)
+    c, plan = H.run16("bf16", M, N, K, H.dev(A), K, 1, H.dev(B), N, 1)
+    want = gen.round_bf16(np.resize([256.0, 260.0, 260.0, 264.0, -256.0], N)[None, :].repeat(M, 0))
+    assert np.array_equal(c, want), plan
+
+
+# --------------------------------------------------------------- workloads
+
+def _wl_rows(w):
+    if FULL or w.check_rows == 0 and w.M * w.N * w.K <= 2 ** 34:
+        return None
+    return gen.sample_rows(w.M, w.check_rows or 128, w.seed)
+
+
+def _run_workload16(w, d):
+    A, B = H.dev(d["A"]), H.dev(d["B"])
+    H.log(f"workload {w.name}: {w.M}x{w.N}x{w.K} layout={d['layout']}")
+    return H.run16(w.dtype, w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
+
+
+def _oracle16(w, d, rows):
+    return oracle.gemm(w.dtype, w.M, w.N, w.K, d["A"], w.K, 1, d["B"], d["sbk"], d["sbn"],
+                       rows=rows)
+
+
+WL16 = [k for k in configs.ORDER if configs.WORKLOADS[k].dtype != "fp8"]
+
+
+@pytest.mark.parametrize("name", WL16)
+def test_workload_bound(name):
+    w = configs.WORKLOADS[name]
+    d = configs.make_inputs(w)
+    c, plan = _run_workload16(w, d)
+    rows = _wl_rows(w)
+    C_ref, S = _oracle16(w, d, rows)
+    H.assert_within_bound(w.dtype, c if rows is None else c[rows], C_ref, S, f"{name} [{plan}]")
+
+
+@pytest.mark.parametrize("name", WL16)
+def test_workload_bit_exact(name):
+    w = configs.WORKLOADS[name]
+    r = int(math.sqrt(2 ** 24 / w.K))
+    if w.dtype == "f16":
+        r = min(r, 16)
+    d = configs.make_inputs(w, int_r=r)
+    c, plan = _run_workload16(w, d)
+    rows = _wl_rows(w)
+    C_ref, _ = _oracle16(w, d, rows)
+    H.assert_bit_exact(w.dtype, c if rows is None else c[rows], C_ref, f"{name} int r={r} [{plan}]")
+
+
+@pytest.mark.parametrize("name", ["bf16_4096x7168x16384", "bf16_4096", "bf16_skinny_64x7168x7168"])
+def test_workload_selection_full(name):
+    """A[i,k] = 1 iff k = pi(i): every element of C must equal B[pi(i), j]."""
+    w = configs.WORKLOADS[name]
+    d = configs.make_inputs(w)
+    pi = np.random.default_rng(w.seed).permutation(w.K)[: w.M]
+    A = np.zeros((w.M, w.K), np.uint16)
+    A[np.arange(w.M), pi] = 0x3F80
+    H.log(f"selection {name}")
+    c, plan = H.run16(w.dtype, w.M, w.N, w.K, H.dev(A), w.K, 1, H.dev(d["B"]), d["sbk"], d["sbn"])
+    Bkn = d["B"] if d["layout"] == "kn" else d["B"].T
+    assert np.array_equal(c, Bkn[pi, :]), f"{name} selection [{plan}]"
+
+
+def test_workload_deterministic():
+    w = configs.WORKLOADS["bf16_4096x7168x16384"]
+    d = configs.make_inputs(w)
+    A, B = H.dev(d["A"]), H.dev(d["B"])
+    H.log("determinism bf16_4096x7168x16384")
+    c1, _ = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
+    c2, _ = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
+    assert np.array_equal(c1, c2)
+
+
+# ----------------------------------------------------------------- fp8
+
+def _fp8_inputs(M, N, K, seed, layout="nk", int_r=None, pow2_scales=False):
+    w = configs.Workload("t", "fp8", M, N, K, layout, "normal", seed, 0)
+    d = configs.make_inputs(w, int_r=int_r)
+    if pow2_scales:
+        rng = np.random.default_rng(seed)
+        d["SA"] = np.exp2(rng.integers(-2, 3, d["SA"].shape)).astype(np.float32)
+        d["SB"] = np.exp2(rng.integers(-2, 3, d["SB"].shape)).astype(np.float32)
+    return d
+
+
+def _check_fp8(M, N, K, d, rows=None, exact=False, what=""):
+    nkb = d["SA"].shape[1]
+    A, B, SA, SB = H.dev(d["A"]), H.dev(d["B"]), H.dev(d["SA"]), H.dev(d["SB"])
+    H.log(f"fp8 {what} M={M} N={N} K={K} layout={d['layout']}")
+    c, plan = H.run_fp8(M, N, K, A, K, 1, SA, nkb, 1, B, d["sbk"], d["sbn"], SB, nkb, 1)
+    C_ref, S = oracle.gemm_fp8_blockscaled(M, N, K, d["A"], K, 1, d["SA"], nkb, 1, d["B"],
+                                           d["sbk"], d["sbn"], d["SB"], nkb, 1, rows=rows)
+    cc = c if rows is None else c[rows]
+    if exact:
+        H.assert_bit_exact("bf16", cc, C_ref, f"fp8 {what} [{plan}]")
+    else:
+        H.assert_within_bound("bf16", cc, C_ref, S, f"fp8 {what} [{plan}]")
+    return plan
+
+
+FP8_SHAPES = [(1, 1, 1), (64, 64, 128), (13, 200, 300), (130, 129, 257), (256, 256, 1024),
+              (512, 384, 640), (5, 3, 0)]
+
+
+@pytest.mark.parametrize("shape", FP8_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in FP8_SHAPES])
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+def test_fp8_small(layout, shape):
+    M, N, K = shape
+    _check_fp8(M, N, K, _fp8_inputs(M, N, K, 300 + M + K, layout), what="bound")
+    _check_fp8(M, N, K, _fp8_inputs(M, N, K, 400 + M + K, layout, int_r=16), exact=True,
+               what="int unit scales")
+    _check_fp8(M, N, K, _fp8_inputs(M, N, K, 500 + M + K, layout, int_r=4, pow2_scales=True),
+               exact=True, what="int pow2 scales")
+
+
+def test_fp8_workload_bound():
+    w = configs.WORKLOADS["fp8_4096x7168x16384"]
+    d = configs.make_inputs(w)
+    _check_fp8(w.M, w.N, w.K, d, rows=_wl_rows(w), what=w.name)
+
+
+def test_fp8_workload_bit_exact():
+    w = configs.WORKLOADS["fp8_4096x7168x16384"]
+    d = configs.make_inputs(w, int_r=16)
+    _check_fp8(w.M, w.N, w.K, d, rows=_wl_rows(w), exact=True, what=w.name + " int")
