@@ -149,7 +149,8 @@ const char* tg_gemm_plan(int op, int64_t M, int64_t N, int64_t K, const void* A,
   if (tg::validate(c) != TG_SUCCESS) return nullptr;
   if (M == 0 || N == 0) return "none";
   const tg::Variant* v = tg::select(c);
-  return v ? v->name : nullptr;
+  if (v == nullptr) return nullptr;
+  return v->plan_name ? v->plan_name(c.a) : v->name;
 }
 
 }  // extern "C"

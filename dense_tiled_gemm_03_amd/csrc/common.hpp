@@ -29,6 +29,8 @@ struct Variant {
   const char* name;
   bool (*accepts)(Op op, const GemmArgs& a);
   hipError_t (*launch)(Op op, const GemmArgs& a, hipStream_t s);
+  // Name of the instantiation a call would run (tile shape); NULL: `name`.
+  const char* (*plan_name)(const GemmArgs& a);
 };
 
 // Defined by each kernel source file (host functions; see the tables in api.cpp).

@@ -138,11 +138,11 @@ hipError_t launch_fp8(Op, const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 const Variant* variant_generic16() {
-  static const Variant v = {"generic16_64x64", accepts_any, launch16};
+  static const Variant v = {"generic16_64x64", accepts_any, launch16, nullptr};
   return &v;
 }
 const Variant* variant_generic_fp8() {
-  static const Variant v = {"generic_fp8_64x64", accepts_any, launch_fp8};
+  static const Variant v = {"generic_fp8_64x64", accepts_any, launch_fp8, nullptr};
   return &v;
 }
 

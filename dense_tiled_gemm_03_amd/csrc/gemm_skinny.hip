@@ -6,7 +6,7 @@ bool accepts(Op, const GemmArgs&) { return false; }
 hipError_t launch(Op, const GemmArgs&, hipStream_t) { return hipErrorInvalidValue; }
 }  // namespace
 const Variant* variant_skinny16() {
-  static const Variant v = {"skinny", accepts, launch};
+  static const Variant v = {"skinny", accepts, launch, nullptr};
   return &v;
 }
 }  // namespace tg

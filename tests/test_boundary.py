@@ -117,3 +117,24 @@ def test_plan_names(lib):
     # a ragged, odd-strided call must go to the general kernel
     assert plan(tg.OP_F16, 13, 7, 5, PA + 2, 5, 1, PB, 1, 5, PC, 7, 1).startswith("generic")
     assert plan(tg.OP_FP8, 13, 7, 5, PA + 1, 5, 1, PB, 1, 5, PC, 7, 1).startswith("generic")
+
+
+# The kernel each benchmark workload is planned onto (host-side choice; no
+# launch).  A silent fallback to the general kernel fails here.
+EXPECTED_PLANS = {
+    "fp16_256": "generic16_64x64",
+    "bf16_4096": "generic16_64x64",
+    "bf16_4096x7168x16384": "tile_nt_256x224",
+    "bf16_skinny_64x7168x7168": "tile_nt_256x224",
+    "fp8_4096x7168x16384": "generic_fp8_64x64",
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXPECTED_PLANS))
+def test_workload_plans(lib, name):
+    from gen import configs
+    w = configs.WORKLOADS[name]
+    sbk, sbn = configs.b_strides(w.b_layout, w.N, w.K)
+    op = {"f16": tg.OP_F16, "bf16": tg.OP_BF16, "fp8": tg.OP_FP8}[w.dtype]
+    got = tg.tg_gemm_plan(op, w.M, w.N, w.K, PA, w.K, 1, PB, sbk, sbn, PC, w.N, 1)
+    assert got == EXPECTED_PLANS[name]

@@ -239,3 +239,34 @@ def test_fp8_workload_bit_exact():
     w = configs.WORKLOADS["fp8_4096x7168x16384"]
     d = configs.make_inputs(w, int_r=16)
     _check_fp8(w.M, w.N, w.K, d, rows=_wl_rows(w), exact=True, what=w.name + " int")
+
+
+# ------------------------------------------------------- tuned tile kernels
+
+# (M, N, K, expected plan): ragged edges in M, N and K (K a multiple of 8 but
+# not of the 64-wide slice), one or both tile shapes of the N x K kernel.
+TILE_CASES = [
+    (300, 500, 136, "tile_nt_256x224"),
+    (4000, 4000, 136, "tile_nt_256x256"),
+    (513, 449, 72, "tile_nt_256x224"),
+    (256, 224, 64, "tile_nt_256x224"),
+    (1, 1, 8, "tile_nt_256x224"),
+]
+
+
+@pytest.mark.parametrize("case", TILE_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in TILE_CASES])
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_tile_nt_ragged(fmt, case):
+    M, N, K, want = case
+    plan = _check16(fmt, M, N, K, "nk", seed=600 + M + N + K)
+    assert plan == want
+    r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
+    plan = _check16(fmt, M, N, K, "nk", seed=700 + M + N + K, int_r=r)
+    assert plan == want
+
+
+def test_tile_nt_padded_leading_dims():
+    """Leading dimensions padded to multiples of 8 (not of the tile)."""
+    M, N, K = 520, 460, 200
+    plan = _check16("bf16", M, N, K, "padded", seed=31)
+    assert plan.startswith("tile_nt"), plan
