@@ -250,7 +250,7 @@ TILE_CASES = [
     (4000, 4000, 136, "tile_nt_256x256"),
     (513, 449, 72, "tile_nt_256x224"),
     (256, 224, 64, "tile_nt_256x224"),
-    (1, 1, 8, "tile_nt_256x224"),
+    (65, 1, 8, "tile_nt_256x224"),
 ]
 
 
@@ -270,3 +270,25 @@ def test_tile_nt_padded_leading_dims():
     M, N, K = 520, 460, 200
     plan = _check16("bf16", M, N, K, "padded", seed=31)
     assert plan.startswith("tile_nt"), plan
+
+
+# ------------------------------------------------------------ skinny kernel
+
+SKINNY_CASES = [(1, 100, 64), (17, 300, 200), (64, 64, 8), (64, 33, 1000), (40, 7168, 1024),
+                (63, 95, 4104)]
+
+
+@pytest.mark.parametrize("case", SKINNY_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SKINNY_CASES])
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_skinny(fmt, case):
+    M, N, K = case
+    plan = _check16(fmt, M, N, K, "nk", seed=800 + M + N + K)
+    assert plan == "skinny_64x32", plan
+    r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
+    plan = _check16(fmt, M, N, K, "nk", seed=900 + M + N + K, int_r=r)
+    assert plan == "skinny_64x32", plan
+
+
+def test_skinny_padded():
+    plan = _check16("bf16", 50, 70, 136, "padded", seed=41)
+    assert plan == "skinny_64x32", plan
