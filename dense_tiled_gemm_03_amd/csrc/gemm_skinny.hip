@@ -38,8 +38,15 @@ constexpr int SLICE_BYTES = (SM + SN) * ROWB;  // 12 KiB
 constexpr int A_LD = SM / 8, B_LD = SN / 8;    // 1 KiB loads per slice
 constexpr int NLD = A_LD + B_LD;               // 12
 
+// Raw buffer descriptor over [base, base + bytes).  The fields go through
+// readfirstlane: they are wave-uniform, and saying so keeps the descriptor in
+// scalar registers (otherwise every load can become a per-lane waterfall).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* q = reinterpret_cast<void*>((uint64_t)hi << 32 | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
                                            0x00020000);
 }
 

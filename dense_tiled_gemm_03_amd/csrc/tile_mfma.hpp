@@ -1,0 +1,381 @@
+#pragma once
+// The tuned fp16 / bf16 tile kernel shared by the two operand layouts it
+// serves (A row-major M x K, sak = 1):
+//   B stored N x K (sbk = 1): the layout of the 4096 x 7168 x 16384 BF16
+//     GEMM reported for the Ascend release in "Getting to know TileLang"
+//     (six-piece section);
+//   B stored K x N (sbn = 1): the row-major B of the first-GEMM listing of
+//     "Getting to know TileLang".
+//
+// The structure is the tile loop of "TileKernels deep dive" section 3.1 and
+// the first-GEMM listing of "Getting to know TileLang" (one output tile per
+// workgroup, operand tiles staged in on-chip memory per K slice with a
+// multi-stage pipeline, an fp32 accumulator copied to C once with a cast),
+// laid out for gfx950:
+//  - workgroup tile BM x BN (256 x 224 or 256 x 256), 4 waves in a 2 x 2
+//    grid, each wave owning a (BM/2) x (BN/2) block of fp32 accumulators in
+//    registers: 128 x 112 with 16x16x32 MFMAs, 128 x 128 with 32x32x16;
+//  - K slice of 64: one LDS row is 128 bytes (eight 16-byte chunks); tiles
+//    go HBM/L2 -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging);
+//    two LDS stages, the next slice's loads in flight while the current one
+//    is multiplied;
+//  - LDS chunk swizzle: chunk c of row r sits at chunk position
+//    c ^ ((r >> 1) & 7); with it the ds_read_b128 patterns of both MFMA
+//    shapes (rows l % 16 or l % 32, chunks by lane group) are free of bank
+//    conflicts (measured with the LDS bank-conflict counter on gfx950; the
+//    plain c ^ (r & 7) conflicts for one shape, c ^ (r & 7) ^ ((r >> 3) & 1)
+//    for the other);
+//  - each MFMA sub-step's fragments are read from LDS while the previous
+//    sub-step's MFMAs run, one read issued after each MFMA (a wave can have
+//    at most 15 LDS reads outstanding, and LDS latency under load is a few
+//    hundred cycles, so reads are spread over the MFMA stream);
+//  - edges: the buffer descriptor of each operand tile ends at the last valid
+//    element, so rows past M (or N) read as zero; chunks past K get an
+//    out-of-range offset and read as zero; the epilogue masks the stores;
+//  - tile order: workgroups the hardware places on one XCD (blockIdx % 8)
+//    get consecutive tile ids, walked in groups of GM M-tiles so concurrent
+//    tiles on one XCD share A rows and B columns in that XCD's L2.
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace tg {
+namespace tile {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int V> using Int = std::integral_constant<int, V>;
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // past every descriptor's range
+constexpr int kXcds = 8;
+
+// MFMA shapes.  A fragment is DIM rows x KSTEP k of one operand; lane l
+// supplies row (l % DIM) and the 16-byte chunk (l / DIM) of the sub-step's
+// KSTEP-wide k range.  Accumulator element v of lane l is output row
+// out_row(l, v), column l % DIM of the DIM x DIM block.
+struct Mfma32 {
+  static constexpr int DIM = 32, KSTEP = 16, NACC = 16;
+  typedef f32x16 Acc;
+  __device__ static int out_row(int l, int v) { return 8 * (v >> 2) + 4 * (l >> 5) + (v & 3); }
+  template <typename T8>
+  __device__ static Acc mma(T8 a, T8 b, Acc c) { return mfma32x32x16(a, b, c); }
+};
+struct Mfma16 {
+  static constexpr int DIM = 16, KSTEP = 32, NACC = 4;
+  typedef f32x4 Acc;
+  __device__ static int out_row(int l, int v) { return 4 * (l >> 4) + v; }
+  template <typename T8>
+  __device__ static Acc mma(T8 a, T8 b, Acc c) { return mfma16x16x32(a, b, c); }
+};
+
+template <int BM_, int BN_, typename MMA_>
+struct Tile {
+  typedef MMA_ MMA;
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int BK = 64;                      // k per LDS stage
+  static constexpr int WTM = BM / 2, WTN = BN / 2;   // wave tile (2 x 2 waves)
+  static constexpr int FM = WTM / MMA::DIM, FN = WTN / MMA::DIM;
+  static constexpr int SUBS = BK / MMA::KSTEP;       // MFMA sub-steps per slice
+  static constexpr int ROW_BYTES = BK * 2;           // 128
+  static constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024 / 4;  // 1 KiB loads per wave per stage
+  static constexpr int B_LOADS = B_BYTES / 1024 / 4;
+  static constexpr int GM = 4;                       // M-tiles per tile-order group
+  static_assert(WTM % MMA::DIM == 0 && WTN % MMA::DIM == 0, "wave tile must fit the MFMA");
+  static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole loads per wave");
+  static_assert(FM + FN <= 15, "a sub-step's reads must fit the lgkmcnt counter");
+  static_assert(SUBS % 2 == 0, "fragment buffers alternate per sub-step");
+};
+
+// Raw buffer descriptor over [base, base + bytes), as four scalar
+// registers (base, stride 0, byte range, raw-buffer flags).  Every field is
+// wave-uniform; readfirstlane says so and keeps it in SGPRs.
+__device__ __forceinline__ i32x4 make_desc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 d;
+  d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  d[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFF));
+  d[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  d[3] = 0x00020000;
+  return d;
+}
+
+// 16-byte-per-lane global -> LDS load (buffer_load_dwordx4 ... lds): lane l
+// writes LDS bytes [lds + 16 l, lds + 16 l + 16), zeros when voff is out of
+// the descriptor's range.  Issued as inline assembly so the compiler does
+// not track it: each wave waits for its own loads with s_waitcnt vmcnt
+// before the barrier that publishes them (the compiler's tracking would add
+// vmcnt(0) waits in front of LDS transpose reads of other stages).  It has
+// no register results, so no value the compiler sees is ever pending.  M0
+// holds the LDS base; the s_nop covers the M0 -> LDS DMA hazard.  Nothing
+// else in these kernels uses M0 (gfx950 LDS reads and MFMAs do not).
+// `lds` is the 32-bit LDS byte address (wave-uniform).
+__device__ __forceinline__ void load_lds16(const i32x4& desc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(desc) : "memory");
+}
+
+// Tile id -> (tile row, tile column): XCD-contiguous ids, then groups of GM
+// tile rows walked row-fastest.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm_size, int& tm,
+                                            int& tn) {
+  const int G = gridDim.x, b = blockIdx.x;
+  const int xcd = b % kXcds, local = b / kXcds;
+  const int per = G / kXcds, rem = G % kXcds;
+  const int id = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  const int span = gm_size * tiles_n;
+  const int group = id / span, first_m = group * gm_size;
+  const int gm = min(gm_size, tiles_m - first_m);
+  const int in = id - group * span;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+// BKN = false: B stored N x K (sbk = 1); true: B stored K x N (sbn = 1).
+template <typename T, typename Cfg, bool BKN>
+__global__ __launch_bounds__(256) void gemm16_tile(GemmArgs a, int tiles_m, int tiles_n) {
+  typedef typename Elem<T>::x8 T8;
+  typedef typename Cfg::MMA MMA;
+  typedef typename MMA::Acc Acc;
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, SUBS = Cfg::SUBS, DIM = MMA::DIM;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * Cfg::STAGE_BYTES];
+  // the array's 32-bit LDS address, for the M0 operand of the LDS-direct loads
+  const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int wm = w >> 1, wn = w & 1;
+  const int K = (int)a.K;
+  const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)(BKN ? a.sbk : a.sbn);
+
+  // Operand tiles as buffer descriptors that end at the last valid element:
+  // A rows m0 .. of length K; B rows n0 .. of length K (N x K), or B rows
+  // 0 .. K-1 from column n0 (K x N).
+  const int rows_a = (int)min<int64_t>(BM, a.M - m0), rows_b = (int)min<int64_t>(BN, a.N - n0);
+  const T* Ab = static_cast<const T*>(a.A) + m0 * a.sam;
+  const T* Bb = static_cast<const T*>(a.B) + (BKN ? n0 : n0 * a.sbn);
+  const i32x4 ra = make_desc(Ab, (uint32_t)(((rows_a - 1) * lda + K) * 2));
+  const i32x4 rb =
+      make_desc(Bb, (uint32_t)(BKN ? ((K - 1) * ldb + rows_b) * 2 : ((rows_b - 1) * ldb + K) * 2));
+
+  // Loads: wave w's i-th load fills LDS rows 8*(4i + w) .. +7 of a tile; lane
+  // l writes row 8*(4i + w) + (l >> 3), chunk position l & 7, so it fetches
+  // logical chunk (l & 7) ^ swizzle(row) = (l & 7) ^ (4 * (w & 1) + (l >> 4)).
+  const int lrow = 8 * w + (lane >> 3);
+  const int lchunk = (lane & 7) ^ (4 * (w & 1) + (lane >> 4));
+  const uint32_t a_lane = (uint32_t)lrow * lda * 2 + 16 * lchunk;
+  const uint32_t b_lane = (uint32_t)lrow * ldb * 2 + 16 * lchunk;
+  const uint32_t a_step = 32 * lda * 2, b_step = 32 * ldb * 2;  // 32 rows per load index
+
+  // K x N B: the stage holds B as [k][n] rows of BN * 2 bytes (BN = 256:
+  // 32 chunks); chunk c of row k sits at position c ^ ((4k) & 31), which
+  // keeps the transpose reads below free of bank conflicts.  Wave w's i-th
+  // load fills k-rows 2 * (4i + w) and +1; lane l writes row 2 * (4i + w) +
+  // (l >> 5), position l & 31, i.e. logical chunk (l & 31) ^ ((8w + 4 *
+  // (l >> 5)) & 31).  Rows past K are fetched out of range (zeros).
+  static_assert(!BKN || BN == 256, "K x N tiles are 256 columns wide");
+  const int nrow = lane >> 5;
+  const uint32_t nchunk = (lane & 31) ^ ((8 * w + 4 * nrow) & 31);
+  const uint32_t nb_lane = (uint32_t)(2 * w + nrow) * ldb * 2 + 16 * nchunk;
+  auto load_b = [&](uint32_t stage_base, int i, int k0, bool kin) {
+    const uint32_t dst = stage_base + Cfg::A_BYTES + (4 * i + w) * 1024;
+    if constexpr (BKN) {
+      const bool rin = k0 + 8 * i + 2 * w + nrow < K;
+      load_lds16(rb, dst, rin ? nb_lane + (uint32_t)(8 * i + k0) * ldb * 2 : kOutOfRange);
+    } else {
+      load_lds16(rb, dst, kin ? b_lane + i * b_step + 2 * k0 : kOutOfRange);
+    }
+  };
+
+  auto load_stage = [&](int st, int k0) {
+    const bool kin = k0 + 8 * lchunk < K;
+    const uint32_t base = lds32 + st * Cfg::STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < Cfg::A_LOADS; ++i)
+      load_lds16(ra, base + (4 * i + w) * 1024, kin ? a_lane + i * a_step + 2 * k0 : kOutOfRange);
+#pragma unroll
+    for (int i = 0; i < Cfg::B_LOADS; ++i) load_b(base, i, k0, kin);
+  };
+
+  // Reads: fragment row r = (DIM-aligned base) + (l % DIM), chunk
+  // s * (KSTEP / 8) + l / DIM of the 64-wide slice for sub-step s, at chunk
+  // position chunk ^ swizzle(r) = chunk ^ ((l >> 1) & 7).
+  const int sw = (lane >> 1) & 7;
+  const int rd_lane = (lane % DIM) * Cfg::ROW_BYTES;
+  const int rd_chunk = lane / DIM;
+  const int a_rd = wm * Cfg::WTM * Cfg::ROW_BYTES + rd_lane;
+  const int b_rd = Cfg::A_BYTES + wn * Cfg::WTN * Cfg::ROW_BYTES + rd_lane;
+
+  Acc acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < MMA::NACC; ++v) acc[i][j][v] = 0.0f;
+
+  // K x N B fragments come from ds_read_b64_tr_b16 (transpose read, gfx950):
+  // within each 16-lane group, lane 4r + q supplies the address of 4
+  // consecutive columns n0 + 4q .. +3 of k-row k0 + r, and lane i receives
+  // column n0 + i of those 4 rows.  So lane l of group u = l / 16 points at
+  // row s * KSTEP + 8 * kg + 4h + r, column nbase + nsub + 4q, with kg and
+  // nsub the MFMA's k-group and column half of that lane group (32x32x16:
+  // kg = u >> 1, nsub = 16 (u & 1); 16x16x32: kg = u, nsub = 0); two reads
+  // (h = 0, 1) give the lane's 8 k-values.  Per lane and fragment the offset
+  // does not depend on the sub-step or slice: precomputed for both h.
+  constexpr int BROW = BN * 2;
+  int kn_off[FN][2];
+  if constexpr (BKN) {
+    const int u = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+    const int kg = DIM == 32 ? u >> 1 : u, nsub = DIM == 32 ? 16 * (u & 1) : 0;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kr = 8 * kg + 4 * h + r;          // row within the sub-step
+        const int nbase = wn * Cfg::WTN + j * DIM;  // multiple of 16
+        const int chunk = (((nbase + nsub) >> 3) ^ ((4 * kr) & 31)) + (q >> 1);
+        kn_off[j][h] = Cfg::A_BYTES + kr * BROW + chunk * 16 + (q & 1) * 8;
+      }
+  }
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  auto read_b_kn = [&](const char* stage_base, int sub, int j) {
+    const char* p = stage_base + sub * MMA::KSTEP * BROW;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p + kn_off[j][0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p + kn_off[j][1]));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(T8, v);
+  };
+
+  // Fragments of one sub-step, double-buffered.
+  T8 fa[2][FM], fb[2][FN];
+  constexpr int BR = BKN ? 2 : 1;                    // LDS reads per B fragment
+  constexpr int NRD = FM + BR * FN;                  // LDS reads per sub-step
+  constexpr int NLD = Cfg::A_LOADS + Cfg::B_LOADS;   // LDS-direct loads per slice
+  static_assert(NRD <= FM * FN && NLD <= FM * FN, "one read and one load per MFMA");
+  auto frag_base = [&](int st, int sub) {
+    return lds + st * Cfg::STAGE_BYTES + ((sub * (MMA::KSTEP / 8) + rd_chunk) ^ sw) * 16;
+  };
+  // The r-th read of sub-step `sub` of stage st, in the order the MFMAs
+  // consume fragments: a0, b0 .. b[FN-1], a1 .. a[FM-1] (a K x N B fragment
+  // is a pair of reads, both issued at its first slot).
+  auto read_one = [&](int buf, int st, int sub, int r) {
+    const char* base = frag_base(st, sub);
+    if (r == 0) {
+      fa[buf][0] = *reinterpret_cast<const T8*>(base + a_rd);
+    } else if (r <= BR * FN) {
+      if constexpr (BKN) {
+        if ((r - 1) % 2 == 0)
+          fb[buf][(r - 1) / 2] = read_b_kn(lds + st * Cfg::STAGE_BYTES, sub, (r - 1) / 2);
+      } else {
+        fb[buf][r - 1] = *reinterpret_cast<const T8*>(base + b_rd + (r - 1) * DIM * Cfg::ROW_BYTES);
+      }
+    } else {
+      fa[buf][r - BR * FN] =
+          *reinterpret_cast<const T8*>(base + a_rd + (r - BR * FN) * DIM * Cfg::ROW_BYTES);
+    }
+  };
+  // keeps the scheduler from moving work across it (one wave per SIMD issues
+  // everything in order, so the source order below is the issue order)
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  // One sub-step: the MFMAs on fragment buffer `cur`; after the n-th MFMA,
+  // the n-th read of the next sub-step (into buffer cur ^ 1, from `next`)
+  // and, when LOADS, the LDS-direct loads of the slice at ld_k0 into stage
+  // ld_st, spread over the sub-step.  Spreading reads and loads over the MFMA stream hides their
+  // issue cycles under MFMA execution and keeps at most one sub-step of
+  // reads (<= 15, the lgkmcnt limit) in flight.
+  auto substep = [&](auto loads_c, int cur, int nst, int nsub, int ld_st, int ld_k0) {
+    constexpr bool LOADS = decltype(loads_c)::value;
+    const bool kin = ld_k0 + 8 * lchunk < K;
+    const uint32_t ld_base = lds32 + ld_st * Cfg::STAGE_BYTES;
+#pragma unroll
+    for (int n = 0; n < FM * FN; ++n) {
+      const int i = n / FN, j = n % FN;
+      acc[i][j] = MMA::mma(fa[cur][i], fb[cur][j], acc[i][j]);
+      if (n < NRD) read_one(cur ^ 1, nst, nsub, n);
+      if constexpr (LOADS) {
+        // load q goes after MFMA q * FM * FN / NLD: spread evenly, since a CU
+        // moves 64 B per clock from L2 and a burst of loads would stall the
+        // wave's issue (and with it the MFMAs) behind a full memory queue
+#pragma unroll
+        for (int q = 0; q < NLD; ++q) {
+          if (q * FM * FN / NLD != n) continue;
+          if (q < Cfg::A_LOADS)
+            load_lds16(ra, ld_base + (4 * q + w) * 1024,
+                       kin ? a_lane + q * a_step + 2 * ld_k0 : kOutOfRange);
+          else
+            load_b(ld_base, q - Cfg::A_LOADS, ld_k0, kin);
+        }
+      }
+      fence();
+    }
+  };
+
+  // Pipeline, per slice kt in stage st = kt & 1 (sub-steps s = 0 .. SUBS-1):
+  //   s < SUBS-1: MFMAs of sub-step s | reads of sub-step s+1;
+  //   then: wait for this wave's loads of slice kt+1 and barrier (after it,
+  //     slice kt+1 is in LDS for every wave, and every wave's reads of stage
+  //     st have returned -- the last sub-step needs them now anyway);
+  //   s = SUBS-1: MFMAs | reads of sub-step 0 of kt+1 | loads of slice
+  //     kt+2 -> stage st.
+  // Slices at or past K are fetched with out-of-range offsets: they move no
+  // data, fill the idle stage with zeros and keep the loop free of branches.
+  const int nk = (K + BK - 1) / BK;
+  load_stage(0, 0);
+  load_stage(1, BK);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");
+  __syncthreads();
+  {
+#pragma unroll
+    for (int r = 0; r < NRD; ++r) read_one(0, 0, 0, r);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+#pragma unroll
+    for (int sub = 0; sub < SUBS - 1; ++sub) {
+      fence();
+      substep(std::false_type(), sub & 1, st, sub + 1, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    fence();
+    substep(std::true_type(), (SUBS - 1) & 1, st ^ 1, 0, st, (kt + 2) * BK);
+  }
+
+  // Epilogue: round each accumulator to the output type and store it inside
+  // M x N.
+  T* C = static_cast<T*>(a.C);
+  const int64_t row0 = m0 + wm * Cfg::WTM, col0 = n0 + wn * Cfg::WTN + (lane % DIM);
+  if (m0 + BM <= a.M && n0 + BN <= a.N) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < MMA::NACC; ++v)
+          C[(row0 + i * DIM + MMA::out_row(lane, v)) * a.scm + col0 + j * DIM] =
+              to_out<T>(acc[i][j][v]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < MMA::NACC; ++v) {
+          const int64_t row = row0 + i * DIM + MMA::out_row(lane, v), col = col0 + j * DIM;
+          if (row < a.M && col < a.N) C[row * a.scm + col] = to_out<T>(acc[i][j][v]);
+        }
+  }
+}
+
+}  // namespace tile
+}  // namespace tg

@@ -122,8 +122,8 @@ def test_plan_names(lib):
 # The kernel each benchmark workload is planned onto (host-side choice; no
 # launch).  A silent fallback to the general kernel fails here.
 EXPECTED_PLANS = {
-    "fp16_256": "generic16_64x64",
-    "bf16_4096": "generic16_64x64",
+    "fp16_256": "tile_nn_256x256",
+    "bf16_4096": "tile_nn_256x256",
     "bf16_4096x7168x16384": "tile_nt_256x224",
     "bf16_skinny_64x7168x7168": "skinny_64x32",
     "fp8_4096x7168x16384": "generic_fp8_64x64",

@@ -58,6 +58,11 @@ def _layout_args(fmt, M, N, K, layout, seed, int_r=None):
         B = np.zeros((N, K + 24), np.uint16)
         B[:, :K] = draw((N, K), 1)
         return A, K + 24, 1, B, 1, K + 24
+    if layout == "kn_padded":           # B stored K x N with rows padded by 40 elements
+        A = draw((M, K), 0)
+        B = np.zeros((K, N + 40), np.uint16)
+        B[:, :N] = draw((K, N), 1)
+        return A, K, 1, B, N + 40, 1
     if layout == "colmajor":            # A stored K x M (A^T row-major), B K x N
         A, B = draw((K, M), 0), draw((K, N), 1)
         return A, 1, M, B, N, 1
@@ -292,3 +297,27 @@ def test_skinny(fmt, case):
 def test_skinny_padded():
     plan = _check16("bf16", 50, 70, 136, "padded", seed=41)
     assert plan == "skinny_64x32", plan
+
+
+# ------------------------------------------------------ K x N tile kernel
+
+NN_CASES = [(300, 512, 136), (513, 264, 72), (4000, 4000, 136), (256, 256, 64), (65, 8, 8),
+            (257, 1032, 1000)]
+
+
+@pytest.mark.parametrize("case", NN_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in NN_CASES])
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_tile_nn(fmt, case):
+    M, N, K = case
+    plan = _check16(fmt, M, N, K, "kn", seed=1000 + M + N + K)
+    assert plan == "tile_nn_256x256", plan
+    r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
+    plan = _check16(fmt, M, N, K, "kn", seed=1100 + M + N + K, int_r=r)
+    assert plan == "tile_nn_256x256", plan
+
+
+def test_tile_nn_padded():
+    plan = _check16("bf16", 300, 264, 200, "kn_padded", seed=51)
+    assert plan == "tile_nn_256x256", plan
+    plan = _check16("f16", 70, 96, 64, "kn_padded", seed=52)
+    assert plan == "tile_nn_256x256", plan
