@@ -1,12 +1,270 @@
-// placeholder: replaced by the tuned kernel
-#include "common.hpp"
+// Tuned fp8 block-scaled kernel: C (bf16) = A * B with OCP E4M3FN codes and
+// fp32 scales, one per 1 x 128 slice of each A row and one per 128 x 128
+// block of B, A row-major (M x K, sak = 1) and B stored N x K (sbk = 1).
+// FP8 and block-scaled GEMM are among the TileLang examples ("Getting to
+// know TileLang", operator-coverage section); the E4M3 format with
+// scale = amax / 448 is the one of "TileKernels deep dive" sections 4.3 and
+// 7.2.  The 128-wide K slice of the tile loop ("TileKernels deep dive"
+// section 3.1) is exactly one scale block:
+//   P = sum over the slice of e4m3(a) * e4m3(b)      (fp8 MFMA, fp32, exact
+//                                                      products)
+//   acc += (SA[i, kb] * SB[j / 128, kb]) * P          (one VALU FMA)
+// and C = round_bf16(acc) once at the end.
+//
+// Layout (gfx950):
+//  - workgroup tile 256 (M) x 128 (N), 4 waves stacked along M, each owning
+//    64 x 128 fp32 accumulators in VGPRs (the per-slice fold-in is VALU
+//    work) as 4 x 8 blocks of 16 x 16;
+//  - one v_mfma_scale_f32_16x16x128_f8f6f4 (unit block exponents) per
+//    block and slice; its fold-in into acc runs a few MFMAs later, so the
+//    VALU work overlaps the matrix core;
+//  - LDS: a 3-stage ring; a stage holds the A tile (256 rows x 128 bytes),
+//    the B tile (128 x 128 bytes), the slice's 256 A-row scales and the
+//    tile's B scale, all filled by LDS-direct loads (full 128-byte lines
+//    for A and B), two slices ahead of use;
+//  - fragment reads: lane l of a 16x16x128 operand supplies row l % 16 and
+//    32 k-bytes; lane group g = l / 16 takes 16-byte chunks g and g + 4 of
+//    the 128-byte row (A and B use the same k assignment, so the sum is the
+//    same), which with the chunk swizzle c ^ ((r >> 1) & 7) are
+//    bank-conflict free (the bf16 kernel's 16x16x32 patterns);
+//  - edges as in the bf16 kernels: descriptors end at the last valid row,
+//    chunks past K read as zero, stores are masked; rows past M read zero
+//    scales.
+#include "tile_mfma.hpp"
+
 namespace tg {
 namespace {
-bool accepts(Op, const GemmArgs&) { return false; }
-hipError_t launch(Op, const GemmArgs&, hipStream_t) { return hipErrorInvalidValue; }
+
+using tile::Int;
+using tile::kOutOfRange;
+using tile::load_lds16;
+using tile::make_desc;
+using tile::waitcnt_imm;
+
+constexpr int F_BM = 256, F_BN = 128, F_BK = 128;    // tile, k per slice (bytes)
+constexpr int F_FM = 4, F_FN = 8;                     // 16x16 blocks per wave
+constexpr int F_STAGES = 3;
+constexpr int F_A_BYTES = F_BM * F_BK;                // 32 KiB
+constexpr int F_B_BYTES = F_BN * F_BK;                // 16 KiB
+constexpr int F_SA_OFF = F_A_BYTES + F_B_BYTES;       // 256 fp32 A scales
+constexpr int F_SB_OFF = F_SA_OFF + F_BM * 4;         // 4 waves x 64 lanes x 4 bytes
+constexpr int F_STAGE = F_SB_OFF + 4 * 256;           // 50176 bytes
+constexpr int F_A_LD = F_A_BYTES / 1024 / 4;          // 8 loads per wave
+constexpr int F_B_LD = F_B_BYTES / 1024 / 4;          // 4 loads per wave
+constexpr int F_NLD = F_A_LD + F_B_LD + 2;            // + A scales, B scale
+constexpr int F_LAG = 4;                              // MFMAs between a block and its fold-in
+static_assert(F_STAGES * F_STAGE <= 160 * 1024, "LDS");
+
+// 4-byte-per-lane global -> LDS load (buffer_load_dword ... lds): lane l
+// writes LDS bytes [lds + 4 l, lds + 4 l + 4).  Inline assembly for the same
+// reason as the 16-byte loads (tile_mfma.hpp).
+__device__ __forceinline__ void load_lds4(const i32x4& desc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(desc) : "memory");
+}
+
+__global__ __launch_bounds__(256) void gemm_fp8_tile(GemmArgs a, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char lds[F_STAGES * F_STAGE];
+  const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+
+  int tm, tn;
+  tile::tile_coords(tiles_m, tiles_n, 4, tm, tn);
+  const int64_t m0 = (int64_t)tm * F_BM, n0 = (int64_t)tn * F_BN;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = (int)a.K;
+  const int nkb = (K + F_BK - 1) / F_BK;
+  const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
+
+  const int rows_a = (int)min<int64_t>(F_BM, a.M - m0), rows_b = (int)min<int64_t>(F_BN, a.N - n0);
+  const uint8_t* Ab = static_cast<const uint8_t*>(a.A) + m0 * a.sam;
+  const uint8_t* Bb = static_cast<const uint8_t*>(a.B) + n0 * a.sbn;
+  const i32x4 ra = make_desc(Ab, (uint32_t)((rows_a - 1) * lda + K));
+  const i32x4 rb = make_desc(Bb, (uint32_t)((rows_b - 1) * ldb + K));
+  // A scales of rows m0 ..: SA[i, kb] at (i * ssam + kb * ssak) floats; the
+  // tile's B scale row SB[n0 / 128, kb] at kb * ssbk floats
+  const float* SAb = a.SA + m0 * a.ssam;
+  const float* SBb = a.SB + (n0 / 128) * a.ssbn;
+  const i32x4 rsa = make_desc(SAb, (uint32_t)(((rows_a - 1) * a.ssam + (nkb - 1) * a.ssak + 1) * 4));
+  const i32x4 rsb = make_desc(SBb, (uint32_t)(((nkb - 1) * a.ssbk + 1) * 4));
+
+  // Loads of a slice (k0 bytes in): A rows 8 * (4i + w) + (l >> 3), B rows
+  // likewise, lane l fetching the chunk that belongs at LDS position l & 7:
+  // logical chunk (l & 7) ^ (4 * (w & 1) + (l >> 4)).  Then this wave's 64
+  // A-row scales and (lane 0 of wave 0) the B scale.
+  const uint32_t lrow = 8 * w + (lane >> 3);
+  const uint32_t lchunk = (lane & 7) ^ (4 * (w & 1) + (lane >> 4));
+  const uint32_t a_lane = lrow * lda + 16 * lchunk, b_lane = lrow * ldb + 16 * lchunk;
+  const int sa_row = 64 * w + lane;
+  const uint32_t sa_lane = (uint32_t)sa_row * (uint32_t)a.ssam * 4;
+  auto load_one = [&](int q, int st, int kb) {
+    const uint32_t base = lds32 + st * F_STAGE;
+    const int k0 = kb * F_BK;
+    const bool kin = k0 + 16 * (int)lchunk < K;
+    if (q < F_A_LD) {
+      load_lds16(ra, base + (4 * q + w) * 1024, kin ? a_lane + 32 * q * lda + k0 : kOutOfRange);
+    } else if (q < F_A_LD + F_B_LD) {
+      const int i = q - F_A_LD;
+      load_lds16(rb, base + F_A_BYTES + (4 * i + w) * 1024,
+                 kin ? b_lane + 32 * i * ldb + k0 : kOutOfRange);
+    } else if (q == F_A_LD + F_B_LD) {
+      const bool ok = kb < nkb && sa_row < rows_a;
+      load_lds4(rsa, base + F_SA_OFF + 256 * w,
+                ok ? sa_lane + (uint32_t)(kb * a.ssak) * 4 : kOutOfRange);
+    } else {
+      const bool ok = kb < nkb && w == 0 && lane == 0;
+      load_lds4(rsb, base + F_SB_OFF + 256 * w, ok ? (uint32_t)(kb * a.ssbk) * 4 : kOutOfRange);
+    }
+  };
+
+  // Fragment reads: block row r = 16-aligned base + (l & 15); lane group g
+  // reads chunks g and g + 4 at positions chunk ^ ((l >> 1) & 7).
+  const int sw = (lane >> 1) & 7, g = lane >> 4;
+  const int rd0 = (lane & 15) * F_BK + ((g ^ sw) * 16), rd1 = (lane & 15) * F_BK + (((g + 4) ^ sw) * 16);
+  const int a_rd = 64 * w * F_BK;
+  const int sa_rd = F_SA_OFF + (64 * w + 4 * g) * 4;   // + 64 * i bytes for block i
+
+  f32x4 acc[F_FM][F_FN];
+#pragma unroll
+  for (int i = 0; i < F_FM; ++i)
+#pragma unroll
+    for (int j = 0; j < F_FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // fragments of a slice, double-buffered; scales of a slice
+  i32x8 fa[2][F_FM], fb[2][F_FN];
+  f32x4 sa[2][F_FM];
+  float sb[2];
+  // r-th read of slice data in stage st (order of first use: a0, b0..b7,
+  // a1..a3 -- as read pairs -- then the scales)
+  auto read_one = [&](int buf, int st, int r) {
+    const char* base = lds + st * F_STAGE;
+    auto rd32 = [&](const char* p) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(p + rd0);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(p + rd1);
+      return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    if (r == 0) fa[buf][0] = rd32(base + a_rd);
+    else if (r <= F_FN) fb[buf][r - 1] = rd32(base + F_A_BYTES + (r - 1) * 16 * F_BK);
+    else if (r < F_FN + F_FM) fa[buf][r - F_FN] = rd32(base + a_rd + (r - F_FN) * 16 * F_BK);
+    else if (r < F_FN + 2 * F_FM)
+      sa[buf][r - F_FN - F_FM] = *reinterpret_cast<const f32x4*>(base + sa_rd + 64 * (r - F_FN - F_FM));
+    else
+      sb[buf] = *reinterpret_cast<const float*>(base + F_SB_OFF);
+  };
+  constexpr int NREAD = F_FN + 2 * F_FM + 1;          // read_one calls per slice
+  static_assert(NREAD <= F_FM * F_FN, "one read call per MFMA");
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+
+  // One slice (stage st, fragments in buffer cur): for each block n the
+  // MFMA, then the fold-in of block n - F_LAG; the reads of the next slice
+  // (stage nst, into buffer cur ^ 1) and the loads of slice kb_ld into stage
+  // ld_st are spread over the MFMAs.
+  auto slice = [&](int cur, int nst, int ld_st, int kb_ld) {
+    f32x4 p[F_LAG + 1];
+    float s[F_FM][4];
+#pragma unroll
+    for (int i = 0; i < F_FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s[i][v] = sa[cur][i][v] * sb[cur];
+#pragma unroll
+    for (int n = 0; n < F_FM * F_FN + F_LAG; ++n) {
+      if (n < F_FM * F_FN) {
+        const int i = n / F_FN, j = n % F_FN;
+        p[n % (F_LAG + 1)] = mfma16x16x128_e4m3(fa[cur][i], fb[cur][j], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+      }
+      if (n >= F_LAG) {
+        const int m = n - F_LAG, i = m / F_FN, j = m % F_FN;
+        const f32x4 pm = p[m % (F_LAG + 1)];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] += s[i][v] * pm[v];
+      }
+      // read calls spread over the slice (about one LDS read per MFMA keeps
+      // the wave under its 15 outstanding LDS reads)
+#pragma unroll
+      for (int r = 0; r < NREAD; ++r)
+        if (r * (F_FM * F_FN) / NREAD == n) read_one(cur ^ 1, nst, r);
+#pragma unroll
+      for (int q = 0; q < F_NLD; ++q)
+        if (q * (F_FM * F_FN) / F_NLD == n) load_one(q, ld_st, kb_ld);
+      fence();
+    }
+  };
+
+  // Pipeline over 128-wide slices kb (stage kb % 3): at the start of slice
+  // kb, wait for this wave's loads of slice kb + 1 (slice kb + 2's may stay
+  // in flight) and for its reads of slice kb (returned: its MFMAs start
+  // now), then barrier: slice kb + 1 is in LDS for every wave and no wave
+  // reads stage (kb + 2) % 3 any more; the slice then issues the loads of
+  // slice kb + 3 into stage kb % 3... which holds slice kb, whose fragments
+  // are already in registers.  Slices at or past K load out of range
+  // (zeros, no traffic).  Fragment buffers alternate per slice: two slices
+  // per trip (a slice past K adds zeros).
+#pragma unroll
+  for (int q = 0; q < F_NLD; ++q) load_one(q, 0, 0);
+#pragma unroll
+  for (int q = 0; q < F_NLD; ++q) load_one(q, 1, 1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(F_NLD) : "memory");
+  asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < NREAD; ++r) read_one(0, 0, r);
+#pragma unroll
+  for (int q = 0; q < F_NLD; ++q) load_one(q, 2, 2);
+  for (int kb = 0; kb < nkb; kb += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = kb + h;
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(F_NLD, 0));
+      asm volatile("s_barrier" ::: "memory");
+      fence();
+      slice(h, (k + 1) % F_STAGES, k % F_STAGES, k + 3);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Epilogue: lane l holds column l & 15, rows 4 (l >> 4) + v of each block.
+  __bf16* C = static_cast<__bf16*>(a.C);
+  const int64_t row0 = m0 + 64 * w + 4 * g, col0 = n0 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < F_FM; ++i)
+#pragma unroll
+    for (int j = 0; j < F_FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = row0 + 16 * i + v, col = col0 + 16 * j;
+        if (row < a.M && col < a.N) C[row * a.scm + col] = to_out<__bf16>(acc[i][j][v]);
+      }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Both code operands K-contiguous with 16-byte aligned rows, K a multiple of
+// 16 (whole 16-byte chunks); descriptor ranges fit 31 bits.
+bool accepts(Op op, const GemmArgs& a) {
+  if (op != Op::FP8) return false;
+  if (a.K == 0 || a.K % 16 != 0) return false;
+  if (a.sak != 1 || a.sbk != 1) return false;
+  if (a.sam % 16 != 0 || a.sbn % 16 != 0) return false;
+  if (!aligned16(a.A) || !aligned16(a.B)) return false;
+  if ((reinterpret_cast<uintptr_t>(a.SA) & 3) || (reinterpret_cast<uintptr_t>(a.SB) & 3)) return false;
+  const int64_t lim = int64_t(1) << 30, nkb = cdiv(a.K, 128);
+  if (F_BM * a.sam + a.K >= lim || F_BN * a.sbn + a.K >= lim) return false;
+  if ((F_BM * a.ssam + nkb * a.ssak) * 4 >= lim || (nkb * a.ssbk) * 4 >= lim) return false;
+  if (a.M > (int64_t(1) << 24) || a.N > (int64_t(1) << 24)) return false;
+  return true;
+}
+
+hipError_t launch(Op, const GemmArgs& a, hipStream_t s) {
+  const int tm = (int)cdiv(a.M, F_BM), tn = (int)cdiv(a.N, F_BN);
+  hipLaunchKernelGGL(gemm_fp8_tile, dim3(tm * tn), dim3(256), 0, s, a, tm, tn);
+  return hipGetLastError();
+}
+
 }  // namespace
+
 const Variant* variant_tile_fp8() {
-  static const Variant v = {"tile_fp8", accepts, launch, nullptr};
+  static const Variant v = {"tile_fp8_256x128", accepts, launch, nullptr};
   return &v;
 }
+
 }  // namespace tg

@@ -88,6 +88,12 @@ struct Tile {
   static_assert(SUBS % 2 == 0, "fragment buffers alternate per sub-step");
 };
 
+// s_waitcnt immediate (gfx9 layout): wait until at most `vm` vector-memory
+// and `lgkm` LDS operations of this wave are outstanding; no expcnt wait.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return ((vm >> 4) & 3) << 14 | (lgkm & 15) << 8 | 7 << 4 | (vm & 15);
+}
+
 // Raw buffer descriptor over [base, base + bytes), as four scalar
 // registers (base, stride 0, byte range, raw-buffer flags).  Every field is
 // wave-uniform; readfirstlane says so and keeps it in SGPRs.

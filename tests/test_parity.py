@@ -321,3 +321,22 @@ def test_tile_nn_padded():
     assert plan == "tile_nn_256x256", plan
     plan = _check16("f16", 70, 96, 64, "kn_padded", seed=52)
     assert plan == "tile_nn_256x256", plan
+
+
+# ------------------------------------------------------- fp8 tile kernel
+
+FP8_TILE_CASES = [(256, 128, 128), (300, 200, 400), (513, 384, 1040), (64, 1000, 2048),
+                  (1000, 136, 16), (257, 129, 3072)]
+
+
+@pytest.mark.parametrize("case", FP8_TILE_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in FP8_TILE_CASES])
+def test_fp8_tile(case):
+    M, N, K = case
+    plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 1200 + M + K), what="tile bound")
+    assert plan == "tile_fp8_256x128", plan
+    plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 1300 + M + K, int_r=16), exact=True,
+                      what="tile int unit scales")
+    assert plan == "tile_fp8_256x128", plan
+    plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 1400 + M + K, int_r=4, pow2_scales=True),
+                      exact=True, what="tile int pow2 scales")
+    assert plan == "tile_fp8_256x128", plan
