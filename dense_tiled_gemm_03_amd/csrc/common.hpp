@@ -41,6 +41,11 @@ const Variant* variant_tile_nn16();
 const Variant* variant_skinny16();
 const Variant* variant_tile_fp8();
 
+// Scratch of at least `bytes` for kernels on `stream` (current device); its
+// leading completion counters are zero between kernels.  NULL when it cannot
+// be had (allocation failure, or the stream is being captured).
+void* stream_workspace(hipStream_t stream, size_t bytes);
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

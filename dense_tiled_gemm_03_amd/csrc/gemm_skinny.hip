@@ -3,86 +3,103 @@
 // the 7168 hidden size of "TileKernels deep dive" (sections 5.1, 8.1).
 //
 // Here the product is bound by HBM: B (N x K) is read exactly once and is
-// ~98% of the bytes; A (64 x K) is re-read from L2 by every workgroup.  The
-// tile loop of "TileKernels deep dive" section 3.1 (clear an fp32 tile,
-// accumulate C tile += A tile * B tile over K, round once) is laid out so
-// that as many bytes as possible are in flight:
-//  - one workgroup per 32 columns of C, all (up to 64) rows;
-//  - K is split across the 4 waves by 64-wide slices (slice s goes to wave
-//    s % 4), each wave with its own 3-stage LDS ring filled by
-//    buffer_load_dwordx4 ... lds, so waves never wait on each other in the
-//    main loop and every wave keeps two slices (24 KiB) of loads in flight;
-//  - loads cover whole 128-byte lines (8 rows x 64 k per instruction);
-//    partial-line loads move far fewer bytes per clock on gfx950;
-//  - 32x32x16 MFMAs: per 64-wide slice, 2 x 1 blocks per wave;
-//  - the four partial 64 x 32 fp32 tiles are summed through LDS, rounded
-//    once and stored 16 bytes per lane.
+// ~98% of the bytes, so the kernel is laid out to keep as many B bytes in
+// flight as the LDS holds, using the tile loop of "TileKernels deep dive"
+// section 3.1 (clear an fp32 tile, accumulate C tile += A tile * B tile over
+// K, round once):
+//  - a workgroup owns 128 columns of C and all (up to 64) rows, over one of
+//    `splits` equal ranges of K (split-K across workgroups, so that there
+//    are about as many workgroups as CUs); its 4 waves each own 32 columns
+//    and share the A slice;
+//  - 64-wide K slices go HBM -> LDS with buffer_load_dwordx4 ... lds (whole
+//    128-byte lines) into a 6-stage ring shared by the 4 waves: five slices
+//    (80 KiB of B) in flight per workgroup; one barrier per slice; each
+//    slice's fragments are read from LDS while the previous slice's MFMAs
+//    run; nothing is loaded past the workgroup's K range;
+//  - 32x32x16 MFMAs: per slice, 2 x 1 blocks x 4 k-steps per wave;
+//  - each workgroup writes its fp32 64 x 128 partial tile to scratch; the
+//    last of a column strip's workgroups to finish (a device-scope counter)
+//    adds the strip's partial tiles in split order, rounds once and stores C,
+//    and clears the counter for the next call.  With one split the partial
+//    tile is rounded and stored directly.
 // LDS chunk swizzle, edges and descriptors as in the N x K tile kernel:
 // chunk c of row r at position c ^ ((r >> 1) & 7); rows past M / N read as
-// zero through the descriptor bounds; chunks past K get an out-of-range
-// offset; stores are masked.
-#include "common.hpp"
+// zero through the descriptor bounds; chunks past K (or past the
+// workgroup's K range) get an out-of-range offset; stores are masked.
+#include "tile_mfma.hpp"
 
 namespace tg {
 namespace {
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+using tile::kOutOfRange;
+using tile::load_lds16;
+using tile::make_desc;
 
-constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr int SM = 64;          // rows of C per workgroup (all of M)
-constexpr int SN = 32;          // columns of C per workgroup
-constexpr int SK = 64;          // k per slice
-constexpr int SSTAGES = 3;      // LDS ring depth per wave
-constexpr int ROWB = SK * 2;    // 128 bytes per LDS row
-constexpr int SLICE_BYTES = (SM + SN) * ROWB;  // 12 KiB
-constexpr int A_LD = SM / 8, B_LD = SN / 8;    // 1 KiB loads per slice
-constexpr int NLD = A_LD + B_LD;               // 12
-
-// Raw buffer descriptor over [base, base + bytes).  The fields go through
-// readfirstlane: they are wave-uniform, and saying so keeps the descriptor in
-// scalar registers (otherwise every load can become a per-lane waterfall).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-  void* q = reinterpret_cast<void*>((uint64_t)hi << 32 | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
-                                           0x00020000);
-}
+constexpr int SM = 64;                     // rows of C per workgroup (all of M)
+constexpr int SN = 128;                    // columns of C per workgroup (32 per wave)
+constexpr int SK = 64;                     // k per slice
+constexpr int SSTAGES = 6;                 // LDS ring depth
+constexpr int ROWB = SK * 2;               // 128 bytes per LDS row
+constexpr int STAGE = (SM + SN) * ROWB;    // 24 KiB
+constexpr int A_LD = SM / 8 / 4;           // 1 KiB loads per wave per slice (A)
+constexpr int B_LD = SN / 8 / 4;           // (B)
+constexpr int NLD = A_LD + B_LD;           // 6
+constexpr int RED_PITCH = SN + 4;          // fp32 tile row pitch in LDS (words)
+constexpr int kCus = 256;
+constexpr int kMinSlices = 8;              // fewest K slices per split
+constexpr int kCoherent = 0x10;            // sc1: device-coherent buffer access
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+static_assert(SSTAGES * NLD <= 63, "loads in flight must fit the vmcnt counter");
+static_assert(SM * RED_PITCH * 4 <= SSTAGES * STAGE, "reduction tile must fit the ring");
 
 template <typename T>
-__global__ __launch_bounds__(256) void gemm16_skinny(GemmArgs a) {
+__global__ __launch_bounds__(256) void gemm16_skinny(GemmArgs a, int splits, float* part,
+                                                     int* counters) {
   typedef typename Elem<T>::x8 T8;
-  __shared__ __attribute__((aligned(1024))) char lds[4 * SSTAGES * SLICE_BYTES];  // 144 KiB
+  __shared__ __attribute__((aligned(1024))) char lds[SSTAGES * STAGE];  // 144 KiB
+  __shared__ int last;  // this workgroup is the strip's last to finish
+  const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n0 = (int64_t)blockIdx.x * SN;
+  const int strip = blockIdx.x / splits, split = blockIdx.x % splits;
+  const int64_t n0 = (int64_t)strip * SN;
   const int K = (int)a.K;
   const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
-  const int rows_a = (int)a.M;                                 // <= 64
+  const int rows_a = (int)a.M;  // <= 64
   const int rows_b = (int)min<int64_t>(SN, a.N - n0);
   const T* Bb = static_cast<const T*>(a.B) + n0 * a.sbn;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(((rows_a - 1) * lda + K) * 2));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, (uint32_t)(((rows_b - 1) * ldb + K) * 2));
-  char* ring = lds + w * SSTAGES * SLICE_BYTES;
+  const i32x4 ra = make_desc(a.A, (uint32_t)(((rows_a - 1) * lda + K) * 2));
+  const i32x4 rb = make_desc(Bb, (uint32_t)(((rows_b - 1) * ldb + K) * 2));
 
-  // Load j (0 .. NLD-1) of a slice fills LDS rows 8j .. 8j+7 of the slice
-  // (A rows 0..63, then B rows 64..95); lane l writes row 8j + (l >> 3),
-  // chunk position l & 7, i.e. logical chunk (l & 7) ^ ((row >> 1) & 7)
-  // = (l & 7) ^ (4 * (j & 1) + (l >> 4)).
+  // This workgroup's slices [s_begin, s_end) of the nk 64-wide K slices.
+  const int nk = (K + SK - 1) / SK;
+  const int s_begin = (int)((int64_t)split * nk / splits);
+  const int s_end = (int)((int64_t)(split + 1) * nk / splits);
+  const int k_end = min(K, s_end * SK);
+
+  // Wave w fills stage rows 16w .. 16w+15 (A) and 64 + 32w .. 64+32w+31 (B),
+  // eight rows per load; lane l writes row 8m + (l >> 3) of the stage at
+  // chunk position l & 7, i.e. logical chunk (l & 7) ^ (4 (m & 1) + (l >> 4)).
   const uint32_t lrow = lane >> 3;
   const uint32_t lc0 = (lane & 7) ^ (lane >> 4), lc1 = (lane & 7) ^ (4 + (lane >> 4));
-  auto load_slice = [&](int slot, int k0) {
-    char* base = ring + slot * SLICE_BYTES;
+  auto load_slice = [&](int slot, int slice) {
+    // past this workgroup's range there is nothing to load (a load that
+    // would fetch nothing still costs the CU's load pipe a full issue)
+    if (slice >= s_end) return;
+    const int k0 = slice * SK;
+    const uint32_t stage = lds32 + slot * STAGE;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
-      const uint32_t c = (j & 1) ? lc1 : lc0;
-      const bool kin = k0 + 8 * (int)c < K;
-      const uint32_t row = 8 * (j < A_LD ? j : j - A_LD) + lrow;
-      const uint32_t off = row * (j < A_LD ? lda : ldb) * 2 + 2 * k0 + 16 * c;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(j < A_LD ? ra : rb, (lds_ptr_t)(base + j * 1024), 16,
-                                               kin ? off : kOutOfRange, 0, 0, 0);
+      const bool is_a = j < A_LD;
+      const int jj = is_a ? j : j - A_LD;
+      const uint32_t c = (jj & 1) ? lc1 : lc0;
+      const uint32_t row = (is_a ? 16 * w : 32 * w) + 8 * jj + lrow;  // row of A or of the B strip
+      const uint32_t group = is_a ? 2 * w + jj : 8 + 4 * w + jj;     // 8-row group in the stage
+      const bool kin = k0 + 8 * (int)c < k_end;
+      const uint32_t off = row * (is_a ? lda : ldb) * 2 + 2 * k0 + 16 * c;
+      load_lds16(is_a ? ra : rb, stage + group * 1024, kin ? off : kOutOfRange);
     }
   };
 
@@ -92,9 +109,10 @@ __global__ __launch_bounds__(256) void gemm16_skinny(GemmArgs a) {
   int rd[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) rd[s] = (lane & 31) * ROWB + (((2 * s + (lane >> 5)) ^ sw) * 16);
+  const int b_rows = (SM + 32 * w) * ROWB;
 
-  // Four accumulators (row block i, k16-step parity p) keep the dependent
-  // MFMA chains short; the parities are added before the reduction.
+  // Two accumulators per row block (k16-step parity) keep the dependent MFMA
+  // chains short; they are added before the epilogue.
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -103,76 +121,138 @@ __global__ __launch_bounds__(256) void gemm16_skinny(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][p][v] = 0.0f;
 
-  // Wave w takes slices w, w + 4, w + 8, ...; its ring holds slices i (being
-  // read), i + 1 and i + 2 (in flight).  Slices past K fetch out of range
-  // (no traffic, zeros), so every wave runs the same uniform loop.  Per
-  // slice all twelve fragments are read before the MFMAs, so the slice
-  // costs one LDS round trip.
-  const int nk = (K + SK - 1) / SK;
-  const int my = (nk - w + 3) / 4;   // slices of this wave
+  const int count = s_end - s_begin;
+  // Fragments of two slices alternate: slice i + 1 is read from LDS while
+  // slice i's MFMAs run.
+  T8 fa0[2][4], fa1[2][4], fb[2][4];
+  auto read_slice = [&](int buf, int slot) {
+    const char* base = lds + slot * STAGE;
 #pragma unroll
-  for (int s = 0; s < SSTAGES - 1; ++s) load_slice(s, (w + 4 * s) * SK);
-  for (int i = 0; i < my; ++i) {
-    // the slot refilled here held slice i - 1, whose reads this wave has
-    // already consumed in MFMAs
-    load_slice((i + SSTAGES - 1) % SSTAGES, (w + 4 * (i + SSTAGES - 1)) * SK);
+    for (int s = 0; s < 4; ++s) {
+      fa0[buf][s] = *reinterpret_cast<const T8*>(base + rd[s]);
+      fa1[buf][s] = *reinterpret_cast<const T8*>(base + 32 * ROWB + rd[s]);
+      fb[buf][s] = *reinterpret_cast<const T8*>(base + b_rows + rd[s]);
+    }
+  };
+  // One slice: wait until slice i + 1 has landed and every wave's reads of
+  // slice i are done; refill slice i's slot with slice i + SSTAGES; read
+  // slice i + 1; multiply slice i.
+  // The waits count loads: slice i + 1 is complete once at most the loads
+  // of the SSTAGES - 2 slices issued after it are outstanding.  Near the end
+  // of the range fewer slices follow (nothing is loaded past it), so there
+  // the wait is for every load.
+  auto step = [&](int i, int cur) {
+    if (i + SSTAGES - 1 < count)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((SSTAGES - 2) * NLD) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+    load_slice(i % SSTAGES, s_begin + i + SSTAGES);
+    read_slice(cur ^ 1, (i + 1) % SSTAGES);
+    __builtin_amdgcn_sched_barrier(0);  // reads ahead of the MFMAs
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      acc[0][s & 1] = mfma32x32x16(fa0[cur][s], fb[cur][s], acc[0][s & 1]);
+      acc[1][s & 1] = mfma32x32x16(fa1[cur][s], fb[cur][s], acc[1][s & 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int p = 0; p < SSTAGES; ++p) load_slice(p, s_begin + p);
+  if (SSTAGES <= count)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((SSTAGES - 1) * NLD) : "memory");
-    const char* base = ring + (i % SSTAGES) * SLICE_BYTES;
-    T8 fa0[4], fa1[4], fb[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      fa0[s] = *reinterpret_cast<const T8*>(base + rd[s]);
-      fa1[s] = *reinterpret_cast<const T8*>(base + 32 * ROWB + rd[s]);
-      fb[s] = *reinterpret_cast<const T8*>(base + SM * ROWB + rd[s]);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      acc[0][s & 1] = mfma32x32x16(fa0[s], fb[s], acc[0][s & 1]);
-      acc[1][s & 1] = mfma32x32x16(fa1[s], fb[s], acc[1][s & 1]);
-    }
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_barrier" ::: "memory");
+  read_slice(0, 0);
+  int i = 0;
+  for (; i + 1 < count; i += 2) {
+    step(i, 0);
+    step(i + 1, 1);
   }
+  if (i < count) step(i, 0);
+  // every load has landed (the last steps wait for all); once every wave is
+  // past its last reads the LDS is reused for the fp32 tile
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  // Sum the four partial tiles: wave w stores its 64 x 32 fp32 tile at
-  // red[w][row][col]; lane l holds column l & 31, rows 32i + 8(v/4) +
-  // 4(l >> 5) + (v % 4).
   __syncthreads();
+
+  // The 64 x 128 fp32 tile through LDS: wave w's lane l holds column
+  // 32w + (l & 31), rows 32i + 8(v/4) + 4(l >> 5) + (v % 4).
   float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int row = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      red[(w * SM + row) * SN + (lane & 31)] = acc[i][0][v] + acc[i][1][v];
+      red[row * RED_PITCH + 32 * w + (lane & 31)] = acc[i][0][v] + acc[i][1][v];
     }
   __syncthreads();
-  // thread t: row t >> 2, columns 8 * (t & 3) .. +7
-  const int t = threadIdx.x, row = t >> 2, c0 = 8 * (t & 3);
-  float sum[8];
+  // Thread t, step e handles float4 q = 256 e + t of the tile (row q >> 5,
+  // columns 4 (q & 31) .. + 3): consecutive lanes touch consecutive 16 bytes
+  // in LDS, in scratch and (8 bytes) in C.
+  const int t = threadIdx.x;
+  f32x4 x[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sum[e] = 0.0f;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(red + (p * SM + row) * SN + c0);
-    const f32x4 x0 = src[0], x1 = src[1];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sum[e] += x0[e];
-      sum[4 + e] += x1[e];
-    }
+  for (int e = 0; e < 8; ++e) {
+    const int q = 256 * e + t;
+    x[e] = *reinterpret_cast<const f32x4*>(red + (q >> 5) * RED_PITCH + 4 * (q & 31));
   }
-  if (row < a.M) {
-    T* C = static_cast<T*>(a.C) + (int64_t)row * a.scm + n0 + c0;
-    if (n0 + c0 + 8 <= a.N && (reinterpret_cast<uintptr_t>(C) & 15) == 0) {
-      typename Elem<T>::x8 o;
+
+  if (splits > 1) {
+    // Publish this split's partial tile, then count the strip's finished
+    // splits; the last one sums all partial tiles in split order (so the
+    // result does not depend on which finishes last).  The tiles are written
+    // and read with device-coherent (sc1) accesses, and every wave waits for
+    // its writes to complete before the barrier that precedes the counter
+    // increment, so the last workgroup reads every tile whole.
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        part + (int64_t)strip * splits * SM * SN, (short)0, splits * SM * SN * 4, 0x00020000);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = to_out<T>(sum[e]);
-      *reinterpret_cast<typename Elem<T>::x8*>(C) = o;
+    for (int e = 0; e < 8; ++e)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x[e]), rp,
+                                             (split * SM * SN + 4 * (256 * e + t)) * 4, 0,
+                                             kCoherent);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t == 0) last = atomicAdd(counters + strip, 1) == splits - 1;
+    __syncthreads();
+    if (!last) return;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // four splits' tiles in flight at a time, added in split order
+    for (int sp0 = 0; sp0 < splits; sp0 += 4) {
+      u32x4 y[4][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          y[j][e] = __builtin_amdgcn_raw_buffer_load_b128(
+              rp, ((sp0 + j) * SM * SN + 4 * (256 * e + t)) * 4, 0, kCoherent);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (sp0 + j < splits)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] += __builtin_bit_cast(f32x4, y[j][e]);
+    }
+    if (t == 0) __hip_atomic_store(counters + strip, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  typedef typename Elem<T>::x4 T4;
+  T* Cb = static_cast<T*>(a.C);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int q = 256 * e + t, row = q >> 5, col = 4 * (q & 31);
+    if (row >= a.M) continue;
+    T* C = Cb + (int64_t)row * a.scm + n0 + col;
+    T4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = to_out<T>(x[e][j]);
+    if (n0 + col + 4 <= a.N && (reinterpret_cast<uintptr_t>(C) & 7) == 0) {
+      *reinterpret_cast<T4*>(C) = o;
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (n0 + c0 + e < a.N) C[e] = to_out<T>(sum[e]);
+      for (int j = 0; j < 4; ++j)
+        if (n0 + col + j < a.N) C[j] = o[j];
     }
   }
 }
@@ -193,19 +273,44 @@ bool accepts(Op op, const GemmArgs& a) {
   return true;
 }
 
-hipError_t launch(Op op, const GemmArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)cdiv(a.N, SN)), block(256);
+// Split K so that the grid is about one workgroup per CU, keeping at least
+// kMinSlices slices per split.
+int choose_splits(const GemmArgs& a) {
+  const int64_t strips = cdiv(a.N, SN), nk = cdiv(a.K, SK);
+  int64_t s = kCus / strips;
+  if (s > nk / kMinSlices) s = nk / kMinSlices;
+  return s < 1 ? 1 : (int)s;
+}
+
+hipError_t launch(Op op, const GemmArgs& a, hipStream_t stream) {
+  const int64_t strips = cdiv(a.N, SN);
+  int splits = choose_splits(a);
+  float* part = nullptr;
+  int* counters = nullptr;
+  if (splits > 1) {
+    const size_t cnt_bytes = ((size_t)strips * 4 + 255) & ~size_t(255);
+    const size_t bytes = cnt_bytes + (size_t)strips * splits * SM * SN * 4;
+    char* ws = static_cast<char*>(stream_workspace(stream, bytes));
+    if (ws == nullptr) {
+      splits = 1;  // no scratch to be had: one workgroup per strip, no combining
+    } else {
+      counters = reinterpret_cast<int*>(ws);
+      part = reinterpret_cast<float*>(ws + cnt_bytes);
+    }
+  }
+  const dim3 grid((unsigned)(strips * splits)), block(256);
   if (op == Op::BF16)
-    hipLaunchKernelGGL(gemm16_skinny<__bf16>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(gemm16_skinny<__bf16>, grid, block, 0, stream, a, splits, part, counters);
   else
-    hipLaunchKernelGGL(gemm16_skinny<_Float16>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(gemm16_skinny<_Float16>, grid, block, 0, stream, a, splits, part,
+                       counters);
   return hipGetLastError();
 }
 
 }  // namespace
 
 const Variant* variant_skinny16() {
-  static const Variant v = {"skinny_64x32", accepts, launch, nullptr};
+  static const Variant v = {"skinny_64x128", accepts, launch, nullptr};
   return &v;
 }
 

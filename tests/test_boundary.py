@@ -125,7 +125,7 @@ EXPECTED_PLANS = {
     "fp16_256": "tile_nn_256x256",
     "bf16_4096": "tile_nn_256x256",
     "bf16_4096x7168x16384": "tile_nt_256x224",
-    "bf16_skinny_64x7168x7168": "skinny_64x32",
+    "bf16_skinny_64x7168x7168": "skinny_64x128",
     "fp8_4096x7168x16384": "tile_fp8_256x128",
 }
 

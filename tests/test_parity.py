@@ -279,8 +279,11 @@ def test_tile_nt_padded_leading_dims():
 
 # ------------------------------------------------------------ skinny kernel
 
+# (M, N, K): one split (short K) and split-K across workgroups (K of 16 or
+# more 64-wide slices), ragged N strips, K not a multiple of the slice.
 SKINNY_CASES = [(1, 100, 64), (17, 300, 200), (64, 64, 8), (64, 33, 1000), (40, 7168, 1024),
-                (63, 95, 4104)]
+                (63, 95, 4104), (64, 1000, 2056), (64, 7168, 520)]
+SKINNY = "skinny_64x128"
 
 
 @pytest.mark.parametrize("case", SKINNY_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SKINNY_CASES])
@@ -288,15 +291,36 @@ SKINNY_CASES = [(1, 100, 64), (17, 300, 200), (64, 64, 8), (64, 33, 1000), (40, 
 def test_skinny(fmt, case):
     M, N, K = case
     plan = _check16(fmt, M, N, K, "nk", seed=800 + M + N + K)
-    assert plan == "skinny_64x32", plan
+    assert plan == SKINNY, plan
     r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
     plan = _check16(fmt, M, N, K, "nk", seed=900 + M + N + K, int_r=r)
-    assert plan == "skinny_64x32", plan
+    assert plan == SKINNY, plan
 
 
 def test_skinny_padded():
     plan = _check16("bf16", 50, 70, 136, "padded", seed=41)
-    assert plan == "skinny_64x32", plan
+    assert plan == SKINNY, plan
+    plan = _check16("bf16", 64, 300, 3000, "padded", seed=42)
+    assert plan == SKINNY, plan
+
+
+def test_skinny_split_k_deterministic_and_per_stream():
+    """The split-K combination adds the partial tiles in a fixed order: two
+    runs agree bit for bit, on the default stream and on a second stream
+    (which has scratch of its own), with calls of other shapes in between."""
+    w = configs.WORKLOADS["bf16_skinny_64x7168x7168"]
+    d = configs.make_inputs(w)
+    A, B = H.dev(d["A"]), H.dev(d["B"])
+    H.log("skinny determinism / second stream")
+    c1, plan = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
+    assert plan == SKINNY, plan
+    _check16("bf16", 64, 1000, 2056, "nk", seed=61)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c2, _ = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
+    torch.cuda.synchronize()
+    c3, _ = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
+    assert np.array_equal(c1, c2) and np.array_equal(c1, c3)
 
 
 # ------------------------------------------------------ K x N tile kernel
