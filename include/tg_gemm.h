@@ -24,10 +24,18 @@
  *  - C = A * B overwrites C (no alpha/beta).  Accumulation is fp32; the result
  *    is rounded once to the output type, round-to-nearest-even.
  *  - A, B, C (and scales) are DEVICE pointers owned by the caller; they must
- *    stay valid until the work enqueued on `stream` has completed.  The library
- *    allocates no memory and keeps no state between calls.
+ *    stay valid until the work enqueued on `stream` has completed.
+ *  - Scratch: products with M <= 64 split K across workgroups and combine the
+ *    partial results through a device buffer the library owns, one per
+ *    (device, stream), allocated on the first such call on that stream (and
+ *    grown, after synchronising the stream, when a later call needs more) and
+ *    kept until the process ends; about 32 KiB per 64 x 128 block of C per
+ *    K split (7.3 MiB for 64 x 7168 x 7168).  Such a call made while the
+ *    stream is being captured into a graph, or when the buffer cannot be had,
+ *    runs without splitting K instead.  No other call allocates.
  *  - Calls are asynchronous: they enqueue on `stream` (a hipStream_t; NULL is
- *    the null stream) and return.  They are reentrant.
+ *    the null stream) and return.  They are reentrant; calls on different
+ *    streams never share scratch.
  *  - C must not overlap A, B or the scales (undefined behaviour otherwise).
  *
  * Errors (tg_status)
