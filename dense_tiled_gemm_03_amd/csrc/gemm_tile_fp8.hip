@@ -12,12 +12,16 @@
 // and C = round_bf16(acc) once at the end.
 //
 // Layout (gfx950):
-//  - workgroup tile 256 (M) x 128 (N), 4 waves stacked along M, each owning
-//    64 x 128 fp32 accumulators in VGPRs (the per-slice fold-in is VALU
-//    work) as 4 x 8 blocks of 16 x 16;
+//  - workgroup tile 256 (M) x 128 (N), 8 waves (4 along M x 2 along N, two
+//    per SIMD, so one wave's VALU fold-in runs while the other's MFMAs do),
+//    each owning 64 x 64 fp32 accumulators in VGPRs as 4 x 4 blocks of
+//    16 x 16;
 //  - one v_mfma_scale_f32_16x16x128_f8f6f4 (unit block exponents) per
-//    block and slice; its fold-in into acc runs a few MFMAs later, so the
-//    VALU work overlaps the matrix core;
+//    block and slice, blocks taken column by column; the fold-in of a block
+//    runs two MFMAs after it;
+//  - registers: the A fragments of two slices alternate; each B fragment is
+//    re-read for the next slice right after its last use in this one (so a
+//    wave fits in 256 VGPRs with no accumulation registers);
 //  - LDS: a 3-stage ring; a stage holds the A tile (256 rows x 128 bytes),
 //    the B tile (128 x 128 bytes), the slice's 256 A-row scales and the
 //    tile's B scale, all filled by LDS-direct loads (full 128-byte lines
@@ -35,35 +39,48 @@
 namespace tg {
 namespace {
 
-using tile::Int;
 using tile::kOutOfRange;
-using tile::load_lds16;
 using tile::make_desc;
 using tile::waitcnt_imm;
 
 constexpr int F_BM = 256, F_BN = 128, F_BK = 128;    // tile, k per slice (bytes)
-constexpr int F_FM = 4, F_FN = 8;                     // 16x16 blocks per wave
+constexpr int F_WAVES = 8;                            // 4 along M x 2 along N
+constexpr int F_FM = 4, F_FN = 4;                     // 16x16 blocks per wave
 constexpr int F_STAGES = 3;
 constexpr int F_A_BYTES = F_BM * F_BK;                // 32 KiB
 constexpr int F_B_BYTES = F_BN * F_BK;                // 16 KiB
 constexpr int F_SA_OFF = F_A_BYTES + F_B_BYTES;       // 256 fp32 A scales
 constexpr int F_SB_OFF = F_SA_OFF + F_BM * 4;         // 4 waves x 64 lanes x 4 bytes
 constexpr int F_STAGE = F_SB_OFF + 4 * 256;           // 50176 bytes
-constexpr int F_A_LD = F_A_BYTES / 1024 / 4;          // 8 loads per wave
-constexpr int F_B_LD = F_B_BYTES / 1024 / 4;          // 4 loads per wave
-constexpr int F_NLD = F_A_LD + F_B_LD + 2;            // + A scales, B scale
-constexpr int F_LAG = 4;                              // MFMAs between a block and its fold-in
+constexpr int F_A_LD = F_A_BYTES / 1024 / F_WAVES;    // 4 loads per wave
+constexpr int F_B_LD = F_B_BYTES / 1024 / F_WAVES;    // 2 loads per wave
+constexpr int F_NLD = F_A_LD + F_B_LD + 1;            // + a scale load
+constexpr int F_LAG = 2;                              // MFMAs between a block and its fold-in
+constexpr int F_NMMA = F_FM * F_FN;                   // MFMAs per wave per slice
 static_assert(F_STAGES * F_STAGE <= 160 * 1024, "LDS");
 
-// 4-byte-per-lane global -> LDS load (buffer_load_dword ... lds): lane l
-// writes LDS bytes [lds + 4 l, lds + 4 l + 4).  Inline assembly for the same
-// reason as the 16-byte loads (tile_mfma.hpp).
-__device__ __forceinline__ void load_lds4(const i32x4& desc, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(desc) : "memory");
+// Global -> LDS loads with a wave-uniform scalar offset: lane l reads
+// [voff + soff, + 16) (or + 4) of the buffer into LDS bytes [lds + 16 l, + 16)
+// (or [lds + 4 l, + 4)).  The range check is left to voff alone (on this
+// architecture the scalar offset may be outside it): every lane that must
+// read zeros gets an out-of-range voff, and an in-range voff plus the
+// scalar offset (the slice's k) stays inside the row and chunk it names.
+// Inline assembly for the same reason as the loads of tile_mfma.hpp;
+// keeping the per-lane part to one register per load keeps the kernel
+// within 256 VGPRs.
+__device__ __forceinline__ void load_lds16s(const i32x4& desc, uint32_t lds, uint32_t voff,
+                                            uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void load_lds4s(const i32x4& desc, uint32_t lds, uint32_t voff,
+                                           uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory");
 }
 
-__global__ __launch_bounds__(256) void gemm_fp8_tile(GemmArgs a, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(64 * F_WAVES) void gemm_fp8_tile(GemmArgs a, int tiles_m,
+                                                                int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char lds[F_STAGES * F_STAGE];
   const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
@@ -73,6 +90,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_tile(GemmArgs a, int tiles_m, in
   const int64_t m0 = (int64_t)tm * F_BM, n0 = (int64_t)tn * F_BN;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w & 3, wn = w >> 2;
   const int K = (int)a.K;
   const int nkb = (K + F_BK - 1) / F_BK;
   const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
@@ -89,32 +107,46 @@ __global__ __launch_bounds__(256) void gemm_fp8_tile(GemmArgs a, int tiles_m, in
   const i32x4 rsa = make_desc(SAb, (uint32_t)(((rows_a - 1) * a.ssam + (nkb - 1) * a.ssak + 1) * 4));
   const i32x4 rsb = make_desc(SBb, (uint32_t)(((nkb - 1) * a.ssbk + 1) * 4));
 
-  // Loads of a slice (k0 bytes in): A rows 8 * (4i + w) + (l >> 3), B rows
-  // likewise, lane l fetching the chunk that belongs at LDS position l & 7:
-  // logical chunk (l & 7) ^ (4 * (w & 1) + (l >> 4)).  Then this wave's 64
-  // A-row scales and (lane 0 of wave 0) the B scale.
+  // Loads of a slice (k0 bytes in): the tile's 8-row groups g = w + 8 q of A
+  // (q < 4) and of B (q < 2), rows 8 g + (l >> 3), lane l fetching the chunk
+  // that belongs at LDS position l & 7: logical chunk
+  // (l & 7) ^ (4 (g & 1) + (l >> 4)), and g & 1 = w & 1.  Then one 4-byte
+  // load: waves 0-3 the A-row scales of rows 64 w .., wave 4 the B scale
+  // (lane 0), waves 5-7 nothing (out of range).
   const uint32_t lrow = 8 * w + (lane >> 3);
   const uint32_t lchunk = (lane & 7) ^ (4 * (w & 1) + (lane >> 4));
   const uint32_t a_lane = lrow * lda + 16 * lchunk, b_lane = lrow * ldb + 16 * lchunk;
+  // Per-lane offsets of this wave's loads (the slice's k goes in the scalar
+  // offset): A row groups q, B row groups i, out of range for rows past M /
+  // N; the scale load: waves 0-3 one A row each, wave 4 lane 0 the B scale,
+  // everything else out of range.
+  uint32_t av[F_A_LD], bv[F_B_LD];
+#pragma unroll
+  for (int q = 0; q < F_A_LD; ++q)
+    av[q] = (int)(lrow + 64 * q) < rows_a ? a_lane + 64 * q * lda : kOutOfRange;
+#pragma unroll
+  for (int i = 0; i < F_B_LD; ++i)
+    bv[i] = (int)(lrow + 64 * i) < rows_b ? b_lane + 64 * i * ldb : kOutOfRange;
   const int sa_row = 64 * w + lane;
-  const uint32_t sa_lane = (uint32_t)sa_row * (uint32_t)a.ssam * 4;
+  const uint32_t s_lane =
+      w < 4 ? (sa_row < rows_a ? (uint32_t)sa_row * (uint32_t)a.ssam * 4 : kOutOfRange)
+            : (w == 4 && lane == 0 ? 0u : kOutOfRange);
+  const i32x4 rs = w < 4 ? rsa : rsb;
+  const uint32_t s_lds = w < 4 ? F_SA_OFF + 256 * w : F_SB_OFF + 256 * (w - 4);
+  const uint32_t s_step = (uint32_t)(w < 4 ? a.ssak : a.ssbk) * 4;
+  // load q of slice kb into stage st; chunks past K and slices past the
+  // last scale block read zeros
   auto load_one = [&](int q, int st, int kb) {
     const uint32_t base = lds32 + st * F_STAGE;
-    const int k0 = kb * F_BK;
-    const bool kin = k0 + 16 * (int)lchunk < K;
+    const uint32_t k0 = (uint32_t)(kb * F_BK);
+    const bool kin = (int)k0 + 16 * (int)lchunk < K;
     if (q < F_A_LD) {
-      load_lds16(ra, base + (4 * q + w) * 1024, kin ? a_lane + 32 * q * lda + k0 : kOutOfRange);
+      load_lds16s(ra, base + (w + 8 * q) * 1024, kin ? av[q] : kOutOfRange, k0);
     } else if (q < F_A_LD + F_B_LD) {
       const int i = q - F_A_LD;
-      load_lds16(rb, base + F_A_BYTES + (4 * i + w) * 1024,
-                 kin ? b_lane + 32 * i * ldb + k0 : kOutOfRange);
-    } else if (q == F_A_LD + F_B_LD) {
-      const bool ok = kb < nkb && sa_row < rows_a;
-      load_lds4(rsa, base + F_SA_OFF + 256 * w,
-                ok ? sa_lane + (uint32_t)(kb * a.ssak) * 4 : kOutOfRange);
+      load_lds16s(rb, base + F_A_BYTES + (w + 8 * i) * 1024, kin ? bv[i] : kOutOfRange, k0);
     } else {
-      const bool ok = kb < nkb && w == 0 && lane == 0;
-      load_lds4(rsb, base + F_SB_OFF + 256 * w, ok ? (uint32_t)(kb * a.ssbk) * 4 : kOutOfRange);
+      load_lds4s(rs, base + s_lds, kb < nkb ? s_lane : kOutOfRange, (uint32_t)kb * s_step);
     }
   };
 
@@ -122,8 +154,8 @@ __global__ __launch_bounds__(256) void gemm_fp8_tile(GemmArgs a, int tiles_m, in
   // reads chunks g and g + 4 at positions chunk ^ ((l >> 1) & 7).
   const int sw = (lane >> 1) & 7, g = lane >> 4;
   const int rd0 = (lane & 15) * F_BK + ((g ^ sw) * 16), rd1 = (lane & 15) * F_BK + (((g + 4) ^ sw) * 16);
-  const int a_rd = 64 * w * F_BK;
-  const int sa_rd = F_SA_OFF + (64 * w + 4 * g) * 4;   // + 64 * i bytes for block i
+  const int a_rd = 64 * wm * F_BK, b_rd = F_A_BYTES + 64 * wn * F_BK;
+  const int sa_rd = F_SA_OFF + (64 * wm + 4 * g) * 4;   // + 64 * i bytes for block i
 
   f32x4 acc[F_FM][F_FN];
 #pragma unroll
@@ -131,75 +163,69 @@ __global__ __launch_bounds__(256) void gemm_fp8_tile(GemmArgs a, int tiles_m, in
 #pragma unroll
     for (int j = 0; j < F_FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // fragments of a slice, double-buffered; scales of a slice
-  i32x8 fa[2][F_FM], fb[2][F_FN];
-  f32x4 sa[2][F_FM];
-  float sb[2];
-  // r-th read of slice data in stage st (order of first use: a0, b0..b7,
-  // a1..a3 -- as read pairs -- then the scales)
-  auto read_one = [&](int buf, int st, int r) {
-    const char* base = lds + st * F_STAGE;
-    auto rd32 = [&](const char* p) {
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(p + rd0);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(p + rd1);
-      return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    if (r == 0) fa[buf][0] = rd32(base + a_rd);
-    else if (r <= F_FN) fb[buf][r - 1] = rd32(base + F_A_BYTES + (r - 1) * 16 * F_BK);
-    else if (r < F_FN + F_FM) fa[buf][r - F_FN] = rd32(base + a_rd + (r - F_FN) * 16 * F_BK);
-    else if (r < F_FN + 2 * F_FM)
-      sa[buf][r - F_FN - F_FM] = *reinterpret_cast<const f32x4*>(base + sa_rd + 64 * (r - F_FN - F_FM));
-    else
-      sb[buf] = *reinterpret_cast<const float*>(base + F_SB_OFF);
+  // A fragments of two slices; B fragments of one (re-read after last use);
+  // the next slice's scales
+  i32x8 fa[2][F_FM], fb[F_FN];
+  f32x4 sa[F_FM];
+  float sb;
+  auto rd32 = [&](const char* p) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(p + rd0);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + rd1);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  constexpr int NREAD = F_FN + 2 * F_FM + 1;          // read_one calls per slice
-  static_assert(NREAD <= F_FM * F_FN, "one read call per MFMA");
+  auto read_a = [&](int buf, int st, int i) { fa[buf][i] = rd32(lds + st * F_STAGE + a_rd + i * 16 * F_BK); };
+  auto read_b = [&](int st, int j) { fb[j] = rd32(lds + st * F_STAGE + b_rd + j * 16 * F_BK); };
+  auto read_s = [&](int st) {
+    const char* base = lds + st * F_STAGE;
+#pragma unroll
+    for (int i = 0; i < F_FM; ++i) sa[i] = *reinterpret_cast<const f32x4*>(base + sa_rd + 64 * i);
+    sb = *reinterpret_cast<const float*>(base + F_SB_OFF);
+  };
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
-  // One slice (stage st, fragments in buffer cur): for each block n the
-  // MFMA, then the fold-in of block n - F_LAG; the reads of the next slice
-  // (stage nst, into buffer cur ^ 1) and the loads of slice kb_ld into stage
-  // ld_st are spread over the MFMAs.
+  // One slice (A fragments in buffer cur; B fragments and scales of this
+  // slice in fb / sa / sb): MFMA n covers block (i, j) = (n % F_FM, n / F_FM)
+  // and the fold-in of MFMA n - F_LAG follows it.  Reads of the next slice
+  // (stage nst): B fragment j after its last use here, A fragments into
+  // buffer cur ^ 1 and the scales spread over the slice; the loads of
+  // slice kb_ld into stage ld_st are spread over the MFMAs.
   auto slice = [&](int cur, int nst, int ld_st, int kb_ld) {
     f32x4 p[F_LAG + 1];
     float s[F_FM][4];
 #pragma unroll
     for (int i = 0; i < F_FM; ++i)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) s[i][v] = sa[cur][i][v] * sb[cur];
+      for (int v = 0; v < 4; ++v) s[i][v] = sa[i][v] * sb;
 #pragma unroll
-    for (int n = 0; n < F_FM * F_FN + F_LAG; ++n) {
-      if (n < F_FM * F_FN) {
-        const int i = n / F_FN, j = n % F_FN;
-        p[n % (F_LAG + 1)] = mfma16x16x128_e4m3(fa[cur][i], fb[cur][j], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+    for (int n = 0; n < F_NMMA + F_LAG; ++n) {
+      if (n < F_NMMA) {
+        const int i = n % F_FM, j = n / F_FM;
+        p[n % (F_LAG + 1)] = mfma16x16x128_e4m3(fa[cur][i], fb[j], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+        if (i == F_FM - 1) read_b(nst, j);
       }
       if (n >= F_LAG) {
-        const int m = n - F_LAG, i = m / F_FN, j = m % F_FN;
+        const int m = n - F_LAG, i = m % F_FM, j = m / F_FM;
         const f32x4 pm = p[m % (F_LAG + 1)];
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[i][j][v] += s[i][v] * pm[v];
       }
-      // read calls spread over the slice (about one LDS read per MFMA keeps
-      // the wave under its 15 outstanding LDS reads)
-#pragma unroll
-      for (int r = 0; r < NREAD; ++r)
-        if (r * (F_FM * F_FN) / NREAD == n) read_one(cur ^ 1, nst, r);
+      if (n == 1 || n == 5 || n == 9 || n == 13) read_a(cur ^ 1, nst, n / 4);
+      if (n == 10) read_s(nst);
 #pragma unroll
       for (int q = 0; q < F_NLD; ++q)
-        if (q * (F_FM * F_FN) / F_NLD == n) load_one(q, ld_st, kb_ld);
+        if (q * F_NMMA / F_NLD == n) load_one(q, ld_st, kb_ld);
       fence();
     }
   };
 
   // Pipeline over 128-wide slices kb (stage kb % 3): at the start of slice
   // kb, wait for this wave's loads of slice kb + 1 (slice kb + 2's may stay
-  // in flight) and for its reads of slice kb (returned: its MFMAs start
-  // now), then barrier: slice kb + 1 is in LDS for every wave and no wave
-  // reads stage (kb + 2) % 3 any more; the slice then issues the loads of
-  // slice kb + 3 into stage kb % 3... which holds slice kb, whose fragments
-  // are already in registers.  Slices at or past K load out of range
-  // (zeros, no traffic).  Fragment buffers alternate per slice: two slices
-  // per trip (a slice past K adds zeros).
+  // in flight) and for all its reads (slice kb's fragments and scales are
+  // in registers), then barrier: slice kb + 1 is in LDS for every wave and
+  // no wave reads stage kb % 3 any more; the slice then reads slice kb + 1
+  // and loads slice kb + 3 into stage kb % 3.  Slices at or past K load out
+  // of range (zeros, no traffic).  A fragment buffers alternate per slice:
+  // two slices per trip (a slice past K adds zeros).
 #pragma unroll
   for (int q = 0; q < F_NLD; ++q) load_one(q, 0, 0);
 #pragma unroll
@@ -207,7 +233,10 @@ __global__ __launch_bounds__(256) void gemm_fp8_tile(GemmArgs a, int tiles_m, in
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(F_NLD) : "memory");
   asm volatile("s_barrier" ::: "memory");
 #pragma unroll
-  for (int r = 0; r < NREAD; ++r) read_one(0, 0, r);
+  for (int i = 0; i < F_FM; ++i) read_a(0, 0, i);
+#pragma unroll
+  for (int j = 0; j < F_FN; ++j) read_b(0, j);
+  read_s(0);
 #pragma unroll
   for (int q = 0; q < F_NLD; ++q) load_one(q, 2, 2);
   for (int kb = 0; kb < nkb; kb += 2) {
@@ -224,7 +253,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_tile(GemmArgs a, int tiles_m, in
 
   // Epilogue: lane l holds column l & 15, rows 4 (l >> 4) + v of each block.
   __bf16* C = static_cast<__bf16*>(a.C);
-  const int64_t row0 = m0 + 64 * w + 4 * g, col0 = n0 + (lane & 15);
+  const int64_t row0 = m0 + 64 * wm + 4 * g, col0 = n0 + 64 * wn + (lane & 15);
 #pragma unroll
   for (int i = 0; i < F_FM; ++i)
 #pragma unroll
@@ -256,7 +285,7 @@ bool accepts(Op op, const GemmArgs& a) {
 
 hipError_t launch(Op, const GemmArgs& a, hipStream_t s) {
   const int tm = (int)cdiv(a.M, F_BM), tn = (int)cdiv(a.N, F_BN);
-  hipLaunchKernelGGL(gemm_fp8_tile, dim3(tm * tn), dim3(256), 0, s, a, tm, tn);
+  hipLaunchKernelGGL(gemm_fp8_tile, dim3(tm * tn), dim3(64 * F_WAVES), 0, s, a, tm, tn);
   return hipGetLastError();
 }
 
