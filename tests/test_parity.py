@@ -323,6 +323,52 @@ def test_skinny_split_k_deterministic_and_per_stream():
     assert np.array_equal(c1, c2) and np.array_equal(c1, c3)
 
 
+def _capture_skinny(stream, M, N, K, A, B, C):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        st = H.tg.tg_gemm_bf16(M, N, K, A.data_ptr(), K, 1, B.data_ptr(), 1, K, C.data_ptr(), N, 1,
+                               stream.cuda_stream)
+    return g
+
+
+def test_skinny_graph_capture():
+    """Under stream capture the skinny kernel allocates nothing: on a stream
+    without scratch it runs unsplit, on one that already has scratch it uses
+    it.  Both graphs, replayed several times with eager work in between,
+    give the eager result bit for bit (integer inputs: every split order
+    sums exactly)."""
+    M, N, K = 64, 2048, 4096
+    w = configs.Workload("t", "bf16", M, N, K, "nk", "normal", 77, 0)
+    d = configs.make_inputs(w, int_r=48)
+    A, B = H.dev(d["A"]), H.dev(d["B"])
+    H.log("skinny graph capture")
+    c_eager, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+    assert plan == SKINNY, plan
+    C_ref, _ = oracle.gemm("bf16", M, N, K, d["A"], K, 1, d["B"], 1, K)
+    H.assert_bit_exact("bf16", c_eager, C_ref, "skinny eager")
+    fresh, warm = torch.cuda.Stream(), torch.cuda.Stream()
+    C1 = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    C2 = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    # give `warm` its scratch with an eager call first
+    with torch.cuda.stream(warm):
+        H.tg.tg_gemm_bf16(M, N, K, A.data_ptr(), K, 1, B.data_ptr(), 1, K, C2.data_ptr(), N, 1,
+                          warm.cuda_stream)
+    torch.cuda.synchronize()
+    g1 = _capture_skinny(fresh, M, N, K, A, B, C1)
+    g2 = _capture_skinny(warm, M, N, K, A, B, C2)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        C1.zero_()
+        C2.zero_()
+        torch.cuda.synchronize()
+        g1.replay()
+        g2.replay()
+        torch.cuda.synchronize()
+        c1 = C1.cpu().numpy().view(np.uint16)
+        c2 = C2.cpu().numpy().view(np.uint16)
+        assert np.array_equal(c1, c_eager) and np.array_equal(c2, c_eager)
+
+
 # ------------------------------------------------------ K x N tile kernel
 
 NN_CASES = [(300, 512, 136), (513, 264, 72), (4000, 4000, 136), (256, 256, 64), (65, 8, 8),
