@@ -8,7 +8,9 @@ this module only marshals numpy arrays through ctypes.
 Every function is pinned by tests/test_oracle.py against identities,
 permutations, rank-1 closed forms, exact-integer brute force and NumPy's fp64
 matmul; the decoders and the rounding are pinned exhaustively against
-torch / numpy dtype conversions (tests/test_codecs.py).
+torch / numpy dtype conversions (tests/test_codecs.py); the fp8 block
+quantiser against torch's e4m3fn cast, numpy's fp32 division, the block
+invariants of its definition and the input generator's own quantiser.
 """
 from __future__ import annotations
 
@@ -50,6 +52,8 @@ class Oracle:
         lib.tg_oracle_round.restype = None
         lib.tg_oracle_decode.argtypes = [c_int, vp, i64, vp]
         lib.tg_oracle_decode.restype = None
+        lib.tg_oracle_quant_fp8.argtypes = [i64, i64, vp, i64, i64, vp, i64, vp, i64, i64]
+        lib.tg_oracle_quant_fp8.restype = c_int
         lib.tg_oracle_init()
         self.lib = lib
 
@@ -87,6 +91,19 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle: bad arguments")
         return C, S
+
+    def quant_fp8(self, X: np.ndarray, br: int):
+        """Block quantisation of an R x K fp32 matrix to e4m3fn codes with one
+        fp32 scale per br x 128 block, br = 1 or 128 (see oracle.c): returns
+        (codes R x K uint8, scales ceil(R / br) x ceil(K / 128) fp32)."""
+        X = np.ascontiguousarray(X, dtype=np.float32)
+        R, K = X.shape
+        Q = np.empty((R, K), np.uint8)
+        S = np.empty(((R + br - 1) // br, (K + 127) // 128), np.float32)
+        rc = self.lib.tg_oracle_quant_fp8(R, K, _p(X), K, br, _p(Q), K, _p(S), S.shape[1], 1)
+        if rc != 0:
+            raise ValueError("oracle: bad arguments")
+        return Q, S
 
     def round_to(self, fmt: str, x: np.ndarray) -> np.ndarray:
         """Round fp64 values to fp16 / bf16 codes, nearest-even (overflow -> inf)."""
@@ -137,6 +154,10 @@ def gemm_fp8_blockscaled(*args, **kw):
 
 def round_to(fmt, x):
     return default().round_to(fmt, x)
+
+
+def quant_fp8(X, br):
+    return default().quant_fp8(X, br)
 
 
 def decode(fmt, codes):

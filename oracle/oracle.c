@@ -225,6 +225,74 @@ static uint16_t encode_exact(double v, int ebits, int mbits) {
   return (uint16_t)(sign | ((uint32_t)E << mbits) | m);
 }
 
+/* ---- fp8 block quantisation ---------------------------------------------
+ * "TileKernels deep dive", section 7.2 (the fused RMSNorm + FP8 quantisation
+ * listing) and section 4.3 (E4M3 FN): per block the scale is the absolute
+ * maximum over 448, and the stored code is x / scale cast to E4M3.  Read
+ * here as:
+ *   amax = max |x| over the block (exact in fp32);
+ *   s    = amax / 448 rounded once to fp32 (the fp64 quotient rounded to
+ *          fp32 is the correctly rounded fp32 quotient: 53 >= 2 * 24 + 2);
+ *   if s = 0 (amax = 0, or the quotient underflows): s := 1, all codes 0;
+ *   y    = x / s rounded once to fp32 (same argument), clamped to
+ *          [-448, 448] (a subnormal s is coarse, so x / s can pass 448);
+ *   code = y rounded to the nearest e4m3fn value, ties to the even
+ *          fraction, sign kept (-0 and negatives that round to 0 give 0x80).
+ * Blocks are br x 128 (br = 1: one scale per 128-wide slice of a row; br =
+ * 128: one per 128 x 128 block); partial blocks at the edges have scales of
+ * their own.  X is R x K fp32 with leading dimension ldx, Q is R x K bytes
+ * with leading dimension ldq, S[ib, kb] at S[ib * ssr + kb * ssk]. */
+
+/* the code of v, a finite value on the e4m3fn grid: binary search of the
+ * decoded non-negative codes 0 .. 126 (increasing values) */
+static uint8_t e4m3_code_of(double v) {
+  double a = fabs(v);
+  int lo = 0, hi = 126;
+  while (lo < hi) {
+    int mid = (lo + hi) / 2;
+    if (tab_e4m3[mid] < a) lo = mid + 1;
+    else hi = mid;
+  }
+  return (uint8_t)(lo | (signbit(v) ? 0x80 : 0));
+}
+
+static double round_to_format(double x, int p, int emin, double maxf);
+
+int tg_oracle_quant_fp8(int64_t R, int64_t K, const float* X, int64_t ldx, int64_t br,
+                        uint8_t* Q, int64_t ldq, float* S, int64_t ssr, int64_t ssk) {
+  if (R < 0 || K < 0 || (br != 1 && br != 128)) return -1;
+  build_tables();
+  const int64_t nrb = (R + br - 1) / br, nkb = (K + 127) / 128;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t ib = 0; ib < nrb; ++ib) {
+    const int64_t r0 = ib * br, r1 = r0 + br < R ? r0 + br : R;
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+      const int64_t k0 = kb * 128, k1 = k0 + 128 < K ? k0 + 128 : K;
+      float amax = 0.0f;
+      for (int64_t r = r0; r < r1; ++r)
+        for (int64_t k = k0; k < k1; ++k) {
+          float a = fabsf(X[r * ldx + k]);
+          if (a > amax) amax = a;
+        }
+      float sc = (float)((double)amax / 448.0);
+      const int zero = sc == 0.0f;
+      S[ib * ssr + kb * ssk] = zero ? 1.0f : sc;
+      for (int64_t r = r0; r < r1; ++r)
+        for (int64_t k = k0; k < k1; ++k) {
+          if (zero) {
+            Q[r * ldq + k] = 0;
+            continue;
+          }
+          double y = (double)(float)((double)X[r * ldx + k] / (double)sc);
+          if (y > 448.0) y = 448.0;
+          if (y < -448.0) y = -448.0;
+          Q[r * ldq + k] = e4m3_code_of(round_to_format(y, 4, -6, 448.0));
+        }
+    }
+  }
+  return 0;
+}
+
 /* fmt 1: fp16 (p = 11, emin = -14, max 65504); fmt 2: bf16 (p = 8,
  * emin = -126, max (2 - 2^-7) * 2^127). */
 void tg_oracle_round(int fmt, const double* x, int64_t n, uint16_t* out) {

@@ -314,7 +314,119 @@ def pin_rounding(orc):
         lib_encode("f16", np.array([2048.0, 2052.0])).tolist(), "f16 ties"
 
 
+
+# ------------------------------------------------------- fp8 block quantiser
+
+def _fp32_div(a, b):
+    """IEEE fp32 quotient (numpy's float32 division)."""
+    return (np.float32(a) / np.float32(b)).astype(np.float32)
+
+
+def _blocks(R, K, br):
+    for ib in range((R + br - 1) // br):
+        for kb in range((K + 127) // 128):
+            yield ib, kb, slice(ib * br, min(R, ib * br + br)), slice(kb * 128, min(K, kb * 128 + 128))
+
+
+def pin_quant_codes_match_torch(orc):
+    """With 448 in every block the scale is exactly 1, so the codes are the
+    e4m3fn rounding of the inputs themselves: torch's float8_e4m3fn cast
+    (round to nearest even) must agree -- on every representable value, every
+    midpoint between neighbours (ties), random values, tiny values in the
+    subnormal range and signed zeros."""
+    pos = lib_decode("e4m3fn", np.arange(0, 127, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([pos, -pos, mids, -mids, rng.uniform(-448, 448, 4000),
+                           np.exp2(rng.uniform(-13, -5, 2000)) * rng.choice([-1, 1], 2000),
+                           [0.0, -0.0, 448.0, -448.0]]).astype(np.float32)
+    per = 127
+    rows = -(-vals.size // per)
+    X = np.zeros((rows, 128), np.float32)
+    X[:, 0] = 448.0
+    flat = np.zeros(rows * per, np.float32)
+    flat[:vals.size] = vals
+    X[:, 1:] = flat.reshape(rows, per)
+    for br in (1, 128):
+        Q, S = orc.quant_fp8(X, br)
+        assert np.all(S == 1.0), "scale of a block whose maximum is 448"
+        want = torch.from_numpy(X.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(Q, want), "e4m3fn rounding differs from torch's cast"
+
+
+def _quant_data(R, K, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((R, K)).astype(np.float32)
+    X *= np.exp2(rng.integers(-20, 20, (R, 1))).astype(np.float32)   # rows of varied scale
+    return X
+
+
+def pin_quant_scales_and_bounds(orc):
+    """Each scale is the fp32 quotient amax / 448 (numpy's IEEE division);
+    in every block the largest code decodes to +-448 exactly and every code
+    is within half an e4m3fn step of x / s (plus the fp32 quotient's own
+    rounding)."""
+    for R, K, br in ((130, 300, 1), (300, 257, 128), (1, 128, 1), (129, 1, 128)):
+        X = _quant_data(R, K, 100 + R + K)
+        Q, S = orc.quant_fp8(X, br)
+        dq = lib_decode("e4m3fn", Q)
+        for ib, kb, rs, ks in _blocks(R, K, br):
+            blk = X[rs, ks]
+            amax = np.abs(blk).max()
+            s = _fp32_div(amax, 448.0)
+            assert S[ib, kb] == s, (R, K, br, ib, kb)
+            d = dq[rs, ks]
+            assert np.abs(d).max() == 448.0, "the block maximum maps to 448"
+            y = np.abs(blk.astype(np.float64) / np.float64(s))
+            step = np.exp2(np.maximum(np.floor(np.log2(np.maximum(y, 2.0 ** -30))) - 3, -9))
+            assert np.all(np.abs(np.abs(d) - np.minimum(y, 448.0)) <= step / 2 + 448 * 2.0 ** -22)
+            assert np.all((d == 0) | (np.sign(d) == np.sign(blk)))
+
+
+def pin_quant_edge_blocks(orc):
+    """A zero block, and a block whose maximum over 448 underflows fp32, get
+    scale 1 and zero codes; a block whose scale is a coarse fp32 subnormal
+    (2 x 2^-149 for a maximum of 1075 x 2^-149) gives quotients above 448,
+    which clamp to 448, and rounds the rest on the e4m3fn grid."""
+    t = np.float32(2.0 ** -149)
+    X = np.zeros((3, 128), np.float32)
+    X[1, 5] = t                      # 2^-149 / 448 underflows
+    X[2, 0] = 1075 * t               # s = fl(1075/448 * 2^-149) = 2 * 2^-149
+    X[2, 1] = -300 * t               # -150 -> -144 on the grid
+    X[2, 2] = 32 * t                 # 16 exactly
+    Q, S = orc.quant_fp8(X, 1)
+    assert S[0, 0] == 1.0 and not Q[0].any()
+    assert S[1, 0] == 1.0 and not Q[1].any()
+    assert S[2, 0] == np.float32(2 * t)
+    got = lib_decode("e4m3fn", Q[2, :3])
+    assert list(got) == [448.0, -144.0, 16.0], got
+    assert not Q[2, 3:].any()
+
+
+def pin_quant_block_relation(orc):
+    """The 128 x 128 scale of a block is the largest of its rows' 1 x 128
+    scales (the maximum commutes with the monotone, correctly rounded
+    division)."""
+    X = _quant_data(300, 400, 7)
+    _, S1 = orc.quant_fp8(X, 1)
+    _, S2 = orc.quant_fp8(X, 128)
+    for ib in range(S2.shape[0]):
+        assert np.array_equal(S2[ib], S1[ib * 128:(ib + 1) * 128].max(axis=0))
+
+
+def pin_quant_matches_generator(orc):
+    """The input generator's own block quantiser (separate code, same
+    reading) agrees bit for bit on ordinary data."""
+    for R, K, br in ((200, 333, 1), (260, 384, 128)):
+        X = _quant_data(R, K, 3 + R)
+        Q, S = orc.quant_fp8(X, br)
+        Qg, Sg = gen.quant_e4m3fn(X, br, 128)
+        assert np.array_equal(Q, Qg) and np.array_equal(S, Sg)
+
+
 ALL_PINS = [pin_identity, pin_selection, pin_rank1, pin_all_ones, pin_bruteforce_integers,
             pin_bruteforce_rationals, pin_numpy_matmul, pin_layout_invariance, pin_row_subset,
             pin_nonnegative_s_equals_c, pin_fp8_unit_codes, pin_fp8_bruteforce,
-            pin_fp8_layout_and_rows, pin_decoders, pin_rounding]
+            pin_fp8_layout_and_rows, pin_decoders, pin_rounding, pin_quant_codes_match_torch,
+            pin_quant_scales_and_bounds, pin_quant_edge_blocks, pin_quant_block_relation,
+            pin_quant_matches_generator]

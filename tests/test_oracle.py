@@ -36,6 +36,14 @@ MUTATIONS = [
     ("e4m3 exponent bias", "(int)e - 7 - 3", "(int)e - 8 - 3"),
     ("rounding by truncation", "ldexp(nearbyint(ldexp(x, -q)), q)", "ldexp(trunc(ldexp(x, -q)), q)"),
     ("rounding ties away", "ldexp(nearbyint(ldexp(x, -q)), q)", "ldexp(round(ldexp(x, -q)), q)"),
+    ("quantiser scale over 447", "(double)amax / 448.0", "(double)amax / 447.0"),
+    ("zero block keeps scale 0", "S[ib * ssr + kb * ssk] = zero ? 1.0f : sc;",
+     "S[ib * ssr + kb * ssk] = sc;"),
+    ("128 x 128 blocks one row tall", "r1 = r0 + br < R ? r0 + br : R;", "r1 = r0 + 1 < R ? r0 + 1 : R;"),
+    ("quantiser drops the sign", "return (uint8_t)(lo | (signbit(v) ? 0x80 : 0));",
+     "return (uint8_t)lo;"),
+    ("quantiser amax of the first column only", "for (int64_t k = k0; k < k1; ++k) {\n          float a",
+     "for (int64_t k = k0; k < k0 + 1; ++k) {\n          float a"),
 ]
 
 
