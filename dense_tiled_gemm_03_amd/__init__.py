@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libtg_gemm.so")
 TG_SUCCESS, TG_ERR_INVALID_VALUE, TG_ERR_UNSUPPORTED, TG_ERR_LAUNCH = 0, 1, 2, 3
 OP_F16, OP_BF16, OP_FP8 = 0, 1, 2
 EXPORTS = ("tg_status_string", "tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8_blockscaled",
-           "tg_gemm_plan")
+           "tg_gemm_plan", "tg_quant_fp8_1x128", "tg_quant_fp8_128x128")
 
 
 class TgError(RuntimeError):
@@ -51,6 +51,9 @@ def load():
     lib.tg_gemm_fp8_blockscaled.restype = c_int
     lib.tg_gemm_plan.argtypes = [c_int, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64]
     lib.tg_gemm_plan.restype = ctypes.c_char_p
+    for name in ("tg_quant_fp8_1x128", "tg_quant_fp8_128x128"):
+        getattr(lib, name).argtypes = [i64, i64, vp, i64, vp, i64, vp, i64, i64, vp]
+        getattr(lib, name).restype = c_int
     _lib = lib
     return lib
 
@@ -85,6 +88,14 @@ def tg_gemm_fp8_blockscaled(M, N, K, A, sam, sak, SA, ssam, ssak, B, sbk, sbn, S
                             C, scm, scn, stream=0):
     return _check(load().tg_gemm_fp8_blockscaled(M, N, K, A, sam, sak, SA, ssam, ssak, B, sbk,
                                                  sbn, SB, ssbn, ssbk, C, scm, scn, stream))
+
+
+def tg_quant_fp8_1x128(R, K, X, ldx, Q, ldq, S, ssr, ssk, stream=0):
+    return _check(load().tg_quant_fp8_1x128(R, K, X, ldx, Q, ldq, S, ssr, ssk, stream))
+
+
+def tg_quant_fp8_128x128(R, K, X, ldx, Q, ldq, S, ssr, ssk, stream=0):
+    return _check(load().tg_quant_fp8_128x128(R, K, X, ldx, Q, ldq, S, ssr, ssk, stream))
 
 
 def tg_gemm_plan(op, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn):

@@ -1,0 +1,218 @@
+// Block quantisation of fp32 matrices to OCP E4M3FN codes plus fp32 scales,
+// the step that produces the operands of the block-scaled fp8 product:
+// "TileKernels deep dive", section 7.2 (per block, scale = absolute maximum
+// over 448 and code = x / scale cast to E4M3) and section 4.3 (the E4M3 FN
+// format).  Per block of 1 x 128 (a row slice, the A operand's scales) or
+// 128 x 128 (the B operand's scales):
+//   amax = max |x|;  s = amax / 448 (fp32, correctly rounded);
+//   s = 0 (zero block, or the quotient underflows): s := 1, all codes 0;
+//   code = e4m3fn round-to-nearest-even of clamp(x / s, -448, 448), where
+//          x / s is the correctly rounded fp32 quotient; the sign is kept.
+// Both kernels are bound by HBM (4 bytes read and 1 written per element):
+// every element is loaded once into registers, reduced for the block's
+// maximum and converted from there.
+#include "../../include/tg_gemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace tg {
+namespace {
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// e4m3fn code of y for |y| <= 448, round to nearest even, sign kept.  Below
+// 2^-6 the grid is the multiples of 2^-9 (subnormals, and 2^-6 itself as 8 =
+// exponent 1, fraction 0); above, the fp32 fraction is rounded to 3 bits at
+// bit 20 (a carry moves into the exponent) and the exponent rebiased from
+// 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    uint32_t ua = __float_as_uint(a);
+    ua += 0x7FFFFu + ((ua >> 20) & 1u);
+    code = (((ua >> 23) - 120u) << 3) | ((ua >> 20) & 7u);
+  }
+  return code | sign;
+}
+
+// The block's scale, and whether it is an all-zero block.
+__device__ __forceinline__ float block_scale(float amax, bool& zero) {
+  const float s = amax / 448.0f;
+  zero = s == 0.0f;
+  return zero ? 1.0f : s;
+}
+
+__device__ __forceinline__ uint32_t code_of(float x, float s, bool zero) {
+  if (zero) return 0u;
+  return e4m3_rne(fminf(fmaxf(x / s, -448.0f), 448.0f));
+}
+
+// 1 x 128 blocks: 16 lanes per block (8 elements each), 16 blocks per
+// workgroup, blocks numbered row-major (consecutive blocks of a row are
+// adjacent in memory).
+__global__ __launch_bounds__(256) void quant_1x128(int64_t R, int64_t K, const float* X,
+                                                   int64_t ldx, uint8_t* Q, int64_t ldq, float* S,
+                                                   int64_t ssr, int64_t ssk, int64_t nkb,
+                                                   bool vec) {
+  const int64_t blk = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int t16 = threadIdx.x & 15;
+  const bool live = blk < R * nkb;           // the 16-lane group has a block
+  const int64_t i = live ? blk / nkb : 0, kb = live ? blk % nkb : 0;
+  const int64_t k = kb * 128 + 8 * t16;
+  const bool full = live && kb * 128 + 128 <= K;
+  const float* x = X + i * ldx + k;
+  float v[8];
+  if (full && vec) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(x), hi = *reinterpret_cast<const f32x4*>(x + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = lo[e];
+      v[4 + e] = hi[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = live && k + e < K ? x[e] : 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+  if (!live) return;
+  bool zero;
+  const float s = block_scale(amax, zero);
+  uint32_t c[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c[e] = code_of(v[e], s, zero);
+  uint8_t* q = Q + i * ldq + k;
+  if (full && vec) {
+    const u32x2 packed = {c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
+                          c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24};
+    *reinterpret_cast<u32x2*>(q) = packed;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (k + e < K) q[e] = (uint8_t)c[e];
+  }
+  if (t16 == 0) S[i * ssr + kb * ssk] = s;
+}
+
+// 128 x 128 blocks: one workgroup per block; thread t takes columns
+// 8 (t % 16) .. +7 of rows t / 16 + 16 j (j < 8): 64 elements in registers.
+__global__ __launch_bounds__(256) void quant_128x128(int64_t R, int64_t K, const float* X,
+                                                     int64_t ldx, uint8_t* Q, int64_t ldq,
+                                                     float* S, int64_t ssr, int64_t ssk,
+                                                     int64_t nkb, bool vec) {
+  __shared__ float wmax[4];
+  const int64_t ib = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+  const int t = threadIdx.x, c8 = t & 15, rg = t >> 4;
+  const int64_t k = kb * 128 + 8 * c8;
+  const bool kfull = kb * 128 + 128 <= K;
+  float v[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t r = ib * 128 + rg + 16 * j;
+    const float* x = X + r * ldx + k;
+    if (r < R && kfull && vec) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(x), hi = *reinterpret_cast<const f32x4*>(x + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[j][e] = lo[e];
+        v[j][4 + e] = hi[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = r < R && k + e < K ? x[e] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  if ((t & 63) == 0) wmax[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  bool zero;
+  const float s = block_scale(amax, zero);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t r = ib * 128 + rg + 16 * j;
+    if (r >= R) continue;
+    uint32_t c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = code_of(v[j][e], s, zero);
+    uint8_t* q = Q + r * ldq + k;
+    if (kfull && vec) {
+      const u32x2 packed = {c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
+                            c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24};
+      *reinterpret_cast<u32x2*>(q) = packed;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k + e < K) q[e] = (uint8_t)c[e];
+    }
+  }
+  if (t == 0) S[ib * ssr + kb * ssk] = s;
+}
+
+bool ext_ok(int64_t n, int64_t stride) {
+  int64_t r;
+  return n <= 1 || !__builtin_mul_overflow(n - 1, stride, &r);
+}
+
+tg_status quant(int64_t br, int64_t R, int64_t K, const float* X, int64_t ldx, void* Q,
+                int64_t ldq, float* S, int64_t ssr, int64_t ssk, tg_stream_t stream) {
+  if (R < 0 || K < 0 || ldx < 0 || ldq < 0 || ssr < 0 || ssk < 0) return TG_ERR_INVALID_VALUE;
+  if (R == 0 || K == 0) return TG_SUCCESS;
+  if (X == nullptr || Q == nullptr || S == nullptr) return TG_ERR_INVALID_VALUE;
+  const int64_t nrb = cdiv(R, br), nkb = cdiv(K, 128);
+  if (R > 1 && (ldx < K || ldq < K)) return TG_ERR_INVALID_VALUE;  // rows would overlap
+  if ((nrb > 1 && ssr == 0) || (nkb > 1 && ssk == 0)) return TG_ERR_INVALID_VALUE;
+  if (!ext_ok(R, ldx) || !ext_ok(R, ldq) || !ext_ok(nrb, ssr) || !ext_ok(nkb, ssk))
+    return TG_ERR_INVALID_VALUE;
+  {
+    int64_t r;
+    if (__builtin_add_overflow((R - 1) * ldx, K, &r) || __builtin_add_overflow((R - 1) * ldq, K, &r) ||
+        __builtin_add_overflow((nrb - 1) * ssr, (nkb - 1) * ssk, &r))
+      return TG_ERR_INVALID_VALUE;
+  }
+  const int64_t groups = br == 1 ? cdiv(R * nkb, 16) : nrb * nkb;
+  if (groups >= (int64_t(1) << 31)) return TG_ERR_UNSUPPORTED;
+  // 16-byte fp32 reads and 8-byte code writes when every full block's rows
+  // are aligned so
+  const bool vec = ((reinterpret_cast<uintptr_t>(X) & 15) == 0) && ldx % 4 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(Q) & 7) == 0) && ldq % 8 == 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (br == 1)
+    hipLaunchKernelGGL(quant_1x128, dim3((unsigned)groups), dim3(256), 0, s, R, K, X, ldx,
+                       static_cast<uint8_t*>(Q), ldq, S, ssr, ssk, nkb, vec);
+  else
+    hipLaunchKernelGGL(quant_128x128, dim3((unsigned)groups), dim3(256), 0, s, R, K, X, ldx,
+                       static_cast<uint8_t*>(Q), ldq, S, ssr, ssk, nkb, vec);
+  return hipGetLastError() == hipSuccess ? TG_SUCCESS : TG_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace tg
+
+extern "C" {
+
+tg_status tg_quant_fp8_1x128(int64_t R, int64_t K, const float* X, int64_t ldx, void* Q,
+                             int64_t ldq, float* S, int64_t ssr, int64_t ssk, tg_stream_t stream) {
+  return tg::quant(1, R, K, X, ldx, Q, ldq, S, ssr, ssk, stream);
+}
+
+tg_status tg_quant_fp8_128x128(int64_t R, int64_t K, const float* X, int64_t ldx, void* Q,
+                               int64_t ldq, float* S, int64_t ssr, int64_t ssk,
+                               tg_stream_t stream) {
+  return tg::quant(128, R, K, X, ldx, Q, ldq, S, ssr, ssk, stream);
+}
+
+}  // extern "C"

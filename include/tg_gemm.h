@@ -112,6 +112,39 @@ tg_status tg_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
                                   const float* SB, int64_t ssbn, int64_t ssbk,
                                   void* C, int64_t scm, int64_t scn, tg_stream_t stream);
 
+/* Block quantisation of fp32 to OCP E4M3FN codes with fp32 scales -- the
+ * step that makes the operands of tg_gemm_fp8_blockscaled.  Per block the
+ * scale is the absolute maximum over 448 and each code is x / scale cast to
+ * E4M3 ("TileKernels deep dive", section 7.2, fused RMSNorm + FP8
+ * quantisation; section 4.3, the E4M3 FN format):
+ *   amax = max |x| over the block;  s = amax / 448, rounded to fp32;
+ *   if s == 0 (an all-zero block, or amax / 448 underflows): s = 1 and every
+ *     code of the block is 0;
+ *   otherwise code = e4m3fn(clamp(x / s, -448, 448)), x / s the rounded fp32
+ *     quotient, rounded to the nearest code with ties to the even fraction;
+ *     the sign is kept (0x80 for -0 and for negatives that round to 0).
+ * X (device, fp32): R x K, X[i,k] at X + i*ldx + k.  Q (device, bytes):
+ * Q[i,k] at Q + i*ldq + k.  S (device, fp32): S[ib, kb] at S + ib*ssr +
+ * kb*ssk, kb = k / 128 and
+ *   tg_quant_fp8_1x128:   ib = i        (one scale per 1 x 128 row slice: the
+ *                                        SA layout of the product),
+ *   tg_quant_fp8_128x128: ib = i / 128  (one per 128 x 128 block: the SB
+ *                                        layout for B stored N x K, R = N).
+ * Blocks at the right and bottom edges cover what is left and have scales of
+ * their own.  Inputs must be finite.  Errors: TG_ERR_INVALID_VALUE for a
+ * negative size or stride, a NULL pointer when R, K > 0, rows that would
+ * overlap (R > 1 and ldx < K or ldq < K), a zero scale stride along a
+ * dimension with more than one block, or an address range that overflows;
+ * TG_ERR_UNSUPPORTED for a grid beyond 2^31 workgroups; R == 0 or K == 0 is
+ * a no-op.  Q and S must not overlap X or each other.  Asynchronous on
+ * `stream`; nothing is allocated. */
+tg_status tg_quant_fp8_1x128(int64_t R, int64_t K, const float* X, int64_t ldx,
+                             void* Q, int64_t ldq, float* S, int64_t ssr, int64_t ssk,
+                             tg_stream_t stream);
+tg_status tg_quant_fp8_128x128(int64_t R, int64_t K, const float* X, int64_t ldx,
+                               void* Q, int64_t ldq, float* S, int64_t ssr, int64_t ssk,
+                               tg_stream_t stream);
+
 /* Name of the kernel a call with these arguments would launch ("none" for a
  * no-op, NULL if the arguments are invalid); nothing is launched.  op: 0 =
  * tg_gemm_f16, 1 = tg_gemm_bf16, 2 = tg_gemm_fp8_blockscaled (the scale

@@ -103,6 +103,30 @@ def test_fp8_unsupported_and_noop(lib):
     assert _call8(lib, M=0, SA=0, SB=0, A=0, B=0, C=0) == tg.TG_SUCCESS
 
 
+def _callq(lib, name, **kw):
+    a = dict(R=8, K=300, X=PA, ldx=300, Q=PB, ldq=300, S=PS, ssr=3, ssk=1)
+    a.update(kw)
+    return getattr(lib, name)(a["R"], a["K"], a["X"], a["ldx"], a["Q"], a["ldq"], a["S"],
+                              a["ssr"], a["ssk"], None)
+
+
+INVALIDQ = [dict(R=-1), dict(K=-1), dict(ldx=-1), dict(ssk=-1), dict(X=0), dict(Q=0), dict(S=0),
+            dict(ldx=299), dict(ldq=299), dict(ssk=0), dict(R=300, ssr=0),
+            dict(R=1 << 62, ldx=1 << 20)]
+
+
+@pytest.mark.parametrize("kw", INVALIDQ, ids=[str(k) for k in INVALIDQ])
+@pytest.mark.parametrize("name", ["tg_quant_fp8_1x128", "tg_quant_fp8_128x128"])
+def test_quant_invalid(lib, name, kw):
+    assert _callq(lib, name, **kw) == tg.TG_ERR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("name", ["tg_quant_fp8_1x128", "tg_quant_fp8_128x128"])
+def test_quant_noop(lib, name):
+    assert _callq(lib, name, R=0, X=0, Q=0, S=0) == tg.TG_SUCCESS
+    assert _callq(lib, name, K=0, X=0, Q=0, S=0) == tg.TG_SUCCESS
+
+
 def test_python_wrapper_raises(lib):
     with pytest.raises(tg.TgError) as e:
         tg.tg_gemm_bf16(-1, 8, 8, PA, 8, 1, PB, 8, 1, PC, 8, 1, 0)
