@@ -20,8 +20,6 @@
 namespace tg {
 namespace {
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
 // e4m3fn code of y for |y| <= 448, round to nearest even, sign kept.  Below
 // 2^-6 the grid is the multiples of 2^-9 (subnormals, and 2^-6 itself as 8 =
 // exponent 1, fraction 0); above, the fp32 fraction is rounded to 3 bits at
@@ -53,23 +51,14 @@ __device__ __forceinline__ uint32_t code_of(float x, float s, bool zero) {
   return e4m3_rne(fminf(fmaxf(x / s, -448.0f), 448.0f));
 }
 
-// 1 x 128 blocks: 16 lanes per block (8 elements each), 16 blocks per
-// workgroup, blocks numbered row-major (consecutive blocks of a row are
-// adjacent in memory).
-__global__ __launch_bounds__(256) void quant_1x128(int64_t R, int64_t K, const float* X,
-                                                   int64_t ldx, uint8_t* Q, int64_t ldq, float* S,
-                                                   int64_t ssr, int64_t ssk, int64_t nkb,
-                                                   bool vec) {
-  const int64_t blk = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int t16 = threadIdx.x & 15;
-  const bool live = blk < R * nkb;           // the 16-lane group has a block
-  const int64_t i = live ? blk / nkb : 0, kb = live ? blk % nkb : 0;
-  const int64_t k = kb * 128 + 8 * t16;
-  const bool full = live && kb * 128 + 128 <= K;
-  const float* x = X + i * ldx + k;
-  float v[8];
+// Element mapping inside a 128-wide row segment: lane t (of 16) holds
+// columns 4t .. 4t+3 and 64 + 4t .. 64 + 4t + 3, so each 16-byte load (and
+// each 4-byte code store) of 16 lanes covers one contiguous run.
+__device__ __forceinline__ void load_seg(const float* x, int t, int64_t k0, int64_t K, bool full,
+                                         bool vec, float* v) {
   if (full && vec) {
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(x), hi = *reinterpret_cast<const f32x4*>(x + 4);
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(x + 4 * t);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(x + 64 + 4 * t);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[e] = lo[e];
@@ -77,59 +66,99 @@ __global__ __launch_bounds__(256) void quant_1x128(int64_t R, int64_t K, const f
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = live && k + e < K ? x[e] : 0.0f;
+    for (int e = 0; e < 4; ++e) {
+      v[e] = k0 + 4 * t + e < K ? x[4 * t + e] : 0.0f;
+      v[4 + e] = k0 + 64 + 4 * t + e < K ? x[64 + 4 * t + e] : 0.0f;
+    }
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
-  if (!live) return;
-  bool zero;
-  const float s = block_scale(amax, zero);
-  uint32_t c[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) c[e] = code_of(v[e], s, zero);
-  uint8_t* q = Q + i * ldq + k;
-  if (full && vec) {
-    const u32x2 packed = {c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
-                          c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24};
-    *reinterpret_cast<u32x2*>(q) = packed;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (k + e < K) q[e] = (uint8_t)c[e];
-  }
-  if (t16 == 0) S[i * ssr + kb * ssk] = s;
 }
 
-// 128 x 128 blocks: one workgroup per block; thread t takes columns
-// 8 (t % 16) .. +7 of rows t / 16 + 16 j (j < 8): 64 elements in registers.
+__device__ __forceinline__ void store_seg(uint8_t* q, int t, int64_t k0, int64_t K, bool full,
+                                          bool vec, const uint32_t* c) {
+  if (full && vec) {
+    *reinterpret_cast<uint32_t*>(q + 4 * t) = c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24;
+    *reinterpret_cast<uint32_t*>(q + 64 + 4 * t) = c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (k0 + 4 * t + e < K) q[4 * t + e] = (uint8_t)c[e];
+      if (k0 + 64 + 4 * t + e < K) q[64 + 4 * t + e] = (uint8_t)c[4 + e];
+    }
+  }
+}
+
+// 1 x 128 blocks, numbered row-major (consecutive blocks of a row are
+// adjacent in memory): each 16-lane group takes QNB consecutive blocks and
+// loads all of them before reducing any, 16 groups per workgroup.
+constexpr int QNB = 4;
+
+__global__ __launch_bounds__(256) void quant_1x128(int64_t R, int64_t K, const float* X,
+                                                   int64_t ldx, uint8_t* Q, int64_t ldq, float* S,
+                                                   int64_t ssr, int64_t ssk, int64_t nkb,
+                                                   bool vec) {
+  const int t16 = threadIdx.x & 15;
+  const int64_t first = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * QNB;
+  const int64_t nblk = R * nkb;
+  int64_t i = first / nkb, kb = first % nkb;
+  int64_t row[QNB], col[QNB];
+  float v[QNB][8];
+#pragma unroll
+  for (int b = 0; b < QNB; ++b) {
+    row[b] = i;
+    col[b] = kb * 128;
+    const bool live = first + b < nblk;
+    const bool full = live && col[b] + 128 <= K;
+    if (live) {
+      load_seg(X + i * ldx + col[b], t16, col[b], K, full, vec, v[b]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[b][e] = 0.0f;
+    }
+    if (++kb == nkb) {
+      kb = 0;
+      ++i;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < QNB; ++b) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[b][e]));
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+    if (first + b >= nblk) continue;
+    bool zero;
+    const float s = block_scale(amax, zero);
+    uint32_t c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = code_of(v[b][e], s, zero);
+    const bool full = col[b] + 128 <= K;
+    store_seg(Q + row[b] * ldq + col[b], t16, col[b], K, full, vec, c);
+    if (t16 == 0) S[row[b] * ssr + (col[b] / 128) * ssk] = s;
+  }
+}
+
+// 128 x 128 blocks: one workgroup per block; thread t takes rows t / 16 +
+// 16 j (j < 8) of the block, lane t % 16 of each: 64 elements in registers.
 __global__ __launch_bounds__(256) void quant_128x128(int64_t R, int64_t K, const float* X,
                                                      int64_t ldx, uint8_t* Q, int64_t ldq,
                                                      float* S, int64_t ssr, int64_t ssk,
                                                      int64_t nkb, bool vec) {
   __shared__ float wmax[4];
   const int64_t ib = blockIdx.x / nkb, kb = blockIdx.x % nkb;
-  const int t = threadIdx.x, c8 = t & 15, rg = t >> 4;
-  const int64_t k = kb * 128 + 8 * c8;
-  const bool kfull = kb * 128 + 128 <= K;
+  const int t = threadIdx.x, t16 = t & 15, rg = t >> 4;
+  const int64_t k0 = kb * 128;
+  const bool kfull = k0 + 128 <= K;
   float v[8][8];
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t r = ib * 128 + rg + 16 * j;
-    const float* x = X + r * ldx + k;
-    if (r < R && kfull && vec) {
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(x), hi = *reinterpret_cast<const f32x4*>(x + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[j][e] = lo[e];
-        v[j][4 + e] = hi[e];
-      }
+    if (r < R) {
+      load_seg(X + r * ldx + k0, t16, k0, K, kfull, vec, v[j]);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[j][e] = r < R && k + e < K ? x[e] : 0.0f;
+      for (int e = 0; e < 8; ++e) v[j][e] = 0.0f;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
@@ -148,16 +177,7 @@ __global__ __launch_bounds__(256) void quant_128x128(int64_t R, int64_t K, const
     uint32_t c[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) c[e] = code_of(v[j][e], s, zero);
-    uint8_t* q = Q + r * ldq + k;
-    if (kfull && vec) {
-      const u32x2 packed = {c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
-                            c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24};
-      *reinterpret_cast<u32x2*>(q) = packed;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (k + e < K) q[e] = (uint8_t)c[e];
-    }
+    store_seg(Q + r * ldq + k0, t16, k0, K, kfull, vec, c);
   }
   if (t == 0) S[ib * ssr + kb * ssk] = s;
 }
@@ -183,12 +203,12 @@ tg_status quant(int64_t br, int64_t R, int64_t K, const float* X, int64_t ldx, v
         __builtin_add_overflow((nrb - 1) * ssr, (nkb - 1) * ssk, &r))
       return TG_ERR_INVALID_VALUE;
   }
-  const int64_t groups = br == 1 ? cdiv(R * nkb, 16) : nrb * nkb;
+  const int64_t groups = br == 1 ? cdiv(R * nkb, 16 * QNB) : nrb * nkb;
   if (groups >= (int64_t(1) << 31)) return TG_ERR_UNSUPPORTED;
-  // 16-byte fp32 reads and 8-byte code writes when every full block's rows
+  // 16-byte fp32 reads and 4-byte code writes when every full block's rows
   // are aligned so
   const bool vec = ((reinterpret_cast<uintptr_t>(X) & 15) == 0) && ldx % 4 == 0 &&
-                   ((reinterpret_cast<uintptr_t>(Q) & 7) == 0) && ldq % 8 == 0;
+                   ((reinterpret_cast<uintptr_t>(Q) & 3) == 0) && ldq % 4 == 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (br == 1)
     hipLaunchKernelGGL(quant_1x128, dim3((unsigned)groups), dim3(256), 0, s, R, K, X, ldx,
