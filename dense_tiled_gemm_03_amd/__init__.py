@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libtg_gemm.so")
 TG_SUCCESS, TG_ERR_INVALID_VALUE, TG_ERR_UNSUPPORTED, TG_ERR_LAUNCH = 0, 1, 2, 3
 OP_F16, OP_BF16, OP_FP8 = 0, 1, 2
 EXPORTS = ("tg_status_string", "tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8_blockscaled",
-           "tg_gemm_plan", "tg_quant_fp8_1x128", "tg_quant_fp8_128x128")
+           "tg_gemm_plan", "tg_quant_fp8_1x128", "tg_quant_fp8_128x128", "tg_gemm_grouped_f16",
+           "tg_gemm_grouped_bf16", "tg_gemm_grouped_plan")
 
 
 class TgError(RuntimeError):
@@ -51,6 +52,12 @@ def load():
     lib.tg_gemm_fp8_blockscaled.restype = c_int
     lib.tg_gemm_plan.argtypes = [c_int, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64]
     lib.tg_gemm_plan.restype = ctypes.c_char_p
+    sigg = [i64, vp, i64, i64, vp, i64, vp, i64, i64, vp, i64]
+    for name in ("tg_gemm_grouped_f16", "tg_gemm_grouped_bf16"):
+        getattr(lib, name).argtypes = sigg + [vp]
+        getattr(lib, name).restype = c_int
+    lib.tg_gemm_grouped_plan.argtypes = sigg
+    lib.tg_gemm_grouped_plan.restype = ctypes.c_char_p
     for name in ("tg_quant_fp8_1x128", "tg_quant_fp8_128x128"):
         getattr(lib, name).argtypes = [i64, i64, vp, i64, vp, i64, vp, i64, i64, vp]
         getattr(lib, name).restype = c_int
@@ -96,6 +103,31 @@ def tg_quant_fp8_1x128(R, K, X, ldx, Q, ldq, S, ssr, ssk, stream=0):
 
 def tg_quant_fp8_128x128(R, K, X, ldx, Q, ldq, S, ssr, ssk, stream=0):
     return _check(load().tg_quant_fp8_128x128(R, K, X, ldx, Q, ldq, S, ssr, ssk, stream))
+
+
+def _offsets(offsets):
+    """A host int64 array of the G + 1 group row offsets (kept alive by the
+    caller for the duration of the call)."""
+    import numpy as np
+    return np.ascontiguousarray(offsets, dtype=np.int64)
+
+
+def tg_gemm_grouped_f16(G, offsets, N, K, A, lda, B, ldb, sbg, C, ldc, stream=0):
+    off = _offsets(offsets)
+    return _check(load().tg_gemm_grouped_f16(G, off.ctypes.data, N, K, A, lda, B, ldb, sbg, C,
+                                             ldc, stream))
+
+
+def tg_gemm_grouped_bf16(G, offsets, N, K, A, lda, B, ldb, sbg, C, ldc, stream=0):
+    off = _offsets(offsets)
+    return _check(load().tg_gemm_grouped_bf16(G, off.ctypes.data, N, K, A, lda, B, ldb, sbg, C,
+                                              ldc, stream))
+
+
+def tg_gemm_grouped_plan(G, offsets, N, K, A, lda, B, ldb, sbg, C, ldc):
+    off = _offsets(offsets)
+    r = load().tg_gemm_grouped_plan(G, off.ctypes.data, N, K, A, lda, B, ldb, sbg, C, ldc)
+    return None if r is None else r.decode()
 
 
 def tg_gemm_plan(op, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn):

@@ -43,10 +43,13 @@ tg_status validate(const Call& c) {
       !extent_ok(a.N, a.sbn) || !extent_ok(a.M, a.scm))
     return TG_ERR_INVALID_VALUE;
   {
-    int64_t r;
-    if (__builtin_add_overflow((a.M - 1) * a.sam, (a.K > 0 ? a.K - 1 : 0) * a.sak, &r) ||
-        __builtin_add_overflow((a.K > 0 ? a.K - 1 : 0) * a.sbk, (a.N - 1) * a.sbn, &r) ||
-        __builtin_add_overflow((a.M - 1) * a.scm, a.N - 1, &r))
+    // largest element offsets; their byte addresses must not overflow either
+    const int64_t lim = int64_t(1) << 61;
+    int64_t ra, rb, rc;
+    if (__builtin_add_overflow((a.M - 1) * a.sam, (a.K > 0 ? a.K - 1 : 0) * a.sak, &ra) ||
+        __builtin_add_overflow((a.K > 0 ? a.K - 1 : 0) * a.sbk, (a.N - 1) * a.sbn, &rb) ||
+        __builtin_add_overflow((a.M - 1) * a.scm, a.N - 1, &rc) || ra >= lim || rb >= lim ||
+        rc >= lim)
       return TG_ERR_INVALID_VALUE;
   }
   if (c.op == Op::FP8) {

@@ -198,9 +198,12 @@ tg_status quant(int64_t br, int64_t R, int64_t K, const float* X, int64_t ldx, v
   if (!ext_ok(R, ldx) || !ext_ok(R, ldq) || !ext_ok(nrb, ssr) || !ext_ok(nkb, ssk))
     return TG_ERR_INVALID_VALUE;
   {
-    int64_t r;
-    if (__builtin_add_overflow((R - 1) * ldx, K, &r) || __builtin_add_overflow((R - 1) * ldq, K, &r) ||
-        __builtin_add_overflow((nrb - 1) * ssr, (nkb - 1) * ssk, &r))
+    // element extents; their byte addresses must not overflow either
+    const int64_t lim = int64_t(1) << 60;
+    int64_t ex, eq, es;
+    if (__builtin_add_overflow((R - 1) * ldx, K, &ex) || __builtin_add_overflow((R - 1) * ldq, K, &eq) ||
+        __builtin_add_overflow((nrb - 1) * ssr, (nkb - 1) * ssk, &es) || ex >= lim || eq >= lim ||
+        es >= lim)
       return TG_ERR_INVALID_VALUE;
   }
   const int64_t groups = br == 1 ? cdiv(R * nkb, 16 * QNB) : nrb * nkb;

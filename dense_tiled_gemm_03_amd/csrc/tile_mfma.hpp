@@ -138,9 +138,11 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm_siz
   tn = in / gm;
 }
 
-// BKN = false: B stored N x K (sbk = 1); true: B stored K x N (sbn = 1).
+// One output tile (tile row tm, tile column tn) of C = A * B: the K loop
+// and the epilogue.  BKN = false: B stored N x K (sbk = 1); true: B stored
+// K x N (sbn = 1).
 template <typename T, typename Cfg, bool BKN>
-__global__ __launch_bounds__(256) void gemm16_tile(GemmArgs a, int tiles_m, int tiles_n) {
+__device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn) {
   typedef typename Elem<T>::x8 T8;
   typedef typename Cfg::MMA MMA;
   typedef typename MMA::Acc Acc;
@@ -151,8 +153,6 @@ __global__ __launch_bounds__(256) void gemm16_tile(GemmArgs a, int tiles_m, int 
   const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
 
-  int tm, tn;
-  tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -381,6 +381,13 @@ __global__ __launch_bounds__(256) void gemm16_tile(GemmArgs a, int tiles_m, int 
           if (row < a.M && col < a.N) C[row * a.scm + col] = to_out<T>(acc[i][j][v]);
         }
   }
+}
+
+template <typename T, typename Cfg, bool BKN>
+__global__ __launch_bounds__(256) void gemm16_tile(GemmArgs a, int tiles_m, int tiles_n) {
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
+  tile_body<T, Cfg, BKN>(a, tm, tn);
 }
 
 }  // namespace tile

@@ -116,3 +116,22 @@ def make_inputs(w: Workload, int_r: int | None = None, M: int | None = None,
 def _f32_ints_to_e4m3(x: np.ndarray) -> np.ndarray:
     from . import round_e4m3fn
     return round_e4m3fn(x)
+
+
+def group_sizes(total: int, G: int, seed: int) -> np.ndarray:
+    """Row counts of G groups summing to `total`: a seeded uneven split (the
+    token counts of G experts).  Weights are 0.25 + u with u uniform from
+    (seed, stream 3); counts are floor(total * w / sum w) with the remainder
+    spread over the first groups."""
+    from . import draws
+    u = draws(seed, 3, G).astype(np.float64) / 2.0 ** 64
+    w = 0.25 + u
+    n = np.floor(total * w / w.sum()).astype(np.int64)
+    n[: total - int(n.sum())] += 1
+    return n
+
+
+# The grouped product measured by the benchmark: 8 experts over 8192 tokens,
+# N = 4096, K = 7168 (the 7168 hidden size), bf16, B_g stored N x K.
+GROUPED = {"name": "grouped_bf16_8x8192x4096x7168", "G": 8, "rows": 8192, "N": 4096, "K": 7168,
+           "seed": 6}

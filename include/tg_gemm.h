@@ -112,6 +112,36 @@ tg_status tg_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
                                   const float* SB, int64_t ssbn, int64_t ssbk,
                                   void* C, int64_t scm, int64_t scn, tg_stream_t stream);
 
+/* Grouped product: G independent products sharing N and K, group g with its
+ * own row count -- the grouped GEMM of the TileLang examples ("Getting to
+ * know TileLang", operator-coverage section), as used for the experts of a
+ * mixture-of-experts layer ("TileKernels deep dive", section 5).  For g < G:
+ *   C[i, j] = sum_k A[i, k] * B_g[k, j]   for offsets[g] <= i < offsets[g+1]
+ * A[i,k] at A + i*lda + k; B_g stored N x K: B_g[k,j] at B + g*sbg + j*ldb + k;
+ * C[i,j] at C + i*ldc + j (elements; fp16 or bf16, fp32 accumulation, one
+ * rounding, as for the single products).  `offsets` is a HOST array of G + 1
+ * non-decreasing row indices (groups may be empty).  One launch covers all
+ * groups when G <= 128, K % 8 == 0, lda, ldb, sbg are multiples of 8 and A,
+ * B are 16-byte aligned; other calls run group by group through
+ * tg_gemm_f16 / tg_gemm_bf16.  Errors: TG_ERR_INVALID_VALUE for negative
+ * sizes or strides, decreasing offsets or offsets[0] < 0, NULL pointers for
+ * non-empty extents, overlapping rows (more than one row of A or C with lda <
+ * K or ldc < N, N > 1 with ldb < K) or overflowing address ranges; G == 0, no
+ * rows or N == 0 is a no-op; K == 0 writes zeros.  C must not overlap A or
+ * B.  Asynchronous on `stream`; nothing is allocated. */
+tg_status tg_gemm_grouped_f16(int64_t G, const int64_t* offsets, int64_t N, int64_t K,
+                              const void* A, int64_t lda, const void* B, int64_t ldb,
+                              int64_t sbg, void* C, int64_t ldc, tg_stream_t stream);
+tg_status tg_gemm_grouped_bf16(int64_t G, const int64_t* offsets, int64_t N, int64_t K,
+                               const void* A, int64_t lda, const void* B, int64_t ldb,
+                               int64_t sbg, void* C, int64_t ldc, tg_stream_t stream);
+
+/* How a grouped call would run: "grouped_tile_nt_256x224" or "_256x256" (one
+ * launch), "per_group", "none" (no-op) or NULL (invalid arguments). */
+const char* tg_gemm_grouped_plan(int64_t G, const int64_t* offsets, int64_t N, int64_t K,
+                                 const void* A, int64_t lda, const void* B, int64_t ldb,
+                                 int64_t sbg, void* C, int64_t ldc);
+
 /* Block quantisation of fp32 to OCP E4M3FN codes with fp32 scales -- the
  * step that makes the operands of tg_gemm_fp8_blockscaled.  Per block the
  * scale is the absolute maximum over 448 and each code is x / scale cast to

@@ -127,6 +127,45 @@ def test_quant_noop(lib, name):
     assert _callq(lib, name, K=0, X=0, Q=0, S=0) == tg.TG_SUCCESS
 
 
+def _grouped(lib, fn, **kw):
+    import numpy as np
+    a = dict(G=2, off=[0, 100, 300], N=64, K=128, A=PA, lda=128, B=PB, ldb=128, sbg=64 * 128,
+             C=PC, ldc=64)
+    a.update(kw)
+    off = None if a["off"] is None else np.ascontiguousarray(a["off"], dtype=np.int64)
+    ptr = 0 if off is None else off.ctypes.data
+    args = [a["G"], ptr, a["N"], a["K"], a["A"], a["lda"], a["B"], a["ldb"], a["sbg"], a["C"],
+            a["ldc"]]
+    if fn == "plan":
+        r = lib.tg_gemm_grouped_plan(*args)
+        return None if r is None else r.decode()
+    return getattr(lib, fn)(*args, None)
+
+
+INVALIDG = [dict(G=-1), dict(N=-1), dict(K=-1), dict(lda=-1), dict(sbg=-1), dict(off=[0, 200, 100]),
+            dict(off=[-1, 100, 300]), dict(off=None), dict(lda=100), dict(ldc=63), dict(ldb=127),
+            dict(C=0), dict(A=0), dict(B=0), dict(G=2, sbg=1 << 62)]
+
+
+@pytest.mark.parametrize("kw", INVALIDG, ids=[str(k) for k in INVALIDG])
+@pytest.mark.parametrize("fn", ["tg_gemm_grouped_f16", "tg_gemm_grouped_bf16"])
+def test_grouped_invalid(lib, fn, kw):
+    assert _grouped(lib, fn, **kw) == tg.TG_ERR_INVALID_VALUE
+    assert _grouped(lib, "plan", **kw) is None
+
+
+def test_grouped_noop_and_plans(lib):
+    for kw in (dict(G=0, off=[0]), dict(off=[0, 0, 0]), dict(N=0)):
+        assert _grouped(lib, "tg_gemm_grouped_bf16", **kw) == tg.TG_SUCCESS
+        assert _grouped(lib, "plan", **kw) == "none"
+    assert _grouped(lib, "plan") == "grouped_tile_nt_256x224"
+    assert _grouped(lib, "plan", lda=129) == "per_group"          # rows not 16-byte multiples
+    assert _grouped(lib, "plan", K=100, lda=128, ldb=128) == "per_group"   # K % 8 != 0
+    assert _grouped(lib, "plan", G=129, off=list(range(0, 130 * 2, 2))) == "per_group"
+    assert _grouped(lib, "plan", off=[0, 2048, 4096], N=4096, ldc=4096,
+                    sbg=4096 * 128) == "grouped_tile_nt_256x256"
+
+
 def test_python_wrapper_raises(lib):
     with pytest.raises(tg.TgError) as e:
         tg.tg_gemm_bf16(-1, 8, 8, PA, 8, 1, PB, 8, 1, PC, 8, 1, 0)
