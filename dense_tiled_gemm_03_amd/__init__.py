@@ -19,7 +19,8 @@ TG_SUCCESS, TG_ERR_INVALID_VALUE, TG_ERR_UNSUPPORTED, TG_ERR_LAUNCH = 0, 1, 2, 3
 OP_F16, OP_BF16, OP_FP8 = 0, 1, 2
 EXPORTS = ("tg_status_string", "tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8_blockscaled",
            "tg_gemm_plan", "tg_quant_fp8_1x128", "tg_quant_fp8_128x128", "tg_gemm_grouped_f16",
-           "tg_gemm_grouped_bf16", "tg_gemm_grouped_plan")
+           "tg_gemm_grouped_bf16", "tg_gemm_grouped_plan", "tg_gemm_grouped_fp8_blockscaled",
+           "tg_gemm_grouped_fp8_plan")
 
 
 class TgError(RuntimeError):
@@ -58,6 +59,11 @@ def load():
         getattr(lib, name).restype = c_int
     lib.tg_gemm_grouped_plan.argtypes = sigg
     lib.tg_gemm_grouped_plan.restype = ctypes.c_char_p
+    sig8 = [i64, vp, i64, i64, vp, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, vp, i64]
+    lib.tg_gemm_grouped_fp8_blockscaled.argtypes = sig8 + [vp]
+    lib.tg_gemm_grouped_fp8_blockscaled.restype = c_int
+    lib.tg_gemm_grouped_fp8_plan.argtypes = sig8
+    lib.tg_gemm_grouped_fp8_plan.restype = ctypes.c_char_p
     for name in ("tg_quant_fp8_1x128", "tg_quant_fp8_128x128"):
         getattr(lib, name).argtypes = [i64, i64, vp, i64, vp, i64, vp, i64, i64, vp]
         getattr(lib, name).restype = c_int
@@ -127,6 +133,22 @@ def tg_gemm_grouped_bf16(G, offsets, N, K, A, lda, B, ldb, sbg, C, ldc, stream=0
 def tg_gemm_grouped_plan(G, offsets, N, K, A, lda, B, ldb, sbg, C, ldc):
     off = _offsets(offsets)
     r = load().tg_gemm_grouped_plan(G, off.ctypes.data, N, K, A, lda, B, ldb, sbg, C, ldc)
+    return None if r is None else r.decode()
+
+
+def tg_gemm_grouped_fp8_blockscaled(G, offsets, N, K, A, lda, SA, ssam, ssak, B, ldb, sbg, SB,
+                                    ssbn, ssbk, ssbg, C, ldc, stream=0):
+    off = _offsets(offsets)
+    return _check(load().tg_gemm_grouped_fp8_blockscaled(G, off.ctypes.data, N, K, A, lda, SA,
+                                                         ssam, ssak, B, ldb, sbg, SB, ssbn, ssbk,
+                                                         ssbg, C, ldc, stream))
+
+
+def tg_gemm_grouped_fp8_plan(G, offsets, N, K, A, lda, SA, ssam, ssak, B, ldb, sbg, SB, ssbn,
+                             ssbk, ssbg, C, ldc):
+    off = _offsets(offsets)
+    r = load().tg_gemm_grouped_fp8_plan(G, off.ctypes.data, N, K, A, lda, SA, ssam, ssak, B, ldb,
+                                        sbg, SB, ssbn, ssbk, ssbg, C, ldc)
     return None if r is None else r.decode()
 
 

@@ -41,6 +41,19 @@ const Variant* variant_tile_nn16();
 const Variant* variant_skinny16();
 const Variant* variant_tile_fp8();
 
+// Group table of a grouped product, passed with the kernel arguments: the
+// groups' first rows (in A and C) and first tile ids, and the strides from
+// one group's B (and B scales) to the next.
+constexpr int kMaxGroups = 128;
+struct GroupTable {
+  int G;
+  int tiles_n;
+  int64_t sbg;                        // elements between consecutive groups' B
+  int64_t ssbg;                       // fp32 scales between consecutive groups' B scales
+  int64_t row0[kMaxGroups + 1];
+  int tile0[kMaxGroups + 1];
+};
+
 // Scratch of at least `bytes` for kernels on `stream` (current device); its
 // leading completion counters are zero between kernels.  NULL when it cannot
 // be had (allocation failure, or the stream is being captured).

@@ -21,35 +21,11 @@
 namespace tg {
 namespace {
 
-constexpr int kMaxGroups = 128;
-
-struct GroupTable {
-  int G;
-  int tiles_n;
-  int64_t sbg;                        // elements from one group's B to the next
-  int64_t row0[kMaxGroups + 1];       // first row of each group in A and C
-  int tile0[kMaxGroups + 1];          // first tile id of each group
-};
-
 template <typename T, typename Cfg>
 __global__ __launch_bounds__(256) void gemm16_grouped(GemmArgs a, GroupTable gt) {
-  // XCD-contiguous tile ids (as for the single product)
-  const int nwg = gridDim.x, b = blockIdx.x;
-  const int xcd = b % tile::kXcds, local = b / tile::kXcds;
-  const int per = nwg / tile::kXcds, rem = nwg % tile::kXcds;
-  const int id = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-  // the group holding tile id (groups with no rows hold no tiles)
-  int g = 0;
-  while (g + 1 < gt.G && gt.tile0[g + 1] <= id) ++g;
-  const int t = id - gt.tile0[g];
+  int g, tm, tn;
+  tile::group_coords(gt, Cfg::BM, Cfg::GM, g, tm, tn);
   const int64_t rows = gt.row0[g + 1] - gt.row0[g];
-  const int tiles_m = (int)cdiv(rows, Cfg::BM);
-  // groups of GM tile rows, walked row-fastest, inside the group
-  const int span = Cfg::GM * gt.tiles_n;
-  const int first_m = (t / span) * Cfg::GM;
-  const int gm = min(Cfg::GM, tiles_m - first_m);
-  const int in = t - (t / span) * span;
-  const int tm = first_m + in % gm, tn = in / gm;
   GemmArgs ag = a;
   ag.M = rows;
   ag.A = static_cast<const T*>(a.A) + gt.row0[g] * a.sam;
@@ -137,6 +113,7 @@ tg_status launch_grouped(const Call& c, hipStream_t s) {
   gt.G = (int)c.G;
   gt.tiles_n = (int)cdiv(c.N, Cfg::BN);
   gt.sbg = c.sbg;
+  gt.ssbg = 0;
   int64_t tiles = 0;
   for (int64_t g = 0; g <= c.G; ++g) {
     gt.row0[g] = c.off[g] - c.off[0];

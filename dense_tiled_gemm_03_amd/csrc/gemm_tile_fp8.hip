@@ -34,6 +34,11 @@
 //  - edges as in the bf16 kernels: descriptors end at the last valid row,
 //    chunks past K read as zero, stores are masked; rows past M read zero
 //    scales.
+#include "../../include/tg_gemm.h"
+
+#include <initializer_list>
+#include <utility>
+
 #include "tile_mfma.hpp"
 
 namespace tg {
@@ -79,14 +84,13 @@ __device__ __forceinline__ void load_lds4s(const i32x4& desc, uint32_t lds, uint
                :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory");
 }
 
-__global__ __launch_bounds__(64 * F_WAVES) void gemm_fp8_tile(GemmArgs a, int tiles_m,
-                                                                int tiles_n) {
+// One 256 x 128 output tile (tile row tm, tile column tn): the K loop and the
+// epilogue.
+__device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn) {
   __shared__ __attribute__((aligned(1024))) char lds[F_STAGES * F_STAGE];
   const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
 
-  int tm, tn;
-  tile::tile_coords(tiles_m, tiles_n, 4, tm, tn);
   const int64_t m0 = (int64_t)tm * F_BM, n0 = (int64_t)tn * F_BN;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -265,6 +269,28 @@ __global__ __launch_bounds__(64 * F_WAVES) void gemm_fp8_tile(GemmArgs a, int ti
       }
 }
 
+__global__ __launch_bounds__(64 * F_WAVES) void gemm_fp8_tile(GemmArgs a, int tiles_m,
+                                                                int tiles_n) {
+  int tm, tn;
+  tile::tile_coords(tiles_m, tiles_n, 4, tm, tn);
+  fp8_tile_body(a, tm, tn);
+}
+
+// Grouped products (see gemm_grouped.hip): the tile's group re-bases A and
+// its row scales, B_g and its block scales, and C.
+__global__ __launch_bounds__(64 * F_WAVES) void gemm_fp8_grouped(GemmArgs a, GroupTable gt) {
+  int g, tm, tn;
+  tile::group_coords(gt, F_BM, 4, g, tm, tn);
+  GemmArgs ag = a;
+  ag.M = gt.row0[g + 1] - gt.row0[g];
+  ag.A = static_cast<const uint8_t*>(a.A) + gt.row0[g] * a.sam;
+  ag.SA = a.SA + gt.row0[g] * a.ssam;
+  ag.B = static_cast<const uint8_t*>(a.B) + g * gt.sbg;
+  ag.SB = a.SB + g * gt.ssbg;
+  ag.C = static_cast<__bf16*>(a.C) + gt.row0[g] * a.scm;
+  fp8_tile_body(ag, tm, tn);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // Both code operands K-contiguous with 16-byte aligned rows, K a multiple of
@@ -289,6 +315,108 @@ hipError_t launch(Op, const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+struct Grouped8 {
+  int64_t G;
+  const int64_t* off;
+  int64_t N, K;
+  const void* A;
+  int64_t lda;
+  const float* SA;
+  int64_t ssam, ssak;
+  const void* B;
+  int64_t ldb, sbg;
+  const float* SB;
+  int64_t ssbn, ssbk, ssbg;
+  void* C;
+  int64_t ldc;
+};
+
+// Largest element offset base + sum (n_i - 1) * stride_i + last, checked for
+// overflow and kept below 2^60 (byte addresses of fp32 scales included).
+bool extent_ok(std::initializer_list<std::pair<int64_t, int64_t>> dims, int64_t last) {
+  int64_t e = last, t;
+  for (auto d : dims) {
+    if (d.first <= 0) continue;
+    if (__builtin_mul_overflow(d.first - 1, d.second, &t) || __builtin_add_overflow(e, t, &e))
+      return false;
+  }
+  return e < (int64_t(1) << 60);
+}
+
+tg_status validate_grouped(const Grouped8& c) {
+  if (c.G < 0 || c.N < 0 || c.K < 0 || c.lda < 0 || c.ssam < 0 || c.ssak < 0 || c.ldb < 0 ||
+      c.sbg < 0 || c.ssbn < 0 || c.ssbk < 0 || c.ssbg < 0 || c.ldc < 0)
+    return TG_ERR_INVALID_VALUE;
+  if (c.G == 0) return TG_SUCCESS;
+  if (c.off == nullptr || c.off[0] < 0) return TG_ERR_INVALID_VALUE;
+  for (int64_t g = 0; g < c.G; ++g)
+    if (c.off[g + 1] < c.off[g]) return TG_ERR_INVALID_VALUE;
+  const int64_t rows = c.off[c.G];
+  if (rows == 0 || c.N == 0) return TG_SUCCESS;
+  if (c.C == nullptr) return TG_ERR_INVALID_VALUE;
+  if (c.K > 0 && (c.A == nullptr || c.B == nullptr || c.SA == nullptr || c.SB == nullptr))
+    return TG_ERR_INVALID_VALUE;
+  if ((rows > 1 && (c.lda < c.K || c.ldc < c.N)) || (c.N > 1 && c.ldb < c.K))
+    return TG_ERR_INVALID_VALUE;
+  const int64_t nkb = cdiv(c.K, 128), nnb = cdiv(c.N, 128);
+  if (!extent_ok({{rows, c.lda}}, c.K) || !extent_ok({{rows, c.ldc}}, c.N) ||
+      !extent_ok({{c.G, c.sbg}, {c.N, c.ldb}}, c.K) ||
+      !extent_ok({{rows, c.ssam}, {nkb, c.ssak}}, 1) ||
+      !extent_ok({{c.G, c.ssbg}, {nnb, c.ssbn}, {nkb, c.ssbk}}, 1) || rows >= (int64_t(1) << 60))
+    return TG_ERR_INVALID_VALUE;
+  return TG_SUCCESS;
+}
+
+// One launch when every group's call would take the tile kernel: at most
+// kMaxGroups groups, the single product's conditions, 16-byte aligned group
+// bases.
+bool grouped_tiled(const Grouped8& c) {
+  if (c.G > kMaxGroups || c.K == 0) return false;
+  if (c.sbg % 16 != 0) return false;
+  for (int64_t g = 0; g < c.G; ++g)
+    if (c.off[g + 1] - c.off[g] > (int64_t(1) << 24)) return false;
+  GemmArgs a{1, c.N, c.K, c.A, c.lda, 1, c.B, 1, c.ldb, c.SA, c.ssam, c.ssak, c.SB, c.ssbn,
+             c.ssbk, c.C, c.ldc};
+  return accepts(Op::FP8, a);
+}
+
+tg_status run_grouped(const Grouped8& c, tg_stream_t stream) {
+  tg_status st = validate_grouped(c);
+  if (st != TG_SUCCESS || c.G == 0 || c.off[c.G] == c.off[0] || c.N == 0) return st;
+  if (grouped_tiled(c)) {
+    GroupTable gt;
+    gt.G = (int)c.G;
+    gt.tiles_n = (int)cdiv(c.N, F_BN);
+    gt.sbg = c.sbg;
+    gt.ssbg = c.ssbg;
+    int64_t tiles = 0;
+    for (int64_t g = 0; g <= c.G; ++g) {
+      gt.row0[g] = c.off[g] - c.off[0];
+      gt.tile0[g] = (int)tiles;
+      if (g < c.G) tiles += cdiv(c.off[g + 1] - c.off[g], F_BM) * gt.tiles_n;
+    }
+    if (tiles >= (int64_t(1) << 31)) return TG_ERR_UNSUPPORTED;
+    const GemmArgs a{c.off[c.G] - c.off[0], c.N, c.K,
+                     static_cast<const uint8_t*>(c.A) + c.off[0] * c.lda, c.lda, 1, c.B, 1, c.ldb,
+                     c.SA + c.off[0] * c.ssam, c.ssam, c.ssak, c.SB, c.ssbn, c.ssbk,
+                     static_cast<__bf16*>(c.C) + c.off[0] * c.ldc, c.ldc};
+    hipLaunchKernelGGL(gemm_fp8_grouped, dim3((unsigned)tiles), dim3(64 * F_WAVES), 0,
+                       static_cast<hipStream_t>(stream), a, gt);
+    return hipGetLastError() == hipSuccess ? TG_SUCCESS : TG_ERR_LAUNCH;
+  }
+  for (int64_t g = 0; g < c.G; ++g) {
+    const int64_t m = c.off[g + 1] - c.off[g];
+    if (m == 0) continue;
+    st = tg_gemm_fp8_blockscaled(m, c.N, c.K, static_cast<const uint8_t*>(c.A) + c.off[g] * c.lda,
+                                 c.lda, 1, c.SA + c.off[g] * c.ssam, c.ssam, c.ssak,
+                                 static_cast<const uint8_t*>(c.B) + g * c.sbg, 1, c.ldb,
+                                 c.SB + g * c.ssbg, c.ssbn, c.ssbk,
+                                 static_cast<__bf16*>(c.C) + c.off[g] * c.ldc, c.ldc, 1, stream);
+    if (st != TG_SUCCESS) return st;
+  }
+  return TG_SUCCESS;
+}
+
 }  // namespace
 
 const Variant* variant_tile_fp8() {
@@ -297,3 +425,31 @@ const Variant* variant_tile_fp8() {
 }
 
 }  // namespace tg
+
+extern "C" {
+
+tg_status tg_gemm_grouped_fp8_blockscaled(int64_t G, const int64_t* offsets, int64_t N, int64_t K,
+                                          const void* A, int64_t lda, const float* SA,
+                                          int64_t ssam, int64_t ssak, const void* B, int64_t ldb,
+                                          int64_t sbg, const float* SB, int64_t ssbn,
+                                          int64_t ssbk, int64_t ssbg, void* C, int64_t ldc,
+                                          tg_stream_t stream) {
+  return tg::run_grouped(
+      tg::Grouped8{G, offsets, N, K, A, lda, SA, ssam, ssak, B, ldb, sbg, SB, ssbn, ssbk, ssbg, C,
+                   ldc},
+      stream);
+}
+
+const char* tg_gemm_grouped_fp8_plan(int64_t G, const int64_t* offsets, int64_t N, int64_t K,
+                                     const void* A, int64_t lda, const float* SA, int64_t ssam,
+                                     int64_t ssak, const void* B, int64_t ldb, int64_t sbg,
+                                     const float* SB, int64_t ssbn, int64_t ssbk, int64_t ssbg,
+                                     void* C, int64_t ldc) {
+  const tg::Grouped8 c{G, offsets, N, K, A, lda, SA, ssam, ssak, B, ldb, sbg, SB, ssbn, ssbk,
+                       ssbg, C, ldc};
+  if (tg::validate_grouped(c) != TG_SUCCESS) return nullptr;
+  if (G == 0 || offsets[G] == offsets[0] || N == 0) return "none";
+  return tg::grouped_tiled(c) ? "grouped_tile_fp8_256x128" : "per_group";
+}
+
+}  // extern "C"

@@ -138,6 +138,28 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm_siz
   tn = in / gm;
 }
 
+// Grouped products: the group of this workgroup's (XCD-contiguous) tile id
+// -- the last group whose first tile id is not above it; groups with no rows
+// hold no tiles -- and the tile's row and column inside the group, in
+// groups of gm_size tile rows walked row-fastest.
+__device__ __forceinline__ void group_coords(const GroupTable& gt, int bm, int gm_size, int& g,
+                                             int& tm, int& tn) {
+  const int G = gridDim.x, b = blockIdx.x;
+  const int xcd = b % kXcds, local = b / kXcds;
+  const int per = G / kXcds, rem = G % kXcds;
+  const int id = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  g = 0;
+  while (g + 1 < gt.G && gt.tile0[g + 1] <= id) ++g;
+  const int t = id - gt.tile0[g];
+  const int tiles_m = (int)cdiv(gt.row0[g + 1] - gt.row0[g], bm);
+  const int span = gm_size * gt.tiles_n;
+  const int first_m = (t / span) * gm_size;
+  const int gm = min(gm_size, tiles_m - first_m);
+  const int in = t - (t / span) * span;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
 // One output tile (tile row tm, tile column tn) of C = A * B: the K loop
 // and the epilogue.  BKN = false: B stored N x K (sbk = 1); true: B stored
 // K x N (sbn = 1).

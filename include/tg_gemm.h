@@ -136,6 +136,32 @@ tg_status tg_gemm_grouped_bf16(int64_t G, const int64_t* offsets, int64_t N, int
                                const void* A, int64_t lda, const void* B, int64_t ldb,
                                int64_t sbg, void* C, int64_t ldc, tg_stream_t stream);
 
+/* Grouped block-scaled fp8 product (e4m3fn codes, bf16 output) with the
+ * scale conventions of tg_gemm_fp8_blockscaled: A's row scales follow A's
+ * rows, SA[i, kb] at SA + i*ssam + kb*ssak; group g's B is B + g*sbg (stored
+ * N x K, leading dimension ldb, codes are bytes) and its block scales are
+ * SB_g[jb, kb] at SB + g*ssbg + jb*ssbn + kb*ssbk.  One launch covers all
+ * groups when G <= 128 and every group's call would take the fp8 tile kernel
+ * (K % 16 == 0, lda, ldb, sbg multiples of 16, A and B 16-byte aligned);
+ * other calls run group by group through tg_gemm_fp8_blockscaled.  Errors
+ * and no-ops as for the grouped fp16 / bf16 products (scale pointers and
+ * strides checked like the codes'). */
+tg_status tg_gemm_grouped_fp8_blockscaled(int64_t G, const int64_t* offsets, int64_t N,
+                                          int64_t K, const void* A, int64_t lda,
+                                          const float* SA, int64_t ssam, int64_t ssak,
+                                          const void* B, int64_t ldb, int64_t sbg,
+                                          const float* SB, int64_t ssbn, int64_t ssbk,
+                                          int64_t ssbg, void* C, int64_t ldc,
+                                          tg_stream_t stream);
+
+/* How a grouped fp8 call would run: "grouped_tile_fp8_256x128" (one launch),
+ * "per_group", "none" (no-op) or NULL (invalid arguments). */
+const char* tg_gemm_grouped_fp8_plan(int64_t G, const int64_t* offsets, int64_t N, int64_t K,
+                                     const void* A, int64_t lda, const float* SA, int64_t ssam,
+                                     int64_t ssak, const void* B, int64_t ldb, int64_t sbg,
+                                     const float* SB, int64_t ssbn, int64_t ssbk, int64_t ssbg,
+                                     void* C, int64_t ldc);
+
 /* How a grouped call would run: "grouped_tile_nt_256x224" or "_256x256" (one
  * launch), "per_group", "none" (no-op) or NULL (invalid arguments). */
 const char* tg_gemm_grouped_plan(int64_t G, const int64_t* offsets, int64_t N, int64_t K,

@@ -166,6 +166,40 @@ def test_grouped_noop_and_plans(lib):
                     sbg=4096 * 128) == "grouped_tile_nt_256x256"
 
 
+def _grouped8(lib, plan=False, **kw):
+    import numpy as np
+    a = dict(G=2, off=[0, 100, 300], N=64, K=128, A=PA, lda=128, SA=PS, ssam=1, ssak=1, B=PB,
+             ldb=128, sbg=64 * 128, SB=PS + 4096, ssbn=1, ssbk=1, ssbg=1, C=PC, ldc=64)
+    a.update(kw)
+    off = None if a["off"] is None else np.ascontiguousarray(a["off"], dtype=np.int64)
+    args = [a["G"], 0 if off is None else off.ctypes.data, a["N"], a["K"], a["A"], a["lda"],
+            a["SA"], a["ssam"], a["ssak"], a["B"], a["ldb"], a["sbg"], a["SB"], a["ssbn"],
+            a["ssbk"], a["ssbg"], a["C"], a["ldc"]]
+    if plan:
+        r = lib.tg_gemm_grouped_fp8_plan(*args)
+        return None if r is None else r.decode()
+    return lib.tg_gemm_grouped_fp8_blockscaled(*args, None)
+
+
+INVALIDG8 = INVALIDG + [dict(SA=0), dict(SB=0), dict(ssbg=-1), dict(ssak=-1),
+                        dict(ssbg=1 << 62)]
+
+
+@pytest.mark.parametrize("kw", INVALIDG8, ids=[str(k) for k in INVALIDG8])
+def test_grouped_fp8_invalid(lib, kw):
+    assert _grouped8(lib, **kw) == tg.TG_ERR_INVALID_VALUE
+    assert _grouped8(lib, plan=True, **kw) is None
+
+
+def test_grouped_fp8_noop_and_plans(lib):
+    for kw in (dict(G=0, off=[0]), dict(off=[0, 0, 0]), dict(N=0)):
+        assert _grouped8(lib, **kw) == tg.TG_SUCCESS
+        assert _grouped8(lib, plan=True, **kw) == "none"
+    assert _grouped8(lib, plan=True) == "grouped_tile_fp8_256x128"
+    assert _grouped8(lib, plan=True, lda=136) == "per_group"       # rows not 16-byte multiples
+    assert _grouped8(lib, plan=True, sbg=64 * 128 + 8) == "per_group"
+
+
 def test_python_wrapper_raises(lib):
     with pytest.raises(tg.TgError) as e:
         tg.tg_gemm_bf16(-1, 8, 8, PA, 8, 1, PB, 8, 1, PC, 8, 1, 0)
