@@ -1,7 +1,9 @@
 // Registration of the tuned tile kernel (tile_mfma.hpp) for B stored N x K
 // (both operands K-contiguous), the layout of the 4096 x 7168 x 16384 BF16
 // GEMM reported for the Ascend release in "Getting to know TileLang"
-// (six-piece section).
+// (six-piece section).  Products with too few tiles to fill the CUs (a
+// one-GPU shard of that product, 4096 x 896 x 16384, has 64) split K across
+// the workgroups of a tile.
 #include "tile_mfma.hpp"
 
 namespace tg {
@@ -27,9 +29,45 @@ bool accepts(Op op, const GemmArgs& a) {
   return true;
 }
 
+constexpr int64_t kCus = 256;
+
+// Split K when the tiles would fill fewer than half the CUs: as many splits
+// as bring the grid to about one workgroup per CU, at most 8, with at least
+// 8 K slices (of 64) per split.
+template <typename Cfg>
+int splits_for(const GemmArgs& a) {
+  const int64_t tiles = cdiv(a.M, Cfg::BM) * cdiv(a.N, Cfg::BN);
+  if (2 * tiles > kCus) return 1;
+  int64_t s = kCus / tiles;
+  if (s > 8) s = 8;
+  if (s > cdiv(a.K, 64) / 8) s = cdiv(a.K, 64) / 8;
+  return s < 2 ? 1 : (int)s;
+}
+
 template <typename Cfg>
 hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
   const int tm = (int)cdiv(a.M, Cfg::BM), tn = (int)cdiv(a.N, Cfg::BN);
+  const int splits = splits_for<Cfg>(a);
+  if (splits > 1) {
+    // scratch: per-tile counters, then each split's fp32 partial tile
+    const size_t tiles = (size_t)tm * tn;
+    const size_t cnt_bytes = (tiles * 4 + 255) & ~size_t(255);
+    const size_t part_bytes = (size_t)Cfg::BM * Cfg::BN * 4 * splits * tiles;
+    char* ws = static_cast<char*>(stream_workspace(s, cnt_bytes + part_bytes));
+    if (ws != nullptr) {
+      int* counters = reinterpret_cast<int*>(ws);
+      float* part = reinterpret_cast<float*>(ws + cnt_bytes);
+      const dim3 grid((unsigned)(tiles * splits)), block(256);
+      if (op == Op::BF16)
+        hipLaunchKernelGGL((tile::gemm16_tile_splitk<__bf16, Cfg>), grid, block, 0, s, a, tm, tn,
+                           splits, part, counters);
+      else
+        hipLaunchKernelGGL((tile::gemm16_tile_splitk<_Float16, Cfg>), grid, block, 0, s, a, tm,
+                           tn, splits, part, counters);
+      return hipGetLastError();
+    }
+    // no scratch to be had (stream capture, allocation failure): unsplit
+  }
   const dim3 grid(tm * tn), block(256);
   if (op == Op::BF16)
     hipLaunchKernelGGL((tile::gemm16_tile<__bf16, Cfg, false>), grid, block, 0, s, a, tm, tn);
@@ -42,7 +80,6 @@ hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
 // each wave costs about one tile's MFMA work, so pick the shape with the
 // smaller waves x tile area (4096 x 7168: 256 x 224 gives 512 tiles = 2 full
 // waves, 256 x 256 gives 448 tiles = 1.75 waves rounded up to 2).
-constexpr int64_t kCus = 256;
 int64_t cost(const GemmArgs& a, int64_t bm, int64_t bn) {
   return cdiv(cdiv(a.M, bm) * cdiv(a.N, bn), kCus) * bm * bn;
 }
@@ -52,7 +89,18 @@ hipError_t launch(Op op, const GemmArgs& a, hipStream_t s) {
   return use224(a) ? launch_cfg<Tile224>(op, a, s) : launch_cfg<Tile256>(op, a, s);
 }
 
-const char* name_of(const GemmArgs& a) { return use224(a) ? "tile_nt_256x224" : "tile_nt_256x256"; }
+// plan names, by tile shape and split count (1 .. 8)
+const char* const kNames224[] = {"tile_nt_256x224", "tile_nt_256x224", "tile_nt_256x224_splitk2",
+                                 "tile_nt_256x224_splitk3", "tile_nt_256x224_splitk4",
+                                 "tile_nt_256x224_splitk5", "tile_nt_256x224_splitk6",
+                                 "tile_nt_256x224_splitk7", "tile_nt_256x224_splitk8"};
+const char* const kNames256[] = {"tile_nt_256x256", "tile_nt_256x256", "tile_nt_256x256_splitk2",
+                                 "tile_nt_256x256_splitk3", "tile_nt_256x256_splitk4",
+                                 "tile_nt_256x256_splitk5", "tile_nt_256x256_splitk6",
+                                 "tile_nt_256x256_splitk7", "tile_nt_256x256_splitk8"};
+const char* name_of(const GemmArgs& a) {
+  return use224(a) ? kNames224[splits_for<Tile224>(a)] : kNames256[splits_for<Tile256>(a)];
+}
 
 }  // namespace
 

@@ -122,14 +122,19 @@ __device__ __forceinline__ void load_lds16(const i32x4& desc, uint32_t lds, uint
                :: "s"(lds), "v"(voff), "s"(desc) : "memory");
 }
 
-// Tile id -> (tile row, tile column): XCD-contiguous ids, then groups of GM
-// tile rows walked row-fastest.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm_size, int& tm,
-                                            int& tn) {
+// This workgroup's id with the ids of each XCD (the hardware places
+// workgroup b on XCD b % 8) made contiguous.
+__device__ __forceinline__ int xcd_id() {
   const int G = gridDim.x, b = blockIdx.x;
   const int xcd = b % kXcds, local = b / kXcds;
   const int per = G / kXcds, rem = G % kXcds;
-  const int id = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// Tile id -> (tile row, tile column): groups of GM tile rows walked
+// row-fastest.
+__device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int gm_size, int& tm,
+                                        int& tn) {
   const int span = gm_size * tiles_n;
   const int group = id / span, first_m = group * gm_size;
   const int gm = min(gm_size, tiles_m - first_m);
@@ -137,6 +142,20 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm_siz
   tm = first_m + in % gm;
   tn = in / gm;
 }
+
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm_size, int& tm,
+                                            int& tn) {
+  tile_of(xcd_id(), tiles_m, tiles_n, gm_size, tm, tn);
+}
+
+// Split of K across the workgroups of one tile: this workgroup's split of
+// `splits`, the tile's id, and the scratch that combines the partial tiles
+// (per-tile counters, fp32 partial tiles).  splits == 1: no split.
+struct SplitK {
+  int splits, split, tile;
+  float* part;
+  int* counters;
+};
 
 // Grouped products: the group of this workgroup's (XCD-contiguous) tile id
 // -- the last group whose first tile id is not above it; groups with no rows
@@ -163,8 +182,9 @@ __device__ __forceinline__ void group_coords(const GroupTable& gt, int bm, int g
 // One output tile (tile row tm, tile column tn) of C = A * B: the K loop
 // and the epilogue.  BKN = false: B stored N x K (sbk = 1); true: B stored
 // K x N (sbn = 1).
-template <typename T, typename Cfg, bool BKN>
-__device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn) {
+template <typename T, typename Cfg, bool BKN, bool SPLIT = false>
+__device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
+                                          const SplitK& sk = SplitK{1, 0, 0, nullptr, nullptr}) {
   typedef typename Elem<T>::x8 T8;
   typedef typename Cfg::MMA MMA;
   typedef typename MMA::Acc Acc;
@@ -180,6 +200,13 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int wm = w >> 1, wn = w & 1;
   const int K = (int)a.K;
+  // This workgroup's slices [kb0, kb1) of the K loop (all of them without a
+  // split); loads at or past k_lim read zeros.
+  static_assert(!(BKN && SPLIT), "split K takes B stored N x K");
+  const int nk = (K + BK - 1) / BK;
+  const int kb0 = SPLIT ? (int)((int64_t)sk.split * nk / sk.splits) : 0;
+  const int kb1 = SPLIT ? (int)((int64_t)(sk.split + 1) * nk / sk.splits) : nk;
+  const int k_lim = SPLIT ? min(K, kb1 * BK) : K;
   const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)(BKN ? a.sbk : a.sbn);
 
   // Operand tiles as buffer descriptors that end at the last valid element:
@@ -222,7 +249,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn) {
   };
 
   auto load_stage = [&](int st, int k0) {
-    const bool kin = k0 + 8 * lchunk < K;
+    const bool kin = k0 + 8 * lchunk < k_lim;
     const uint32_t base = lds32 + st * Cfg::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < Cfg::A_LOADS; ++i)
@@ -323,7 +350,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn) {
   // reads (<= 15, the lgkmcnt limit) in flight.
   auto substep = [&](auto loads_c, int cur, int nst, int nsub, int ld_st, int ld_k0) {
     constexpr bool LOADS = decltype(loads_c)::value;
-    const bool kin = ld_k0 + 8 * lchunk < K;
+    const bool kin = ld_k0 + 8 * lchunk < k_lim;
     const uint32_t ld_base = lds32 + ld_st * Cfg::STAGE_BYTES;
 #pragma unroll
     for (int n = 0; n < FM * FN; ++n) {
@@ -357,17 +384,16 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn) {
   //     kt+2 -> stage st.
   // Slices at or past K are fetched with out-of-range offsets: they move no
   // data, fill the idle stage with zeros and keep the loop free of branches.
-  const int nk = (K + BK - 1) / BK;
-  load_stage(0, 0);
-  load_stage(1, BK);
+  load_stage(0, kb0 * BK);
+  load_stage(1, (kb0 + 1) * BK);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");
   __syncthreads();
   {
 #pragma unroll
     for (int r = 0; r < NRD; ++r) read_one(0, 0, 0, r);
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
+  for (int kt = kb0; kt < kb1; ++kt) {
+    const int st = (kt - kb0) & 1;
 #pragma unroll
     for (int sub = 0; sub < SUBS - 1; ++sub) {
       fence();
@@ -377,6 +403,61 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn) {
     __syncthreads();
     fence();
     substep(std::true_type(), (SUBS - 1) & 1, st ^ 1, 0, st, (kt + 2) * BK);
+  }
+
+  if constexpr (SPLIT) {
+    // Publish this split's fp32 partial tile -- accumulator float4 q of
+    // thread t at float4 index (split * NQ + q) * 256 + t of the tile's
+    // slots, 16-byte runs contiguous across threads -- with device-coherent
+    // (sc1) stores; every wave waits for its stores before the barrier that
+    // precedes the tile's counter increment, so the split that finishes last
+    // reads every slot whole.  It adds the slots in split order (the result
+    // does not depend on which split finishes last), clears the counter and
+    // goes on to the epilogue with the sums.
+    constexpr int NV = MMA::NACC / 4, NQ = FM * FN * NV;
+    const int t = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        sk.part + (int64_t)sk.tile * sk.splits * NQ * 256 * 4, (short)0,
+        sk.splits * NQ * 256 * 16, 0x00020000);
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          const f32x4 x = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
+                           acc[i][j][4 * c + 3]};
+          const int q = (i * FN + j) * NV + c;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rp,
+                                                 ((sk.split * NQ + q) * 256 + t) * 16, 0, 0x10);
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __shared__ int last;
+    if (t == 0) last = atomicAdd(sk.counters + sk.tile, 1) == sk.splits - 1;
+    __syncthreads();
+    if (!last) return;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < MMA::NACC; ++v) acc[i][j][v] = 0.0f;
+      for (int sp = 0; sp < sk.splits; ++sp)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int c = 0; c < NV; ++c) {
+            const int q = (i * FN + j) * NV + c;
+            const f32x4 x = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, ((sp * NQ + q) * 256 + t) * 16,
+                                                             0, 0x10));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * c + e] += x[e];
+          }
+    }
+    if (t == 0) __hip_atomic_store(sk.counters + sk.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // Epilogue: round each accumulator to the output type and store it inside
@@ -410,6 +491,19 @@ __global__ __launch_bounds__(256) void gemm16_tile(GemmArgs a, int tiles_m, int 
   int tm, tn;
   tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
   tile_body<T, Cfg, BKN>(a, tm, tn);
+}
+
+// Split K: `splits` consecutive workgroups per tile, each over its share of
+// the K slices, combined through scratch (see SplitK): for products with too
+// few tiles to fill the CUs.
+template <typename T, typename Cfg>
+__global__ __launch_bounds__(256) void gemm16_tile_splitk(GemmArgs a, int tiles_m, int tiles_n,
+                                                          int splits, float* part, int* counters) {
+  const int id = xcd_id();
+  const int tile = id / splits;
+  int tm, tn;
+  tile_of(tile, tiles_m, tiles_n, Cfg::GM, tm, tn);
+  tile_body<T, Cfg, false, true>(a, tm, tn, SplitK{splits, id % splits, tile, part, counters});
 }
 
 }  // namespace tile

@@ -277,6 +277,54 @@ def test_tile_nt_padded_leading_dims():
     assert plan.startswith("tile_nt"), plan
 
 
+# ---------------------------------------------------- split-K tile kernel
+
+# (M, N, K, expected plan): too few tiles to fill the CUs, so K is split
+# across each tile's workgroups; ragged M, N and K tails.
+SPLITK_CASES = [
+    (300, 500, 4096, "tile_nt_256x224_splitk8"),
+    (257, 223, 1032, "tile_nt_256x224_splitk2"),
+    (65, 100, 2048, "tile_nt_256x224_splitk4"),
+    (1024, 1024, 4104, "tile_nt_256x224_splitk8"),
+]
+
+
+@pytest.mark.parametrize("case", SPLITK_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SPLITK_CASES])
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_tile_nt_split_k(fmt, case):
+    M, N, K, want = case
+    plan = _check16(fmt, M, N, K, "nk", seed=1500 + M + N + K)
+    assert plan == want, plan
+    r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
+    plan = _check16(fmt, M, N, K, "nk", seed=1600 + M + N + K, int_r=r)
+    assert plan == want, plan
+
+
+def test_split_k_shard_shape():
+    """One GPU's N-shard of the 4096 x 7168 x 16384 product, 4096 x 896 x
+    16384 (64 tiles): split 4 ways; sampled rows within the bound, integer
+    inputs bit-exact, two runs (and a second stream) bit-identical."""
+    M, N, K = 4096, 896, 16384
+    w = configs.Workload("shard", "bf16", M, N, K, "nk", "normal_sqrtk", 3, 256)
+    rows = gen.sample_rows(M, 256, 3)
+    d = configs.make_inputs(w)
+    A, B = H.dev(d["A"]), H.dev(d["B"])
+    H.log("split-K shard 4096x896x16384")
+    c1, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+    assert plan == "tile_nt_256x224_splitk4", plan
+    C_ref, S = oracle.gemm("bf16", M, N, K, d["A"], K, 1, d["B"], 1, K, rows=rows)
+    H.assert_within_bound("bf16", c1[rows], C_ref, S, f"shard [{plan}]")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c2, _ = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(c1, c2)
+    d = configs.make_inputs(w, int_r=32)
+    c, _ = H.run16("bf16", M, N, K, H.dev(d["A"]), K, 1, H.dev(d["B"]), 1, K)
+    C_ref, _ = oracle.gemm("bf16", M, N, K, d["A"], K, 1, d["B"], 1, K, rows=rows)
+    H.assert_bit_exact("bf16", c[rows], C_ref, "shard int")
+
+
 # ------------------------------------------------------------ skinny kernel
 
 # (M, N, K): one split (short K) and split-K across workgroups (K of 16 or
