@@ -33,14 +33,27 @@ constexpr int64_t kCus = 256;
 
 // Split K when the tiles would fill fewer than half the CUs: as many splits
 // as bring the grid to about one workgroup per CU, at most 8, with at least
-// 8 K slices (of 64) per split.
+// 8 K slices (of 64) per split.  Each split past the first adds about two
+// K slices' time to the combine (the last split of a tile reads the others'
+// partials, latency-bound at about 65 GB/s on one CU), so nk / S slices plus
+// 2 (S - 1) is smallest near S = sqrt(nk / 2), the last cap.  Only the
+// 256 x 224 tile splits: a grid that
+// small is a single wave for either shape, where 256 x 224 always costs less
+// (see use224 below), so the 256 x 256 tile only runs grids too large to
+// split.
+template <typename Cfg>
+constexpr bool kSplitsK = std::is_same<Cfg, Tile224>::value;
+
 template <typename Cfg>
 int splits_for(const GemmArgs& a) {
+  if (!kSplitsK<Cfg>) return 1;
   const int64_t tiles = cdiv(a.M, Cfg::BM) * cdiv(a.N, Cfg::BN);
   if (2 * tiles > kCus) return 1;
   int64_t s = kCus / tiles;
-  if (s > 8) s = 8;
-  if (s > cdiv(a.K, 64) / 8) s = cdiv(a.K, 64) / 8;
+  if (s > tile::kMaxSplits) s = tile::kMaxSplits;
+  const int64_t nk = cdiv(a.K, 64);
+  if (s > nk / 8) s = nk / 8;
+  while (s > 1 && 2 * s * s > nk) --s;
   return s < 2 ? 1 : (int)s;
 }
 
@@ -48,7 +61,8 @@ template <typename Cfg>
 hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
   const int tm = (int)cdiv(a.M, Cfg::BM), tn = (int)cdiv(a.N, Cfg::BN);
   const int splits = splits_for<Cfg>(a);
-  if (splits > 1) {
+  if constexpr (kSplitsK<Cfg>) {
+   if (splits > 1) {
     // scratch: per-tile counters, then each split's fp32 partial tile
     const size_t tiles = (size_t)tm * tn;
     const size_t cnt_bytes = (tiles * 4 + 255) & ~size_t(255);
@@ -67,6 +81,7 @@ hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
       return hipGetLastError();
     }
     // no scratch to be had (stream capture, allocation failure): unsplit
+   }
   }
   const dim3 grid(tm * tn), block(256);
   if (op == Op::BF16)
@@ -89,17 +104,13 @@ hipError_t launch(Op op, const GemmArgs& a, hipStream_t s) {
   return use224(a) ? launch_cfg<Tile224>(op, a, s) : launch_cfg<Tile256>(op, a, s);
 }
 
-// plan names, by tile shape and split count (1 .. 8)
+// plan names of the 256 x 224 tile, by split count (1 .. 8)
 const char* const kNames224[] = {"tile_nt_256x224", "tile_nt_256x224", "tile_nt_256x224_splitk2",
                                  "tile_nt_256x224_splitk3", "tile_nt_256x224_splitk4",
                                  "tile_nt_256x224_splitk5", "tile_nt_256x224_splitk6",
                                  "tile_nt_256x224_splitk7", "tile_nt_256x224_splitk8"};
-const char* const kNames256[] = {"tile_nt_256x256", "tile_nt_256x256", "tile_nt_256x256_splitk2",
-                                 "tile_nt_256x256_splitk3", "tile_nt_256x256_splitk4",
-                                 "tile_nt_256x256_splitk5", "tile_nt_256x256_splitk6",
-                                 "tile_nt_256x256_splitk7", "tile_nt_256x256_splitk8"};
 const char* name_of(const GemmArgs& a) {
-  return use224(a) ? kNames224[splits_for<Tile224>(a)] : kNames256[splits_for<Tile256>(a)];
+  return use224(a) ? kNames224[splits_for<Tile224>(a)] : "tile_nt_256x256";
 }
 
 }  // namespace

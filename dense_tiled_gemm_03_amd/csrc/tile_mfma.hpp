@@ -179,6 +179,79 @@ __device__ __forceinline__ void group_coords(const GroupTable& gt, int bm, int g
   tn = in / gm;
 }
 
+// Split K: at most this many workgroups share one output tile.
+constexpr int kMaxSplits = 8;
+
+// Float4s of a split's partial that one part of the combine loads per other
+// split: the largest divisor of nq with at most `budget` float4s in flight
+// per part across the S - 1 other splits.
+constexpr int split_part_q(int nq, int s, int budget) {
+  int c = budget / (s - 1);
+  if (c < 1) c = 1;
+  while (nq % c != 0) --c;
+  return c;
+}
+
+// The tile's sum over its S split partials, in split order 0 .. S-1,
+// starting from zero, into acc, which holds split `me`'s own partial on
+// entry (so only the other S - 1 partials are read).  Partial float4 q of
+// thread t of split sp sits at float4 (sp * NQ + q) * 256 + t of rp, written
+// with device-coherent stores by the other splits.  The thread's NQ float4s
+// go in parts of QP; each part's loads of every other split are issued
+// unconditionally one part ahead of the additions, so the wait before a
+// part's additions counts exactly the next part's loads.
+template <int S, int FM, int FN, typename Acc>
+__device__ __forceinline__ void sum_splits(Acc (&acc)[FM][FN], __amdgpu_buffer_rsrc_t rp, int me,
+                                           int t) {
+  constexpr int NV = sizeof(Acc) / 16, NQ = FM * FN * NV;
+  // two parts in flight next to the accumulators: 16 float4s per part with
+  // 224 accumulator registers, 8 with 256
+  constexpr int QP = split_part_q(NQ, S, NQ > 56 ? 8 : 16), NP = NQ / QP;
+  f32x4 x[2][S - 1][QP];
+  auto load_part = [&](f32x4(&dst)[S - 1][QP], int p) {
+#pragma unroll
+    for (int o = 0; o < S - 1; ++o) {
+      const int sp = o + (o >= me ? 1 : 0);  // the o-th split other than me
+#pragma unroll
+      for (int u = 0; u < QP; ++u)
+        dst[o][u] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rp, ((sp * NQ + p * QP + u) * 256 + t) * 16, 0, 0x10));
+    }
+  };
+  load_part(x[0], 0);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    if (p + 1 < NP) load_part(x[(p + 1) & 1], p + 1);
+    f32x4 s[QP];
+#pragma unroll
+    for (int u = 0; u < QP; ++u) s[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // splits before me, then mine, then those after me
+#pragma unroll
+    for (int o = 0; o < S - 1; ++o)
+      if (o < me)
+#pragma unroll
+        for (int u = 0; u < QP; ++u) s[u] += x[p & 1][o][u];
+#pragma unroll
+    for (int u = 0; u < QP; ++u) {
+      const int q = p * QP + u, c = q % NV, j = (q / NV) % FN, i = q / (NV * FN);
+      s[u] += f32x4{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
+                    acc[i][j][4 * c + 3]};
+    }
+#pragma unroll
+    for (int o = 0; o < S - 1; ++o)
+      if (o >= me)
+#pragma unroll
+        for (int u = 0; u < QP; ++u) s[u] += x[p & 1][o][u];
+#pragma unroll
+    for (int u = 0; u < QP; ++u) {
+      const int q = p * QP + u, c = q % NV, j = (q / NV) % FN, i = q / (NV * FN);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][4 * c + e] = s[u][e];
+    }
+  }
+}
+
 // One output tile (tile row tm, tile column tn) of C = A * B: the K loop
 // and the epilogue.  BKN = false: B stored N x K (sbk = 1); true: B stored
 // K x N (sbn = 1).
@@ -411,9 +484,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
     // slots, 16-byte runs contiguous across threads -- with device-coherent
     // (sc1) stores; every wave waits for its stores before the barrier that
     // precedes the tile's counter increment, so the split that finishes last
-    // reads every slot whole.  It adds the slots in split order (the result
-    // does not depend on which split finishes last), clears the counter and
-    // goes on to the epilogue with the sums.
+    // reads every slot whole.  It adds the partials in split order (the
+    // result does not depend on which split finishes last), clears the
+    // counter and goes on to the epilogue with the sums.
     constexpr int NV = MMA::NACC / 4, NQ = FM * FN * NV;
     const int t = threadIdx.x;
     const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
@@ -438,24 +511,14 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
     if (t == 0) last = atomicAdd(sk.counters + sk.tile, 1) == sk.splits - 1;
     __syncthreads();
     if (!last) return;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int v = 0; v < MMA::NACC; ++v) acc[i][j][v] = 0.0f;
-      for (int sp = 0; sp < sk.splits; ++sp)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int c = 0; c < NV; ++c) {
-            const int q = (i * FN + j) * NV + c;
-            const f32x4 x = __builtin_bit_cast(
-                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, ((sp * NQ + q) * 256 + t) * 16,
-                                                             0, 0x10));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][4 * c + e] += x[e];
-          }
+    switch (sk.splits) {
+      case 2: sum_splits<2>(acc, rp, sk.split, t); break;
+      case 3: sum_splits<3>(acc, rp, sk.split, t); break;
+      case 4: sum_splits<4>(acc, rp, sk.split, t); break;
+      case 5: sum_splits<5>(acc, rp, sk.split, t); break;
+      case 6: sum_splits<6>(acc, rp, sk.split, t); break;
+      case 7: sum_splits<7>(acc, rp, sk.split, t); break;
+      default: sum_splits<kMaxSplits>(acc, rp, sk.split, t); break;
     }
     if (t == 0) __hip_atomic_store(sk.counters + sk.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

@@ -280,12 +280,17 @@ def test_tile_nt_padded_leading_dims():
 # ---------------------------------------------------- split-K tile kernel
 
 # (M, N, K, expected plan): too few tiles to fill the CUs, so K is split
-# across each tile's workgroups; ragged M, N and K tails.
+# across each tile's workgroups; every split count the kernel takes (2 .. 8,
+# each its own combine), ragged M, N and K tails.
 SPLITK_CASES = [
-    (300, 500, 4096, "tile_nt_256x224_splitk8"),
     (257, 223, 1032, "tile_nt_256x224_splitk2"),
+    (520, 230, 1496, "tile_nt_256x224_splitk3"),
     (65, 100, 2048, "tile_nt_256x224_splitk4"),
-    (1024, 1024, 4104, "tile_nt_256x224_splitk8"),
+    (300, 500, 4096, "tile_nt_256x224_splitk5"),
+    (1024, 1024, 4104, "tile_nt_256x224_splitk5"),
+    (96, 700, 5000, "tile_nt_256x224_splitk6"),
+    (130, 250, 6272, "tile_nt_256x224_splitk7"),
+    (200, 300, 8200, "tile_nt_256x224_splitk8"),
 ]
 
 
