@@ -10,7 +10,9 @@ permutations, rank-1 closed forms, exact-integer brute force and NumPy's fp64
 matmul; the decoders and the rounding are pinned exhaustively against
 torch / numpy dtype conversions (tests/test_codecs.py); the fp8 block
 quantiser against torch's e4m3fn cast, numpy's fp32 division, the block
-invariants of its definition and the input generator's own quantiser.
+invariants of its definition and the input generator's own quantiser; the
+product with fp8 output against an identity product and numpy's integer
+matmul.
 """
 from __future__ import annotations
 
@@ -105,6 +107,19 @@ class Oracle:
             raise ValueError("oracle: bad arguments")
         return Q, S
 
+    def gemm_quant_fp8(self, fmt: str, M: int, N: int, K: int, A: np.ndarray, sam: int,
+                       sak: int, B: np.ndarray, sbk: int, sbn: int, rows=None):
+        """The product with an fp8 output ("TileKernels deep dive" section 7.2:
+        the result quantised to FP8 where it is computed, per row slice of 128,
+        scale = slice maximum over 448): the fp64 product, rounded once to fp32
+        (the accumulator type, with no rounding to 16 bits in between), then
+        quantised with one scale per 1 x 128 row slice.  Returns (codes
+        nrows x N, scales nrows x ceil(N / 128), fp64 C, S = sum |a||b|) for
+        the requested rows (all if None)."""
+        C, S = self.gemm(fmt, M, N, K, A, sam, sak, B, sbk, sbn, rows=rows)
+        Q, SC = self.quant_fp8(C.astype(np.float32), 1)
+        return Q, SC, C, S
+
     def round_to(self, fmt: str, x: np.ndarray) -> np.ndarray:
         """Round fp64 values to fp16 / bf16 codes, nearest-even (overflow -> inf)."""
         x = np.ascontiguousarray(x, dtype=np.float64)
@@ -150,6 +165,10 @@ def gemm(*args, **kw):
 
 def gemm_fp8_blockscaled(*args, **kw):
     return default().gemm_fp8_blockscaled(*args, **kw)
+
+
+def gemm_quant_fp8(*args, **kw):
+    return default().gemm_quant_fp8(*args, **kw)
 
 
 def round_to(fmt, x):

@@ -424,9 +424,56 @@ def pin_quant_matches_generator(orc):
         assert np.array_equal(Q, Qg) and np.array_equal(S, Sg)
 
 
+def pin_gemm_quant_identity(orc):
+    """An identity A selects the rows of B, so C = B exactly: with a 448 in
+    every 128-column slice the scale is 1 and the codes are torch's e4m3fn
+    cast of B's values (a transposed operand, a wrong slice width or a slice
+    taken down a column instead of along a row would all differ)."""
+    rng = np.random.default_rng(21)
+    for fmt in ("bf16", "f16"):
+        M = K = 40
+        N = 300
+        vals = lib_decode(fmt, lib_encode(fmt, rng.uniform(-440, 440, (K, N))))
+        vals[:, ::128] = 448.0 * rng.choice([-1.0, 1.0], (K, (N + 127) // 128))
+        B = lib_encode(fmt, vals)                     # K x N, N-contiguous
+        A = lib_encode(fmt, np.eye(M, K))
+        Q, S, C, _ = orc.gemm_quant_fp8(fmt, M, N, K, A, K, 1, B, N, 1)
+        assert np.array_equal(C, vals)
+        assert np.all(S == 1.0), "slice maximum 448 gives scale 1"
+        want = torch.from_numpy(vals.astype(np.float32)).to(torch.float8_e4m3fn)
+        assert np.array_equal(Q, want.view(torch.uint8).numpy())
+
+
+def pin_gemm_quant_integers(orc):
+    """Small integer operands: the product is numpy's exact int64 matmul; each
+    slice's scale is numpy's fp32 quotient of its maximum by 448 and each code
+    torch's e4m3fn cast of the fp32 quotient C / scale.  Ragged last slice
+    (N = 333), rows of very different size, and a zero row (scale 1, codes 0)."""
+    rng = np.random.default_rng(22)
+    M, N, K = 37, 333, 50
+    Ai = rng.integers(-8, 9, (M, K)) * (2 ** rng.integers(0, 6, (M, 1)))
+    Ai[5] = 0
+    Bi = rng.integers(-8, 9, (K, N))
+    Ci = Ai @ Bi
+    A, B = lib_encode("bf16", Ai), lib_encode("bf16", Bi)
+    Q, S, C, _ = orc.gemm_quant_fp8("bf16", M, N, K, A, K, 1, B, N, 1)
+    assert np.array_equal(C, Ci)
+    for i in range(M):
+        for j in range((N + 127) // 128):
+            blk = Ci[i, j * 128:(j + 1) * 128].astype(np.float32)
+            s = _fp32_div(np.abs(blk).max(), 448.0)
+            if s == 0:
+                assert S[i, j] == 1.0 and not Q[i, j * 128:(j + 1) * 128].any()
+                continue
+            assert S[i, j] == s, (i, j)
+            y = np.clip(blk / s, -448, 448).astype(np.float32)
+            want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(Q[i, j * 128:(j + 1) * 128], want), (i, j)
+
+
 ALL_PINS = [pin_identity, pin_selection, pin_rank1, pin_all_ones, pin_bruteforce_integers,
             pin_bruteforce_rationals, pin_numpy_matmul, pin_layout_invariance, pin_row_subset,
             pin_nonnegative_s_equals_c, pin_fp8_unit_codes, pin_fp8_bruteforce,
             pin_fp8_layout_and_rows, pin_decoders, pin_rounding, pin_quant_codes_match_torch,
             pin_quant_scales_and_bounds, pin_quant_edge_blocks, pin_quant_block_relation,
-            pin_quant_matches_generator]
+            pin_quant_matches_generator, pin_gemm_quant_identity, pin_gemm_quant_integers]
