@@ -20,7 +20,8 @@ OP_F16, OP_BF16, OP_FP8 = 0, 1, 2
 EXPORTS = ("tg_status_string", "tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8_blockscaled",
            "tg_gemm_plan", "tg_quant_fp8_1x128", "tg_quant_fp8_128x128", "tg_gemm_grouped_f16",
            "tg_gemm_grouped_bf16", "tg_gemm_grouped_plan", "tg_gemm_grouped_fp8_blockscaled",
-           "tg_gemm_grouped_fp8_plan")
+           "tg_gemm_grouped_fp8_plan", "tg_gemm_f16_quant_fp8", "tg_gemm_bf16_quant_fp8",
+           "tg_gemm_quant_fp8_plan")
 
 
 class TgError(RuntimeError):
@@ -67,6 +68,12 @@ def load():
     for name in ("tg_quant_fp8_1x128", "tg_quant_fp8_128x128"):
         getattr(lib, name).argtypes = [i64, i64, vp, i64, vp, i64, vp, i64, i64, vp]
         getattr(lib, name).restype = c_int
+    sigq = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, vp, i64, i64]
+    for name in ("tg_gemm_f16_quant_fp8", "tg_gemm_bf16_quant_fp8"):
+        getattr(lib, name).argtypes = sigq + [vp]
+        getattr(lib, name).restype = c_int
+    lib.tg_gemm_quant_fp8_plan.argtypes = [c_int] + sigq
+    lib.tg_gemm_quant_fp8_plan.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -109,6 +116,21 @@ def tg_quant_fp8_1x128(R, K, X, ldx, Q, ldq, S, ssr, ssk, stream=0):
 
 def tg_quant_fp8_128x128(R, K, X, ldx, Q, ldq, S, ssr, ssk, stream=0):
     return _check(load().tg_quant_fp8_128x128(R, K, X, ldx, Q, ldq, S, ssr, ssk, stream))
+
+
+def tg_gemm_f16_quant_fp8(M, N, K, A, sam, sak, B, sbk, sbn, Q, sqm, S, ssm, ssj, stream=0):
+    return _check(load().tg_gemm_f16_quant_fp8(M, N, K, A, sam, sak, B, sbk, sbn, Q, sqm, S, ssm,
+                                               ssj, stream))
+
+
+def tg_gemm_bf16_quant_fp8(M, N, K, A, sam, sak, B, sbk, sbn, Q, sqm, S, ssm, ssj, stream=0):
+    return _check(load().tg_gemm_bf16_quant_fp8(M, N, K, A, sam, sak, B, sbk, sbn, Q, sqm, S, ssm,
+                                                ssj, stream))
+
+
+def tg_gemm_quant_fp8_plan(op, M, N, K, A, sam, sak, B, sbk, sbn, Q, sqm, S, ssm, ssj):
+    r = load().tg_gemm_quant_fp8_plan(op, M, N, K, A, sam, sak, B, sbk, sbn, Q, sqm, S, ssm, ssj)
+    return None if r is None else r.decode()
 
 
 def _offsets(offsets):

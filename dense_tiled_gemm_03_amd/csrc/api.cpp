@@ -18,25 +18,20 @@ bool extent_ok(int64_t n, int64_t stride) {
   return !__builtin_mul_overflow(n - 1, stride, &r);
 }
 
-struct Call {
-  Op op;
-  GemmArgs a;
-  int64_t scn;
-};
+}  // namespace
 
 // Returns TG_SUCCESS when the call is valid (it may still be a no-op).
-tg_status validate(const Call& c) {
-  const GemmArgs& a = c.a;
+tg_status validate_args(Op op, const GemmArgs& a, int64_t scn) {
   if (a.M < 0 || a.N < 0 || a.K < 0) return TG_ERR_INVALID_VALUE;
-  if (a.sam < 0 || a.sak < 0 || a.sbk < 0 || a.sbn < 0 || a.scm < 0 || c.scn < 0)
+  if (a.sam < 0 || a.sak < 0 || a.sbk < 0 || a.sbn < 0 || a.scm < 0 || scn < 0)
     return TG_ERR_INVALID_VALUE;
-  if (c.op == Op::FP8 && (a.ssam < 0 || a.ssak < 0 || a.ssbn < 0 || a.ssbk < 0))
+  if (op == Op::FP8 && (a.ssam < 0 || a.ssak < 0 || a.ssbn < 0 || a.ssbk < 0))
     return TG_ERR_INVALID_VALUE;
   if (a.M == 0 || a.N == 0) return TG_SUCCESS;  // nothing to compute, nothing to check
   if (a.C == nullptr) return TG_ERR_INVALID_VALUE;
   if (a.K > 0) {
     if (a.A == nullptr || a.B == nullptr) return TG_ERR_INVALID_VALUE;
-    if (c.op == Op::FP8 && (a.SA == nullptr || a.SB == nullptr)) return TG_ERR_INVALID_VALUE;
+    if (op == Op::FP8 && (a.SA == nullptr || a.SB == nullptr)) return TG_ERR_INVALID_VALUE;
   }
   if (a.M > 1 && a.scm < a.N) return TG_ERR_INVALID_VALUE;  // rows of C would overlap
   if (!extent_ok(a.M, a.sam) || !extent_ok(a.K, a.sak) || !extent_ok(a.K, a.sbk) ||
@@ -52,16 +47,26 @@ tg_status validate(const Call& c) {
         rc >= lim)
       return TG_ERR_INVALID_VALUE;
   }
-  if (c.op == Op::FP8) {
+  if (op == Op::FP8) {
     const int64_t kb = cdiv(a.K, 128), nb = cdiv(a.N, 128);
     if (!extent_ok(a.M, a.ssam) || !extent_ok(kb, a.ssak) || !extent_ok(nb, a.ssbn) ||
         !extent_ok(kb, a.ssbk))
       return TG_ERR_INVALID_VALUE;
   }
-  if (c.scn != 1) return TG_ERR_UNSUPPORTED;
+  if (scn != 1) return TG_ERR_UNSUPPORTED;
   if (a.M > kMaxDim || a.N > kMaxDim || a.K > kMaxDim) return TG_ERR_UNSUPPORTED;
   return TG_SUCCESS;
 }
+
+namespace {
+
+struct Call {
+  Op op;
+  GemmArgs a;
+  int64_t scn;
+};
+
+tg_status validate(const Call& c) { return validate_args(c.op, c.a, c.scn); }
 
 // Kernel tables, most specialised first; the last entry takes every call.
 const Variant* (*const kTable16[])() = {variant_skinny16, variant_tile_nt16, variant_tile_nn16,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/tg_gemm.h"
+
 namespace tg {
 
 enum class Op : int { F16 = 0, BF16 = 1, FP8 = 2 };
@@ -58,6 +60,10 @@ struct GroupTable {
 // leading completion counters are zero between kernels.  NULL when it cannot
 // be had (allocation failure, or the stream is being captured).
 void* stream_workspace(hipStream_t stream, size_t bytes);
+
+// Host-side checks of a product's sizes, strides and pointers (C with row
+// stride scm and column stride scn); TG_SUCCESS when the call is valid.
+tg_status validate_args(Op op, const GemmArgs& a, int64_t scn);
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));

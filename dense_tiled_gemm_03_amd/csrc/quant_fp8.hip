@@ -10,46 +10,19 @@
 //          x / s is the correctly rounded fp32 quotient; the sign is kept.
 // Both kernels are bound by HBM (4 bytes read and 1 written per element):
 // every element is loaded once into registers, reduced for the block's
-// maximum and converted from there.
+// maximum and converted from there.  The quotient x / s comes from the
+// block's reciprocal with one FMA correction (quotient_by, fp8_codec.hpp),
+// exact for the scales nearly every block has; blocks with extreme scales
+// divide.
 #include "../../include/tg_gemm.h"
 
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
+#include "fp8_codec.hpp"
 
 namespace tg {
 namespace {
-
-// e4m3fn code of y for |y| <= 448, round to nearest even, sign kept.  Below
-// 2^-6 the grid is the multiples of 2^-9 (subnormals, and 2^-6 itself as 8 =
-// exponent 1, fraction 0); above, the fp32 fraction is rounded to 3 bits at
-// bit 20 (a carry moves into the exponent) and the exponent rebiased from
-// 127 to 7.
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  uint32_t code;
-  if (a < 0.015625f) {
-    code = (uint32_t)rintf(a * 512.0f);
-  } else {
-    uint32_t ua = __float_as_uint(a);
-    ua += 0x7FFFFu + ((ua >> 20) & 1u);
-    code = (((ua >> 23) - 120u) << 3) | ((ua >> 20) & 7u);
-  }
-  return code | sign;
-}
-
-// The block's scale, and whether it is an all-zero block.
-__device__ __forceinline__ float block_scale(float amax, bool& zero) {
-  const float s = amax / 448.0f;
-  zero = s == 0.0f;
-  return zero ? 1.0f : s;
-}
-
-__device__ __forceinline__ uint32_t code_of(float x, float s, bool zero) {
-  if (zero) return 0u;
-  return e4m3_rne(fminf(fmaxf(x / s, -448.0f), 448.0f));
-}
 
 // Element mapping inside a 128-wide row segment: lane t (of 16) holds
 // columns 4t .. 4t+3 and 64 + 4t .. 64 + 4t + 3, so each 16-byte load (and
@@ -74,17 +47,28 @@ __device__ __forceinline__ void load_seg(const float* x, int t, int64_t k0, int6
 }
 
 __device__ __forceinline__ void store_seg(uint8_t* q, int t, int64_t k0, int64_t K, bool full,
-                                          bool vec, const uint32_t* c) {
+                                          bool vec, const uint32_t* w) {
   if (full && vec) {
-    *reinterpret_cast<uint32_t*>(q + 4 * t) = c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24;
-    *reinterpret_cast<uint32_t*>(q + 64 + 4 * t) = c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24;
+    *reinterpret_cast<uint32_t*>(q + 4 * t) = w[0];
+    *reinterpret_cast<uint32_t*>(q + 64 + 4 * t) = w[1];
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (k0 + 4 * t + e < K) q[4 * t + e] = (uint8_t)c[e];
-      if (k0 + 64 + 4 * t + e < K) q[64 + 4 * t + e] = (uint8_t)c[4 + e];
+      if (k0 + 4 * t + e < K) q[4 * t + e] = (uint8_t)(w[0] >> (8 * e));
+      if (k0 + 64 + 4 * t + e < K) q[64 + 4 * t + e] = (uint8_t)(w[1] >> (8 * e));
     }
   }
+}
+
+// The eight codes of a lane's segment, packed as store_seg() writes them.
+template <bool FAST>
+__device__ __forceinline__ void codes_of(const float* v, float s, float r, bool zero,
+                                         uint32_t* w) {
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = FAST ? scaled_fast(v[e], s, r) : scaled(v[e], s);
+  w[0] = zero ? 0u : e4m3x4(y[0], y[1], y[2], y[3]);
+  w[1] = zero ? 0u : e4m3x4(y[4], y[5], y[6], y[7]);
 }
 
 // 1 x 128 blocks, numbered row-major (consecutive blocks of a row are
@@ -129,11 +113,14 @@ __global__ __launch_bounds__(256) void quant_1x128(int64_t R, int64_t K, const f
     if (first + b >= nblk) continue;
     bool zero;
     const float s = block_scale(amax, zero);
-    uint32_t c[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = code_of(v[b][e], s, zero);
+    const float rs = 1.0f / s;
+    uint32_t w[2];
+    if (__all(scale_in_fast_range(s)))
+      codes_of<true>(v[b], s, rs, zero, w);
+    else
+      codes_of<false>(v[b], s, rs, zero, w);
     const bool full = col[b] + 128 <= K;
-    store_seg(Q + row[b] * ldq + col[b], t16, col[b], K, full, vec, c);
+    store_seg(Q + row[b] * ldq + col[b], t16, col[b], K, full, vec, w);
     if (t16 == 0) S[row[b] * ssr + (col[b] / 128) * ssk] = s;
   }
 }
@@ -170,14 +157,18 @@ __global__ __launch_bounds__(256) void quant_128x128(int64_t R, int64_t K, const
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   bool zero;
   const float s = block_scale(amax, zero);
+  const float rs = 1.0f / s;
+  const bool fast = scale_in_fast_range(s);  // uniform over the workgroup
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t r = ib * 128 + rg + 16 * j;
     if (r >= R) continue;
-    uint32_t c[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = code_of(v[j][e], s, zero);
-    store_seg(Q + r * ldq + k0, t16, k0, K, kfull, vec, c);
+    uint32_t w[2];
+    if (fast)
+      codes_of<true>(v[j], s, rs, zero, w);
+    else
+      codes_of<false>(v[j], s, rs, zero, w);
+    store_seg(Q + r * ldq + k0, t16, k0, K, kfull, vec, w);
   }
   if (t == 0) S[ib * ssr + kb * ssk] = s;
 }

@@ -36,8 +36,10 @@
 //    get consecutive tile ids, walked in groups of GM M-tiles so concurrent
 //    tiles on one XCD share A rows and B columns in that XCD's L2.
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
+#include "fp8_codec.hpp"
 
 namespace tg {
 namespace tile {
@@ -157,6 +159,99 @@ struct SplitK {
   int* counters;
 };
 
+// fp8 output in place of C: e4m3fn codes Q (M x N bytes, row stride sqm) and
+// one fp32 scale per 1 x 128 row slice, S[m * ssm + j * ssj] for slice j.
+struct QuantOut {
+  uint8_t* Q;
+  int64_t sqm;
+  float* S;
+  int64_t ssm, ssj;
+};
+
+// Codes and scales of one accumulator block row (DIM rows x the wave's 128
+// columns) of the quantising epilogue below.
+template <bool FAST, bool FULL, typename MMA, int FN, typename Acc>
+__device__ __forceinline__ void quant_store(const Acc (&acc)[FN], const float* sc, const float* rc,
+                                            const bool* zero, const QuantOut& qo, int64_t M,
+                                            int64_t N, int64_t row0, int64_t c, int64_t slice,
+                                            int lane) {
+#pragma unroll
+  for (int v = 0; v < MMA::NACC; ++v) {
+    const int64_t r = row0 + MMA::out_row(lane, v);
+    if (FULL || r < M) {
+      uint8_t* q = qo.Q + r * qo.sqm + c;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        if (FULL || c + j * MMA::DIM < N)
+          q[j * MMA::DIM] = (uint8_t)(FAST ? code_of_fast(acc[j][v], sc[v], rc[v], zero[v])
+                                           : code_of(acc[j][v], sc[v], zero[v]));
+      if ((lane & 31) == 0) qo.S[r * qo.ssm + slice * qo.ssj] = sc[v];
+    }
+  }
+}
+
+// One accumulator block row of the quantising epilogue: the row maxima over
+// the wave's columns inside N -- four accumulator blocks in the lane, then
+// the 32 lanes that hold the row's other columns -- the scales, then the
+// codes.  FULL: the wave's whole tile lies inside M x N.
+template <bool FULL, typename MMA, int FN, typename Acc>
+__device__ __forceinline__ void quant_block_row(const Acc (&acc)[FN], const QuantOut& qo, int64_t M,
+                                                int64_t N, int64_t row0, int64_t c, int64_t slice,
+                                                int lane) {
+  float sc[MMA::NACC], rc[MMA::NACC];
+  bool zero[MMA::NACC];
+  bool fast = true;
+#pragma unroll
+  for (int v = 0; v < MMA::NACC; ++v) {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      if (FULL || c + j * MMA::DIM < N) m = fmaxf(m, fabsf(acc[j][v]));
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    sc[v] = block_scale(m, zero[v]);
+    rc[v] = 1.0f / sc[v];
+    fast = fast && scale_in_fast_range(sc[v]);
+  }
+  // codes from x * (1 / s) with one correction when every scale of the
+  // wave's rows allows it (wave-uniform), else by division
+  if (__all(fast))
+    quant_store<true, FULL, MMA>(acc, sc, rc, zero, qo, M, N, row0, c, slice, lane);
+  else
+    quant_store<false, FULL, MMA>(acc, sc, rc, zero, qo, M, N, row0, c, slice, lane);
+}
+
+template <bool FULL, typename MMA, int FM, int FN, typename Acc, int... Is>
+__device__ __forceinline__ void quant_block_rows(Acc (&acc)[FM][FN], const QuantOut& qo, int64_t M,
+                                                 int64_t N, int64_t row0, int64_t c, int64_t slice,
+                                                 int lane, std::integer_sequence<int, Is...>) {
+  // one call per block row, expanded at compile time: the accumulators are
+  // only ever indexed by constants, so they stay in registers
+  (quant_block_row<FULL, MMA>(acc[Is], qo, M, N, row0 + Is * MMA::DIM, c, slice, lane), ...);
+}
+
+// Quantising epilogue, for a wave tile 128 columns wide starting at a
+// multiple of 128 (col0), so that each of its rows is one 1 x 128 slice: the
+// fp32 accumulators go straight to codes, with no rounding to 16 bits first
+// ("TileKernels deep dive" section 7.2: the fused kernel's result is
+// quantised without being written back in a wider type).  Columns past N are
+// left out of the row maxima explicitly: with B stored K x N their
+// accumulators hold products with the next K row's first elements, not
+// zeros.
+template <typename MMA, int FM, int FN, typename Acc>
+__device__ __forceinline__ void quant_epilogue(Acc (&acc)[FM][FN], const QuantOut& qo, int64_t M,
+                                               int64_t N, int64_t row0, int64_t col0, int lane) {
+  static_assert(MMA::DIM == 32 && FN * MMA::DIM == 128, "a wave row is one 1 x 128 slice");
+  if (col0 >= N) return;  // the wave's slice lies past N (wave-uniform)
+  const int64_t c = col0 + (lane & 31), slice = col0 / 128;
+  if (row0 + FM * MMA::DIM <= M && col0 + 128 <= N)
+    quant_block_rows<true, MMA>(acc, qo, M, N, row0, c, slice, lane,
+                                std::make_integer_sequence<int, FM>());
+  else
+    quant_block_rows<false, MMA>(acc, qo, M, N, row0, c, slice, lane,
+                                 std::make_integer_sequence<int, FM>());
+}
+
 // Grouped products: the group of this workgroup's (XCD-contiguous) tile id
 // -- the last group whose first tile id is not above it; groups with no rows
 // hold no tiles -- and the tile's row and column inside the group, in
@@ -255,9 +350,10 @@ __device__ __forceinline__ void sum_splits(Acc (&acc)[FM][FN], __amdgpu_buffer_r
 // One output tile (tile row tm, tile column tn) of C = A * B: the K loop
 // and the epilogue.  BKN = false: B stored N x K (sbk = 1); true: B stored
 // K x N (sbn = 1).
-template <typename T, typename Cfg, bool BKN, bool SPLIT = false>
+template <typename T, typename Cfg, bool BKN, bool SPLIT = false, bool QUANT = false>
 __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
-                                          const SplitK& sk = SplitK{1, 0, 0, nullptr, nullptr}) {
+                                          const SplitK& sk = SplitK{1, 0, 0, nullptr, nullptr},
+                                          const QuantOut& qo = QuantOut{}) {
   typedef typename Elem<T>::x8 T8;
   typedef typename Cfg::MMA MMA;
   typedef typename MMA::Acc Acc;
@@ -523,6 +619,12 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
     if (t == 0) __hip_atomic_store(sk.counters + sk.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
+  static_assert(!(SPLIT && QUANT), "the quantising epilogue takes whole-K tiles");
+  if constexpr (QUANT) {
+    quant_epilogue<MMA>(acc, qo, a.M, a.N, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, lane);
+    return;
+  }
+
   // Epilogue: round each accumulator to the output type and store it inside
   // M x N.
   T* C = static_cast<T*>(a.C);
@@ -554,6 +656,16 @@ __global__ __launch_bounds__(256) void gemm16_tile(GemmArgs a, int tiles_m, int 
   int tm, tn;
   tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
   tile_body<T, Cfg, BKN>(a, tm, tn);
+}
+
+// fp8 output: the product quantised per 1 x 128 row slice in the epilogue
+// (a 256 x 256 tile: each wave's 128 columns are one slice).
+template <typename T, typename Cfg, bool BKN>
+__global__ __launch_bounds__(256) void gemm16_tile_q8(GemmArgs a, int tiles_m, int tiles_n,
+                                                      QuantOut qo) {
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
+  tile_body<T, Cfg, BKN, false, true>(a, tm, tn, SplitK{1, 0, 0, nullptr, nullptr}, qo);
 }
 
 // Split K: `splits` consecutive workgroups per tile, each over its share of

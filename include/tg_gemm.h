@@ -201,6 +201,48 @@ tg_status tg_quant_fp8_128x128(int64_t R, int64_t K, const float* X, int64_t ldx
                                void* Q, int64_t ldq, float* S, int64_t ssr, int64_t ssk,
                                tg_stream_t stream);
 
+/* Product with an fp8 output: C = A * B as tg_gemm_f16 / tg_gemm_bf16
+ * compute it (fp32 accumulation), then each 1 x 128 row slice of the fp32
+ * result quantised as tg_quant_fp8_1x128 quantises fp32 input, in the
+ * product's own epilogue -- the fp32 values are not rounded to 16 bits first
+ * and never reach memory.  Q and S are laid out as tg_gemm_fp8_blockscaled
+ * takes its A operand and SA, so the output feeds the next block-scaled
+ * product directly ("TileKernels deep dive", section 7.2: the fused kernel
+ * that quantises its result to FP8, scale = row maximum over 448; and the
+ * fused SwiGLU + FP8 example, which saves the wide result's write and read).
+ * A, B: as for tg_gemm_f16 (device, element strides).  Q (device, bytes):
+ * code of C[m,n] at Q + m*sqm + n.  S (device, fp32): scale of the slice of
+ * columns 128j .. 128j+127 of row m at S + m*ssm + j*ssj, j < ceil(N / 128);
+ * the last slice of a row covers the columns that are left.  Per slice:
+ *   amax = max |C| over the slice;  s = amax / 448 rounded to fp32;
+ *   s == 0: s = 1 and every code 0;  otherwise code = e4m3fn RNE of
+ *   clamp(C / s, -448, 448) (the rounded fp32 quotient), sign kept.
+ * Errors: those of tg_gemm_f16 with Q for C (sqm for scm, and sqm >= N when
+ * M > 1); TG_ERR_INVALID_VALUE also for a negative scale stride, S == NULL
+ * when M, N > 0, a zero scale stride along a dimension of more than one
+ * slice, or a scale address range that overflows.  K == 0 gives zero codes
+ * and scales of 1.  Q and S must not overlap A, B or each other.
+ * Asynchronous on `stream`; nothing is allocated. */
+tg_status tg_gemm_f16_quant_fp8(int64_t M, int64_t N, int64_t K,
+                                const void* A, int64_t sam, int64_t sak,
+                                const void* B, int64_t sbk, int64_t sbn,
+                                void* Q, int64_t sqm, float* S, int64_t ssm, int64_t ssj,
+                                tg_stream_t stream);
+tg_status tg_gemm_bf16_quant_fp8(int64_t M, int64_t N, int64_t K,
+                                 const void* A, int64_t sam, int64_t sak,
+                                 const void* B, int64_t sbk, int64_t sbn,
+                                 void* Q, int64_t sqm, float* S, int64_t ssm, int64_t ssj,
+                                 tg_stream_t stream);
+
+/* How a product with fp8 output would run: "tile_nt_256x256_q8" (B stored
+ * N x K), "tile_nn_256x256_q8" (B stored K x N), "generic16_32x128_q8" (any
+ * other call), "none" (no-op) or NULL (invalid arguments).  op: 0 = f16,
+ * 1 = bf16. */
+const char* tg_gemm_quant_fp8_plan(int op, int64_t M, int64_t N, int64_t K,
+                                   const void* A, int64_t sam, int64_t sak,
+                                   const void* B, int64_t sbk, int64_t sbn,
+                                   void* Q, int64_t sqm, float* S, int64_t ssm, int64_t ssj);
+
 /* Name of the kernel a call with these arguments would launch ("none" for a
  * no-op, NULL if the arguments are invalid); nothing is launched.  op: 0 =
  * tg_gemm_f16, 1 = tg_gemm_bf16, 2 = tg_gemm_fp8_blockscaled (the scale

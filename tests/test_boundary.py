@@ -127,6 +127,53 @@ def test_quant_noop(lib, name):
     assert _callq(lib, name, K=0, X=0, Q=0, S=0) == tg.TG_SUCCESS
 
 
+def _callqo(lib, name, **kw):
+    a = dict(M=8, N=300, K=64, A=PA, sam=64, sak=1, B=PB, sbk=1, sbn=64, Q=PC, sqm=300, S=PS,
+             ssm=3, ssj=1)
+    a.update(kw)
+    args = [a[k] for k in ("M", "N", "K", "A", "sam", "sak", "B", "sbk", "sbn", "Q", "sqm", "S",
+                           "ssm", "ssj")]
+    if name == "plan":
+        return lib.tg_gemm_quant_fp8_plan(a.get("op", 1), *args)
+    return getattr(lib, name)(*args, None)
+
+
+INVALIDQO = [dict(M=-1), dict(N=-1), dict(K=-1), dict(sam=-1), dict(sbn=-1), dict(sqm=-1),
+             dict(ssm=-1), dict(ssj=-1), dict(A=0), dict(B=0), dict(Q=0), dict(S=0),
+             dict(sqm=299),                        # rows of the codes overlap
+             dict(ssj=0),                          # three slices in one place
+             dict(ssm=0),                          # eight rows' scales in one place
+             dict(M=2, ssm=1 << 62),               # scale range overflows
+             dict(M=1 << 40, sqm=1 << 40)]         # code range overflows
+
+
+@pytest.mark.parametrize("kw", INVALIDQO, ids=[str(k) for k in INVALIDQO])
+@pytest.mark.parametrize("name", ["tg_gemm_f16_quant_fp8", "tg_gemm_bf16_quant_fp8", "plan"])
+def test_quant_out_invalid(lib, name, kw):
+    r = _callqo(lib, name, **kw)
+    assert (r is None) if name == "plan" else (r == tg.TG_ERR_INVALID_VALUE)
+
+
+def test_quant_out_noop_and_plans(lib):
+    assert _callqo(lib, "tg_gemm_bf16_quant_fp8", M=0, A=0, B=0, Q=0, S=0) == tg.TG_SUCCESS
+    assert _callqo(lib, "tg_gemm_bf16_quant_fp8", N=0, A=0, B=0, Q=0, S=0) == tg.TG_SUCCESS
+    base = dict(op=1, M=8, N=300, K=64, A=PA, sam=64, sak=1, B=PB, sbk=1, sbn=64, Q=PC, sqm=300,
+                S=PS, ssm=3, ssj=1)
+    order = ("op", "M", "N", "K", "A", "sam", "sak", "B", "sbk", "sbn", "Q", "sqm", "S", "ssm",
+             "ssj")
+    plan = lambda **kw: tg.tg_gemm_quant_fp8_plan(*[{**base, **kw}[k] for k in order])  # noqa
+    assert plan() == "tile_nt_256x256_q8"
+    assert plan(op=0) == "tile_nt_256x256_q8"
+    assert plan(op=2) is None                                  # fp8 inputs: not this entry
+    assert plan(sbk=304, sbn=1, N=304, sqm=304) == "tile_nn_256x256_q8"
+    assert plan(A=PA + 2) == "generic16_32x128_q8"             # misaligned A
+    assert plan(K=0, A=0, B=0) == "generic16_32x128_q8"        # zero codes, unit scales
+    assert plan(M=0) == "none"
+    # the fused path of the 4096 x 7168 x 16384 product
+    assert plan(M=4096, N=7168, K=16384, sam=16384, sbn=16384, sqm=7168, ssm=56) \
+        == "tile_nt_256x256_q8"
+
+
 def _grouped(lib, fn, **kw):
     import numpy as np
     a = dict(G=2, off=[0, 100, 300], N=64, K=128, A=PA, lda=128, B=PB, ldb=128, sbg=64 * 128,

@@ -5,8 +5,10 @@ Inputs: seeded N(0, 1) fp32 with rows of varied magnitude, the fp8
 workload's own operands at full size (A 4096 x 16384 with 1 x 128 scales, B
 7168 x 16384 with 128 x 128 scales), ragged and padded shapes, and
 constructed blocks (zeros, a maximum whose scale underflows, a coarse
-subnormal scale, e4m3fn ties, signed zeros).  The quantised operands then go
-through the block-scaled product and are checked against the oracle.
+subnormal scale, e4m3fn ties, signed zeros), rows of extreme scale, and a
+strided sweep of every fp32 value up to 448 with scale 1.  The quantised
+operands then go through the block-scaled product and are checked against
+the oracle.
 """
 from __future__ import annotations
 
@@ -107,6 +109,40 @@ def test_quant_edge_blocks(br):
         X[r, 128] = 448.0
         X[r, 129:256] = ties[(r - 3) * 127:(r - 2) * 127]
     X[6, 256:] = -0.0
+    _check(X, br)
+
+
+def test_quant_e4m3_grid():
+    """Blocks whose maximum is 448 have scale 1, so their codes are the
+    e4m3fn rounding of the inputs themselves: every 61st fp32 bit pattern of
+    magnitude up to 448 in both signs, and every e4m3fn midpoint with its
+    four neighbours on each side, against the oracle bit for bit."""
+    lim = 0x43E00000                                   # 448.0
+    mags = np.arange(0, lim + 1, 61, dtype=np.uint32)
+    pos = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    mids = ((pos[:-1].astype(np.float64) + pos[1:]) / 2).astype(np.float32).view(np.uint32)
+    near = (mids[:, None].astype(np.int64) + np.arange(-4, 5)[None, :]).ravel()
+    mags = np.concatenate([mags, near[(near >= 0) & (near <= lim)].astype(np.uint32)])
+    vals = np.concatenate([mags, mags | np.uint32(0x80000000)]).view(np.float32)
+    rows = -(-vals.size // 127)
+    X = np.zeros((rows, 128), np.float32)
+    X[:, 0] = 448.0
+    flat = np.zeros(rows * 127, np.float32)
+    flat[:vals.size] = vals
+    X[:, 1:] = flat.reshape(rows, 127)
+    _check(X, 1)
+
+
+@pytest.mark.parametrize("br", [1, 128])
+def test_quant_extreme_scales(br):
+    """Rows whose scales lie far outside 2^-60 .. 2^60 (divided exactly)
+    next to ordinary rows (reciprocal and one correction), so waves and
+    workgroups mix both ways of forming x / s."""
+    rng = np.random.default_rng(77)
+    R, K = 384, 512
+    X = rng.standard_normal((R, K)).astype(np.float32)
+    exps = rng.choice([-100, -75, -62, -58, 0, 20, 58, 62, 75, 100], R)
+    X *= np.exp2(exps.astype(np.float64))[:, None].astype(np.float32)
     _check(X, br)
 
 
