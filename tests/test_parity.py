@@ -422,6 +422,42 @@ def test_skinny_graph_capture():
         assert np.array_equal(c1, c_eager) and np.array_equal(c2, c_eager)
 
 
+def test_split_k_graph_capture():
+    """The split-K tile kernel under stream capture: on a stream without
+    scratch it runs unsplit, on one whose scratch is already large enough it
+    splits.  Replayed several times with eager work in between, both graphs
+    give the eager result bit for bit (integer inputs)."""
+    M, N, K = 1024, 1024, 4096
+    w = configs.Workload("t", "bf16", M, N, K, "nk", "normal", 78, 0)
+    d = configs.make_inputs(w, int_r=32)
+    A, B = H.dev(d["A"]), H.dev(d["B"])
+    H.log("split-K graph capture")
+    c_eager, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+    assert plan.startswith("tile_nt_256x224_splitk"), plan
+    C_ref, _ = oracle.gemm("bf16", M, N, K, d["A"], K, 1, d["B"], 1, K)
+    H.assert_bit_exact("bf16", c_eager, C_ref, "split-K eager")
+    fresh, warm = torch.cuda.Stream(), torch.cuda.Stream()
+    C1 = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    C2 = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    with torch.cuda.stream(warm):
+        H.tg.tg_gemm_bf16(M, N, K, A.data_ptr(), K, 1, B.data_ptr(), 1, K, C2.data_ptr(), N, 1,
+                          warm.cuda_stream)
+    torch.cuda.synchronize()
+    g1 = _capture_skinny(fresh, M, N, K, A, B, C1)
+    g2 = _capture_skinny(warm, M, N, K, A, B, C2)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        C1.zero_()
+        C2.zero_()
+        H.run16("bf16", 300, 500, 4096, A, K, 1, B, 1, K)   # eager split-K work in between
+        torch.cuda.synchronize()
+        g1.replay()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(C1.cpu().numpy().view(np.uint16), c_eager)
+        assert np.array_equal(C2.cpu().numpy().view(np.uint16), c_eager)
+
+
 # ------------------------------------------------------ K x N tile kernel
 
 NN_CASES = [(300, 512, 136), (513, 264, 72), (4000, 4000, 136), (256, 256, 64), (65, 8, 8),

@@ -245,3 +245,44 @@ def test_quant_out_feeds_fp8_product():
                          H.dev(S2), nkb, 1)
     C_ref, Sb = oracle.gemm_fp8_blockscaled(M, N2, K2, Qo, K2, 1, So, nkb, 1, Q2, 1, K2, S2, nkb, 1)
     H.assert_within_bound("bf16", c, C_ref, Sb, f"chained product [{plan} -> {plan2}]")
+
+
+def test_quant_out_and_quantiser_graph_capture():
+    """Neither the fp8-output product nor the quantiser allocates, so both
+    can be captured: one graph holding both, replayed several times with
+    eager work in between, gives the eager codes and scales bit for bit."""
+    M, N, K = 300, 512, 256
+    A, sam, sak, B, sbk, sbn = _layout_args("bf16", M, N, K, "nk", 2600, _int_r("bf16", K))
+    Ad, Bd = H.dev(A), H.dev(B)
+    X = torch.from_numpy(gen.normal((M, K), 2601, 0, "f32")).cuda()
+    nb, nkb = -(-N // 128), -(-K // 128)
+    Q = torch.zeros((M, N), dtype=torch.uint8, device="cuda")
+    S = torch.zeros((M, nb), dtype=torch.float32, device="cuda")
+    Q2 = torch.zeros((M, K), dtype=torch.uint8, device="cuda")
+    S2 = torch.zeros((M, nkb), dtype=torch.float32, device="cuda")
+
+    def work(st):
+        tg.tg_gemm_bf16_quant_fp8(M, N, K, Ad.data_ptr(), sam, sak, Bd.data_ptr(), sbk, sbn,
+                                  Q.data_ptr(), N, S.data_ptr(), nb, 1, st)
+        tg.tg_quant_fp8_1x128(M, K, X.data_ptr(), K, Q2.data_ptr(), K, S2.data_ptr(), nkb, 1, st)
+
+    H.log("fp8-output product + quantiser graph capture")
+    work(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    want = [t.cpu().numpy().copy() for t in (Q, S, Q2, S2)]
+    Qo, So, _, _ = oracle.gemm_quant_fp8("bf16", M, N, K, A, sam, sak, B, sbk, sbn)
+    assert_exact(want[0], want[1], Qo, So, "eager fp8-output product")
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        work(stream.cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in (Q, S, Q2, S2):
+            t.zero_()
+        _run("bf16", 70, 200, 96, Ad, K, 1, Bd, 1, K)        # eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, w_ in zip((Q, S, Q2, S2), want):
+            assert np.array_equal(t.cpu().numpy().view(np.uint8), w_.view(np.uint8))
