@@ -12,10 +12,11 @@
 //    are about as many workgroups as CUs); its 4 waves each own 32 columns
 //    and share the A slice;
 //  - 64-wide K slices go HBM -> LDS with buffer_load_dwordx4 ... lds (whole
-//    128-byte lines) into a 6-stage ring shared by the 4 waves: five slices
-//    (80 KiB of B) in flight per workgroup; one barrier per slice; each
-//    slice's fragments are read from LDS while the previous slice's MFMAs
-//    run; nothing is loaded past the workgroup's K range;
+//    128-byte lines; B with the non-temporal policy, since it is read once
+//    while A is read by every strip) into a 6-stage ring shared by the 4
+//    waves: five slices (80 KiB of B) in flight per workgroup; one barrier
+//    per slice; each slice's fragments are read from LDS while the previous
+//    slice's MFMAs run; nothing is loaded past the workgroup's K range;
 //  - 32x32x16 MFMAs: per slice, 2 x 1 blocks x 4 k-steps per wave;
 //  - each workgroup writes its fp32 64 x 128 partial tile to scratch; the
 //    last of a column strip's workgroups to finish (a device-scope counter)
@@ -33,6 +34,7 @@ namespace {
 
 using tile::kOutOfRange;
 using tile::load_lds16;
+using tile::load_lds16_nt;
 using tile::make_desc;
 
 constexpr int SM = 64;                     // rows of C per workgroup (all of M)
@@ -99,7 +101,11 @@ __global__ __launch_bounds__(256) void gemm16_skinny(GemmArgs a, int splits, flo
       const uint32_t group = is_a ? 2 * w + jj : 8 + 4 * w + jj;     // 8-row group in the stage
       const bool kin = k0 + 8 * (int)c < k_end;
       const uint32_t off = row * (is_a ? lda : ldb) * 2 + 2 * k0 + 16 * c;
-      load_lds16(is_a ? ra : rb, stage + group * 1024, kin ? off : kOutOfRange);
+      // B is read once (non-temporal); A is shared by every strip
+      if (is_a)
+        load_lds16(ra, stage + group * 1024, kin ? off : kOutOfRange);
+      else
+        load_lds16_nt(rb, stage + group * 1024, kin ? off : kOutOfRange);
     }
   };
 

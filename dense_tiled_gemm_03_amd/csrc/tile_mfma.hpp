@@ -124,6 +124,15 @@ __device__ __forceinline__ void load_lds16(const i32x4& desc, uint32_t lds, uint
                :: "s"(lds), "v"(voff), "s"(desc) : "memory");
 }
 
+// The same load with the non-temporal cache policy (nt): for an operand that
+// is read exactly once, so that streaming it through the XCD's L2 does not
+// push out lines that other workgroups read again (the skinny kernel's B
+// against its shared A).
+__device__ __forceinline__ void load_lds16_nt(const i32x4& desc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :: "s"(lds), "v"(voff), "s"(desc) : "memory");
+}
+
 // This workgroup's id with the ids of each XCD (the hardware places
 // workgroup b on XCD b % 8) made contiguous.
 __device__ __forceinline__ int xcd_id() {
