@@ -56,9 +56,16 @@ struct GroupTable {
   int tile0[kMaxGroups + 1];
 };
 
-// Scratch of at least `bytes` for kernels on `stream` (current device); its
-// leading completion counters are zero between kernels.  NULL when it cannot
-// be had (allocation failure, or the stream is being captured).
+// Scratch of at least `bytes` for kernels on `stream` (current device).  NULL
+// when it cannot be had (allocation failure, or the stream is being captured).
+// Every kernel that uses it lays it out the same way, whatever the sizes of
+// earlier calls on the stream: the first kWorkspaceCounterBytes hold up to
+// kWorkspaceCounters completion counters (ints), zero whenever a kernel starts
+// and left zero by every kernel; partial results start at
+// kWorkspaceCounterBytes, so no call's partials can land on a later call's
+// counters.
+constexpr int kWorkspaceCounters = 4096;
+constexpr size_t kWorkspaceCounterBytes = kWorkspaceCounters * sizeof(int);
 void* stream_workspace(hipStream_t stream, size_t bytes);
 
 // Host-side checks of a product's sizes, strides and pointers (C with row

@@ -294,14 +294,17 @@ hipError_t launch(Op op, const GemmArgs& a, hipStream_t stream) {
   float* part = nullptr;
   int* counters = nullptr;
   if (splits > 1) {
-    const size_t cnt_bytes = ((size_t)strips * 4 + 255) & ~size_t(255);
-    const size_t bytes = cnt_bytes + (size_t)strips * splits * SM * SN * 4;
-    char* ws = static_cast<char*>(stream_workspace(stream, bytes));
+    // one counter per strip at the start of the scratch, partial tiles after
+    // the fixed counter area
+    const size_t bytes = kWorkspaceCounterBytes + (size_t)strips * splits * SM * SN * 4;
+    char* ws = strips <= kWorkspaceCounters
+                   ? static_cast<char*>(stream_workspace(stream, bytes))
+                   : nullptr;
     if (ws == nullptr) {
       splits = 1;  // no scratch to be had: one workgroup per strip, no combining
     } else {
       counters = reinterpret_cast<int*>(ws);
-      part = reinterpret_cast<float*>(ws + cnt_bytes);
+      part = reinterpret_cast<float*>(ws + kWorkspaceCounterBytes);
     }
   }
   const dim3 grid((unsigned)(strips * splits)), block(256);

@@ -63,14 +63,16 @@ hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
   const int splits = splits_for<Cfg>(a);
   if constexpr (kSplitsK<Cfg>) {
    if (splits > 1) {
-    // scratch: per-tile counters, then each split's fp32 partial tile
+    // scratch: one counter per tile in the fixed counter area, then each
+    // split's fp32 partial tile
     const size_t tiles = (size_t)tm * tn;
-    const size_t cnt_bytes = (tiles * 4 + 255) & ~size_t(255);
     const size_t part_bytes = (size_t)Cfg::BM * Cfg::BN * 4 * splits * tiles;
-    char* ws = static_cast<char*>(stream_workspace(s, cnt_bytes + part_bytes));
+    char* ws = tiles <= (size_t)kWorkspaceCounters
+                   ? static_cast<char*>(stream_workspace(s, kWorkspaceCounterBytes + part_bytes))
+                   : nullptr;
     if (ws != nullptr) {
       int* counters = reinterpret_cast<int*>(ws);
-      float* part = reinterpret_cast<float*>(ws + cnt_bytes);
+      float* part = reinterpret_cast<float*>(ws + kWorkspaceCounterBytes);
       const dim3 grid((unsigned)(tiles * splits)), block(256);
       if (op == Op::BF16)
         hipLaunchKernelGGL((tile::gemm16_tile_splitk<__bf16, Cfg>), grid, block, 0, s, a, tm, tn,

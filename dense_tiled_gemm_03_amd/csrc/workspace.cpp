@@ -2,10 +2,12 @@
 // workgroups (the split-K skinny kernel): one buffer per (device, stream),
 // allocated on first use, grown on demand and kept until the process ends.
 //
-// Contract with the kernels: the first `zeroed` bytes of the buffer (the
-// completion counters) are zero whenever a kernel that uses them starts, and
-// every such kernel leaves them zero when it ends.  A fresh buffer is
-// cleared on the stream before any kernel runs on it.  Work on one stream is
+// Contract with the kernels: the first kWorkspaceCounterBytes of the buffer
+// (the completion counters) are zero whenever a kernel that uses them
+// starts, and every such kernel leaves them zero when it ends; partial
+// results live only past that area, so a call with few counters and large
+// partials never leaves data where a later call with more counters looks.
+// A fresh buffer is cleared on the stream before any kernel runs on it.  Work on one stream is
 // ordered, so calls on one stream never share the buffer at the same time;
 // each stream has its own buffer.
 #include <hip/hip_runtime.h>

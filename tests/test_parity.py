@@ -330,6 +330,33 @@ def test_split_k_shard_shape():
     H.assert_bit_exact("bf16", c[rows], C_ref, "shard int")
 
 
+
+def test_split_k_scratch_reused_by_more_tiles():
+    """Two split-K products in a row on one stream: 64 tiles split 4 ways
+    (large partials, few counters), then 80 tiles split 3 ways, which fits
+    the same scratch.  The second call's counters for tiles 64..79 must not
+    start from the first call's partial data: bit-exact on integer inputs."""
+    K = 2048
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        M, N = 2048, 1792
+        a, b = gen.normal((M, K), 71, 0, "bf16"), gen.normal((N, K), 71, 1, "bf16")
+        H.log(f"split-K scratch reuse, first call {M}x{N}x{K}")
+        c, plan = H.run16("bf16", M, N, K, H.dev(a), K, 1, H.dev(b), 1, K)
+        assert plan == "tile_nt_256x224_splitk4", plan
+        rows = gen.sample_rows(M, 128, 71)
+        C_ref, S = oracle.gemm("bf16", M, N, K, a, K, 1, b, 1, K, rows=rows)
+        H.assert_within_bound("bf16", c[rows], C_ref, S, f"first call [{plan}]")
+        N = 2240
+        a, b = gen.integers((M, K), 72, 0, 64, "bf16"), gen.integers((N, K), 72, 1, 64, "bf16")
+        H.log(f"split-K scratch reuse, second call {M}x{N}x{K}")
+        c, plan = H.run16("bf16", M, N, K, H.dev(a), K, 1, H.dev(b), 1, K)
+        assert plan == "tile_nt_256x224_splitk3", plan
+        rows = np.union1d(gen.sample_rows(M, 128, 72), np.arange(1024, 2048, 61))
+        C_ref, _ = oracle.gemm("bf16", M, N, K, a, K, 1, b, 1, K, rows=rows)
+        H.assert_bit_exact("bf16", c[rows], C_ref, f"second call [{plan}]")
+    torch.cuda.synchronize()
+
 # ------------------------------------------------------------ skinny kernel
 
 # (M, N, K): one split (short K) and split-K across workgroups (K of 16 or
