@@ -1,9 +1,10 @@
 // Registration of the tuned tile kernel (tile_mfma.hpp) for B stored N x K
 // (both operands K-contiguous), the layout of the 4096 x 7168 x 16384 BF16
 // GEMM reported for the Ascend release in "Getting to know TileLang"
-// (six-piece section).  Products with too few tiles to fill the CUs (a
-// one-GPU shard of that product, 4096 x 896 x 16384, has 64) split K across
-// the workgroups of a tile.
+// (six-piece section).  Products with too few tiles to fill the CUs take
+// 128 x 128 tiles when K is short, and split K across the workgroups of a
+// tile (a one-GPU shard of that product, 4096 x 896 x 16384, has 64 tiles
+// of 256 x 224, each split 4 ways).
 #include "tile_mfma.hpp"
 
 namespace tg {
@@ -13,6 +14,7 @@ using tile::Mfma16;
 using tile::Mfma32;
 typedef tile::Tile<256, 224, Mfma16> Tile224;  // wave tile 128 x 112, 16x16x32 MFMAs
 typedef tile::Tile<256, 256, Mfma32> Tile256;  // wave tile 128 x 128, 32x32x16 MFMAs
+typedef tile::Tile<128, 128, Mfma16> Tile128;  // wave tile 64 x 64, 16x16x32 MFMAs
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // Both operands K-contiguous with 16-byte aligned rows; offsets inside one
@@ -30,30 +32,36 @@ bool accepts(Op op, const GemmArgs& a) {
 }
 
 constexpr int64_t kCus = 256;
+constexpr int64_t kShortK = 128;  // K slices (of 64) up to which small grids take 128 x 128
 
-// Split K when the tiles would fill fewer than half the CUs: as many splits
-// as bring the grid to about one workgroup per CU, at most 8, with at least
-// 8 K slices (of 64) per split.  Each split past the first adds about two
-// K slices' time to the combine (the last split of a tile reads the others'
-// partials, latency-bound at about 65 GB/s on one CU), so nk / S slices plus
-// 2 (S - 1) is smallest near S = sqrt(nk / 2), the last cap.  Only the
-// 256 x 224 tile splits: a grid that
-// small is a single wave for either shape, where 256 x 224 always costs less
-// (see use224 below), so the 256 x 256 tile only runs grids too large to
-// split.
-template <typename Cfg>
-constexpr bool kSplitsK = std::is_same<Cfg, Tile224>::value;
+// A grid of 256 x 224 tiles is small when it fills at most half the CUs.
+bool small_grid(const GemmArgs& a) { return 2 * cdiv(a.M, 256) * cdiv(a.N, 224) <= kCus; }
 
+// Split K across a tile's workgroups only for small grids.
+//  - 256 x 224 (long K): as many splits as bring the grid to about one
+//    workgroup per CU, at most 8, with at least 8 K slices (of 64) per split.
+//    Each split past the first adds about two K slices' time to the combine
+//    (the last split of a tile reads the others' partials, latency-bound at
+//    about 65 GB/s on one CU), so nk / S slices plus 2 (S - 1) is smallest
+//    near S = sqrt(nk / 2), the last cap.
+//  - 128 x 128 (K of at most kShortK slices): up to one workgroup per CU, at
+//    most 8, with at least 16 K slices per split.
+// A small grid of either shape is a single wave; the 256 x 256 tile only
+// runs grids too large to split.
 template <typename Cfg>
 int splits_for(const GemmArgs& a) {
-  if (!kSplitsK<Cfg>) return 1;
+  if (std::is_same<Cfg, Tile256>::value) return 1;
   const int64_t tiles = cdiv(a.M, Cfg::BM) * cdiv(a.N, Cfg::BN);
-  if (2 * tiles > kCus) return 1;
+  const int64_t nk = cdiv(a.K, 64);
   int64_t s = kCus / tiles;
   if (s > tile::kMaxSplits) s = tile::kMaxSplits;
-  const int64_t nk = cdiv(a.K, 64);
-  if (s > nk / 8) s = nk / 8;
-  while (s > 1 && 2 * s * s > nk) --s;
+  if (std::is_same<Cfg, Tile128>::value) {
+    if (s > nk / 16) s = nk / 16;
+  } else {
+    if (2 * tiles > kCus) return 1;
+    if (s > nk / 8) s = nk / 8;
+    while (s > 1 && 2 * s * s > nk) --s;
+  }
   return s < 2 ? 1 : (int)s;
 }
 
@@ -61,7 +69,7 @@ template <typename Cfg>
 hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
   const int tm = (int)cdiv(a.M, Cfg::BM), tn = (int)cdiv(a.N, Cfg::BN);
   const int splits = splits_for<Cfg>(a);
-  if constexpr (kSplitsK<Cfg>) {
+  if constexpr (!std::is_same<Cfg, Tile256>::value) {
    if (splits > 1) {
     // scratch: one counter per tile in the fixed counter area, then each
     // split's fp32 partial tile
@@ -93,26 +101,48 @@ hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile choice: the grid runs in ceil(tiles / 256) waves over the 256 CUs and
-// each wave costs about one tile's MFMA work, so pick the shape with the
-// smaller waves x tile area (4096 x 7168: 256 x 224 gives 512 tiles = 2 full
-// waves, 256 x 256 gives 448 tiles = 1.75 waves rounded up to 2).
+// Tile choice.  Small grids (at most half the CUs in 256 x 224 tiles) with
+// K of at most kShortK slices take 128 x 128 tiles: four times the tiles,
+// so fewer or no K splits, and a lower fixed cost per tile (measured on
+// 1024^3, 2048^3, 1024 x 1024 x 4096 and 512 x 512 x 8192: 1.6 to 3.2 times
+// faster than 256 x 224 with split K).  With longer K the larger tile's
+// lower bytes per FLOP win (4096 x 896 x 16384, 2048 x 1024 x 16384), and so
+// does 256 x 224 with split K.  Other grids run in ceil(tiles / 256) waves
+// over the 256 CUs, each wave costing about one tile's MFMA work: the shape
+// with the smaller waves x tile area (4096 x 7168: 256 x 224 gives 512 tiles
+// = 2 full waves, 256 x 256 gives 448 tiles = 1.75 waves rounded up to 2).
 int64_t cost(const GemmArgs& a, int64_t bm, int64_t bn) {
   return cdiv(cdiv(a.M, bm) * cdiv(a.N, bn), kCus) * bm * bn;
 }
-bool use224(const GemmArgs& a) { return cost(a, 256, 224) < cost(a, 256, 256); }
-
-hipError_t launch(Op op, const GemmArgs& a, hipStream_t s) {
-  return use224(a) ? launch_cfg<Tile224>(op, a, s) : launch_cfg<Tile256>(op, a, s);
+enum class Shape { T128, T224, T256 };
+Shape shape_of(const GemmArgs& a) {
+  if (small_grid(a)) return cdiv(a.K, 64) <= kShortK ? Shape::T128 : Shape::T224;
+  return cost(a, 256, 224) < cost(a, 256, 256) ? Shape::T224 : Shape::T256;
 }
 
-// plan names of the 256 x 224 tile, by split count (1 .. 8)
+hipError_t launch(Op op, const GemmArgs& a, hipStream_t s) {
+  switch (shape_of(a)) {
+    case Shape::T128: return launch_cfg<Tile128>(op, a, s);
+    case Shape::T224: return launch_cfg<Tile224>(op, a, s);
+    default: return launch_cfg<Tile256>(op, a, s);
+  }
+}
+
+// plan names by split count (1 .. 8)
 const char* const kNames224[] = {"tile_nt_256x224", "tile_nt_256x224", "tile_nt_256x224_splitk2",
                                  "tile_nt_256x224_splitk3", "tile_nt_256x224_splitk4",
                                  "tile_nt_256x224_splitk5", "tile_nt_256x224_splitk6",
                                  "tile_nt_256x224_splitk7", "tile_nt_256x224_splitk8"};
+const char* const kNames128[] = {"tile_nt_128x128", "tile_nt_128x128", "tile_nt_128x128_splitk2",
+                                 "tile_nt_128x128_splitk3", "tile_nt_128x128_splitk4",
+                                 "tile_nt_128x128_splitk5", "tile_nt_128x128_splitk6",
+                                 "tile_nt_128x128_splitk7", "tile_nt_128x128_splitk8"};
 const char* name_of(const GemmArgs& a) {
-  return use224(a) ? kNames224[splits_for<Tile224>(a)] : "tile_nt_256x256";
+  switch (shape_of(a)) {
+    case Shape::T128: return kNames128[splits_for<Tile128>(a)];
+    case Shape::T224: return kNames224[splits_for<Tile224>(a)];
+    default: return "tile_nt_256x256";
+  }
 }
 
 }  // namespace

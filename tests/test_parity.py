@@ -251,11 +251,13 @@ def test_fp8_workload_bit_exact():
 # (M, N, K, expected plan): ragged edges in M, N and K (K a multiple of 8 but
 # not of the 64-wide slice), one or both tile shapes of the N x K kernel.
 TILE_CASES = [
-    (300, 500, 136, "tile_nt_256x224"),
+    (3900, 3100, 72, "tile_nt_256x224"),
+    (4000, 3000, 136, "tile_nt_256x224"),
     (4000, 4000, 136, "tile_nt_256x256"),
-    (513, 449, 72, "tile_nt_256x224"),
-    (256, 224, 64, "tile_nt_256x224"),
-    (65, 1, 8, "tile_nt_256x224"),
+    (300, 500, 136, "tile_nt_128x128"),
+    (513, 449, 72, "tile_nt_128x128"),
+    (256, 224, 64, "tile_nt_128x128"),
+    (65, 1, 8, "tile_nt_128x128"),
 ]
 
 
@@ -279,29 +281,73 @@ def test_tile_nt_padded_leading_dims():
 
 # ---------------------------------------------------- split-K tile kernel
 
-# (M, N, K, expected plan): too few tiles to fill the CUs, so K is split
-# across each tile's workgroups; every split count the kernel takes (2 .. 8,
-# each its own combine), ragged M, N and K tails.
+# (M, N, K, expected plan): too few 256 x 224 tiles to fill the CUs.  With
+# K of more than 128 slices of 64 the 256 x 224 tile splits K across each
+# tile's workgroups, every split count 2 .. 8 (each its own combine); ragged
+# M, N and K tails.  Checked on sampled rows (and the last row).
 SPLITK_CASES = [
-    (257, 223, 1032, "tile_nt_256x224_splitk2"),
-    (520, 230, 1496, "tile_nt_256x224_splitk3"),
-    (65, 100, 2048, "tile_nt_256x224_splitk4"),
-    (300, 500, 4096, "tile_nt_256x224_splitk5"),
-    (1024, 1024, 4104, "tile_nt_256x224_splitk5"),
-    (96, 700, 5000, "tile_nt_256x224_splitk6"),
-    (130, 250, 6272, "tile_nt_256x224_splitk7"),
+    (2000, 3500, 8200, "tile_nt_256x224_splitk2"),
+    (1200, 3500, 8200, "tile_nt_256x224_splitk3"),
+    (1000, 3500, 8264, "tile_nt_256x224_splitk4"),
+    (1000, 2600, 8200, "tile_nt_256x224_splitk5"),
+    (700, 3000, 8200, "tile_nt_256x224_splitk6"),
+    (700, 2600, 8456, "tile_nt_256x224_splitk7"),
     (200, 300, 8200, "tile_nt_256x224_splitk8"),
 ]
+
+
+def _check16_rows(fmt, M, N, K, seed, int_r=None):
+    """B stored N x K; the GPU result on sampled rows (and the last row)."""
+    draw = (lambda shape, st: gen.integers(shape, seed, st, int_r, fmt)) if int_r \
+        else (lambda shape, st: gen.normal(shape, seed, st, fmt))
+    A, B = draw((M, K), 0), draw((N, K), 1)
+    H.log(f"gemm {fmt} M={M} N={N} K={K} rows int_r={int_r}")
+    c, plan = H.run16(fmt, M, N, K, H.dev(A), K, 1, H.dev(B), 1, K)
+    rows = np.union1d(gen.sample_rows(M, 48, seed), [M - 1])
+    C_ref, S = oracle.gemm(fmt, M, N, K, A, K, 1, B, 1, K, rows=rows)
+    what = f"{fmt} {M}x{N}x{K} rows [{plan}]"
+    if int_r:
+        H.assert_bit_exact(fmt, c[rows], C_ref, what)
+    else:
+        H.assert_within_bound(fmt, c[rows], C_ref, S, what)
+    return plan
 
 
 @pytest.mark.parametrize("case", SPLITK_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SPLITK_CASES])
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_tile_nt_split_k(fmt, case):
     M, N, K, want = case
-    plan = _check16(fmt, M, N, K, "nk", seed=1500 + M + N + K)
+    plan = _check16_rows(fmt, M, N, K, seed=1500 + M + N + K)
     assert plan == want, plan
     r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
-    plan = _check16(fmt, M, N, K, "nk", seed=1600 + M + N + K, int_r=r)
+    plan = _check16_rows(fmt, M, N, K, seed=1600 + M + N + K, int_r=r)
+    assert plan == want, plan
+
+
+# (M, N, K, expected plan): small grids with K of at most 128 slices take
+# 128 x 128 tiles, split K across up to 8 workgroups per tile (at least 16
+# slices each); every split count, ragged tails; checked in full.
+SPLITK128_CASES = [
+    (1000, 1000, 1000, "tile_nt_128x128"),
+    (300, 500, 2048, "tile_nt_128x128_splitk2"),
+    (257, 223, 3080, "tile_nt_128x128_splitk3"),
+    (520, 230, 4104, "tile_nt_128x128_splitk4"),
+    (130, 250, 5504, "tile_nt_128x128_splitk5"),
+    (96, 700, 6504, "tile_nt_128x128_splitk6"),
+    (65, 100, 7496, "tile_nt_128x128_splitk7"),
+    (200, 300, 8192, "tile_nt_128x128_splitk8"),
+]
+
+
+@pytest.mark.parametrize("case", SPLITK128_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SPLITK128_CASES])
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_tile_nt_128(fmt, case):
+    M, N, K, want = case
+    plan = _check16(fmt, M, N, K, "nk", seed=1700 + M + N + K)
+    assert plan == want, plan
+    r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
+    plan = _check16(fmt, M, N, K, "nk", seed=1800 + M + N + K, int_r=r)
     assert plan == want, plan
 
 
@@ -332,11 +378,11 @@ def test_split_k_shard_shape():
 
 
 def test_split_k_scratch_reused_by_more_tiles():
-    """Two split-K products in a row on one stream: 64 tiles split 4 ways
-    (large partials, few counters), then 80 tiles split 3 ways, which fits
-    the same scratch.  The second call's counters for tiles 64..79 must not
+    """Two split-K products in a row on one stream: 64 tiles of 256 x 224
+    split 4 ways (large partials, few counters), then 80 tiles split 3 ways,
+    which fits the same scratch.  The second call's counters for tiles 64..79 must not
     start from the first call's partial data: bit-exact on integer inputs."""
-    K = 2048
+    K = 8256
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         M, N = 2048, 1792
@@ -460,7 +506,7 @@ def test_split_k_graph_capture():
     A, B = H.dev(d["A"]), H.dev(d["B"])
     H.log("split-K graph capture")
     c_eager, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
-    assert plan.startswith("tile_nt_256x224_splitk"), plan
+    assert plan.startswith("tile_nt_128x128_splitk"), plan
     C_ref, _ = oracle.gemm("bf16", M, N, K, d["A"], K, 1, d["B"], 1, K)
     H.assert_bit_exact("bf16", c_eager, C_ref, "split-K eager")
     fresh, warm = torch.cuda.Stream(), torch.cuda.Stream()
