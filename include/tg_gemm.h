@@ -37,7 +37,10 @@
  *    runs without splitting K instead.  No other call allocates.
  *  - Calls are asynchronous: they enqueue on `stream` (a hipStream_t; NULL is
  *    the null stream) and return.  They are reentrant; calls on different
- *    streams never share scratch.
+ *    streams never share scratch.  A call captured into a graph on a stream
+ *    whose scratch already exists uses that stream's buffer: replay the
+ *    graph where it cannot overlap other split-K work on the capturing
+ *    stream (on that stream itself, or synchronised with it).
  *  - C must not overlap A, B or the scales (undefined behaviour otherwise).
  *
  * Errors (tg_status)
