@@ -274,6 +274,32 @@ EXPECTED_PLANS = {
 }
 
 
+# The plan for each shape of the benchmark's sweep (bf16, B stored N x K) and
+# for the boundaries of the small-grid rule: small grids (at most half the
+# CUs in 256 x 224 tiles) with K of at most 128 slices of 64 take 128 x 128
+# tiles; with longer K, 256 x 224 with split K; larger grids 256 x 224 or
+# 256 x 256 by wave quantisation.
+SWEEP_PLANS = [
+    (4096, 7168, 7168, "tile_nt_256x224"),
+    (4096, 896, 16384, "tile_nt_256x224_splitk4"),
+    (1024, 1024, 4096, "tile_nt_128x128_splitk4"),
+    (2048, 2048, 2048, "tile_nt_128x128"),
+    (8192, 8192, 8192, "tile_nt_256x256"),
+    (2048, 7168, 16384, "tile_nt_256x224"),
+    (1024, 1024, 8192, "tile_nt_128x128_splitk4"),
+    (1024, 1024, 8200, "tile_nt_256x224_splitk8"),
+    (2048, 2048, 8192, "tile_nt_128x128"),
+    (4096, 4096, 1024, "tile_nt_256x256"),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP_PLANS, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SWEEP_PLANS])
+def test_sweep_plans(lib, case):
+    M, N, K, want = case
+    got = tg.tg_gemm_plan(tg.OP_BF16, M, N, K, PA, K, 1, PB, 1, K, PC, N, 1)
+    assert got == want
+
+
 @pytest.mark.parametrize("name", sorted(EXPECTED_PLANS))
 def test_workload_plans(lib, name):
     from gen import configs
