@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void gemm16_grouped(GemmArgs a, GroupTable gt)
   tile::tile_body<T, Cfg, false>(ag, tm, tn);
 }
 
-typedef tile::Tile<256, 224, tile::Mfma16> Tile224;
+typedef tile::Tile<256, 224, tile::Mfma16, 2, 3> Tile224;  // B one stage deeper than A
 typedef tile::Tile<256, 256, tile::Mfma32> Tile256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }

@@ -12,7 +12,8 @@ namespace {
 
 using tile::Mfma16;
 using tile::Mfma32;
-typedef tile::Tile<256, 224, Mfma16> Tile224;  // wave tile 128 x 112, 16x16x32 MFMAs
+// wave tile 128 x 112, 16x16x32 MFMAs; B one LDS stage deeper than A
+typedef tile::Tile<256, 224, Mfma16, 2, 3> Tile224;
 typedef tile::Tile<256, 256, Mfma32> Tile256;  // wave tile 128 x 128, 32x32x16 MFMAs
 typedef tile::Tile<128, 128, Mfma16> Tile128;  // wave tile 64 x 64, 16x16x32 MFMAs
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }

@@ -17,8 +17,10 @@
 //    registers: 128 x 112 with 16x16x32 MFMAs, 128 x 128 with 32x32x16;
 //  - K slice of 64: one LDS row is 128 bytes (eight 16-byte chunks); tiles
 //    go HBM/L2 -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging);
-//    two LDS stages, the next slice's loads in flight while the current one
-//    is multiplied;
+//    two LDS stages of A and two or three of B, the next slice's loads (and
+//    with three B stages the one after's B) in flight while the current one
+//    is multiplied -- the 256 x 224 tile's B gets the third stage (148 KiB in
+//    all), which gives a B line that misses L2 two slices to arrive;
 //  - LDS chunk swizzle: chunk c of row r sits at chunk position
 //    c ^ ((r >> 1) & 7); with it the ds_read_b128 patterns of both MFMA
 //    shapes (rows l % 16 or l % 32, chunks by lane group) are free of bank
@@ -70,17 +72,20 @@ struct Mfma16 {
   __device__ static Acc mma(T8 a, T8 b, Acc c) { return mfma16x16x32(a, b, c); }
 };
 
-template <int BM_, int BN_, typename MMA_>
+// A_ST / B_ST: LDS stages of the A and B operand tiles (2 or 3; B may run
+// one slice deeper than A, so a slow B line has two slices to arrive).
+template <int BM_, int BN_, typename MMA_, int A_ST_ = 2, int B_ST_ = 2>
 struct Tile {
   typedef MMA_ MMA;
   static constexpr int BM = BM_, BN = BN_;
+  static constexpr int A_ST = A_ST_, B_ST = B_ST_;
   static constexpr int BK = 64;                      // k per LDS stage
   static constexpr int WTM = BM / 2, WTN = BN / 2;   // wave tile (2 x 2 waves)
   static constexpr int FM = WTM / MMA::DIM, FN = WTN / MMA::DIM;
   static constexpr int SUBS = BK / MMA::KSTEP;       // MFMA sub-steps per slice
   static constexpr int ROW_BYTES = BK * 2;           // 128
   static constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = A_ST * A_BYTES + B_ST * B_BYTES;  // A stages, then B stages
   static constexpr int A_LOADS = A_BYTES / 1024 / 4;  // 1 KiB loads per wave per stage
   static constexpr int B_LOADS = B_BYTES / 1024 / 4;
   static constexpr int GM = 4;                       // M-tiles per tile-order group
@@ -88,6 +93,8 @@ struct Tile {
   static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole loads per wave");
   static_assert(FM + FN <= 15, "a sub-step's reads must fit the lgkmcnt counter");
   static_assert(SUBS % 2 == 0, "fragment buffers alternate per sub-step");
+  static_assert(A_ST == 2 && (B_ST == 2 || B_ST == 3), "B at most one stage deeper than A");
+  static_assert(LDS_BYTES <= 160 * 1024, "stages must fit the LDS");
 };
 
 // s_waitcnt immediate (gfx9 layout): wait until at most `vm` vector-memory
@@ -368,7 +375,11 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   typedef typename MMA::Acc Acc;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, SUBS = Cfg::SUBS, DIM = MMA::DIM;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * Cfg::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  // byte offsets of A stage s and B stage s in the LDS array
+  constexpr int A_ST = Cfg::A_ST, B_ST = Cfg::B_ST;
+  auto a_off = [](int s) { return s * Cfg::A_BYTES; };
+  auto b_off = [](int s) { return A_ST * Cfg::A_BYTES + s * Cfg::B_BYTES; };
   // the array's 32-bit LDS address, for the M0 operand of the LDS-direct loads
   const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
@@ -416,8 +427,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   const int nrow = lane >> 5;
   const uint32_t nchunk = (lane & 31) ^ ((8 * w + 4 * nrow) & 31);
   const uint32_t nb_lane = (uint32_t)(2 * w + nrow) * ldb * 2 + 16 * nchunk;
-  auto load_b = [&](uint32_t stage_base, int i, int k0, bool kin) {
-    const uint32_t dst = stage_base + Cfg::A_BYTES + (4 * i + w) * 1024;
+  auto load_b = [&](uint32_t b_base, int i, int k0, bool kin) {
+    const uint32_t dst = b_base + (4 * i + w) * 1024;
     if constexpr (BKN) {
       const bool rin = k0 + 8 * i + 2 * w + nrow < K;
       load_lds16(rb, dst, rin ? nb_lane + (uint32_t)(8 * i + k0) * ldb * 2 : kOutOfRange);
@@ -426,12 +437,16 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
     }
   };
 
-  auto load_stage = [&](int st, int k0) {
+  auto load_a_stage = [&](int sa, int k0) {
     const bool kin = k0 + 8 * lchunk < k_lim;
-    const uint32_t base = lds32 + st * Cfg::STAGE_BYTES;
+    const uint32_t base = lds32 + a_off(sa);
 #pragma unroll
     for (int i = 0; i < Cfg::A_LOADS; ++i)
       load_lds16(ra, base + (4 * i + w) * 1024, kin ? a_lane + i * a_step + 2 * k0 : kOutOfRange);
+  };
+  auto load_b_stage = [&](int sb, int k0) {
+    const bool kin = k0 + 8 * lchunk < k_lim;
+    const uint32_t base = lds32 + b_off(sb);
 #pragma unroll
     for (int i = 0; i < Cfg::B_LOADS; ++i) load_b(base, i, k0, kin);
   };
@@ -443,7 +458,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   const int rd_lane = (lane % DIM) * Cfg::ROW_BYTES;
   const int rd_chunk = lane / DIM;
   const int a_rd = wm * Cfg::WTM * Cfg::ROW_BYTES + rd_lane;
-  const int b_rd = Cfg::A_BYTES + wn * Cfg::WTN * Cfg::ROW_BYTES + rd_lane;
+  const int b_rd = wn * Cfg::WTN * Cfg::ROW_BYTES + rd_lane;  // within a B stage
 
   Acc acc[FM][FN];
 #pragma unroll
@@ -474,7 +489,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
         const int kr = 8 * kg + 4 * h + r;          // row within the sub-step
         const int nbase = wn * Cfg::WTN + j * DIM;  // multiple of 16
         const int chunk = (((nbase + nsub) >> 3) ^ ((4 * kr) & 31)) + (q >> 1);
-        kn_off[j][h] = Cfg::A_BYTES + kr * BROW + chunk * 16 + (q & 1) * 8;
+        kn_off[j][h] = kr * BROW + chunk * 16 + (q & 1) * 8;  // within a B stage
       }
   }
   typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -495,46 +510,46 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   constexpr int NRD = FM + BR * FN;                  // LDS reads per sub-step
   constexpr int NLD = Cfg::A_LOADS + Cfg::B_LOADS;   // LDS-direct loads per slice
   static_assert(NRD <= FM * FN && NLD <= FM * FN, "one read and one load per MFMA");
-  auto frag_base = [&](int st, int sub) {
-    return lds + st * Cfg::STAGE_BYTES + ((sub * (MMA::KSTEP / 8) + rd_chunk) ^ sw) * 16;
-  };
+  auto chunk_off = [&](int sub) { return ((sub * (MMA::KSTEP / 8) + rd_chunk) ^ sw) * 16; };
   // The r-th read of sub-step `sub` of stage st, in the order the MFMAs
   // consume fragments: a0, b0 .. b[FN-1], a1 .. a[FM-1] (a K x N B fragment
   // is a pair of reads, both issued at its first slot).
-  auto read_one = [&](int buf, int st, int sub, int r) {
-    const char* base = frag_base(st, sub);
+  auto read_one = [&](int buf, int sa, int sb, int sub, int r) {
+    const char* abase = lds + a_off(sa) + chunk_off(sub);
+    const char* bbase = lds + b_off(sb) + chunk_off(sub);
     if (r == 0) {
-      fa[buf][0] = *reinterpret_cast<const T8*>(base + a_rd);
+      fa[buf][0] = *reinterpret_cast<const T8*>(abase + a_rd);
     } else if (r <= BR * FN) {
       if constexpr (BKN) {
-        if ((r - 1) % 2 == 0)
-          fb[buf][(r - 1) / 2] = read_b_kn(lds + st * Cfg::STAGE_BYTES, sub, (r - 1) / 2);
+        if ((r - 1) % 2 == 0) fb[buf][(r - 1) / 2] = read_b_kn(lds + b_off(sb), sub, (r - 1) / 2);
       } else {
-        fb[buf][r - 1] = *reinterpret_cast<const T8*>(base + b_rd + (r - 1) * DIM * Cfg::ROW_BYTES);
+        fb[buf][r - 1] = *reinterpret_cast<const T8*>(bbase + b_rd + (r - 1) * DIM * Cfg::ROW_BYTES);
       }
     } else {
       fa[buf][r - BR * FN] =
-          *reinterpret_cast<const T8*>(base + a_rd + (r - BR * FN) * DIM * Cfg::ROW_BYTES);
+          *reinterpret_cast<const T8*>(abase + a_rd + (r - BR * FN) * DIM * Cfg::ROW_BYTES);
     }
   };
   // keeps the scheduler from moving work across it (one wave per SIMD issues
   // everything in order, so the source order below is the issue order)
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
   // One sub-step: the MFMAs on fragment buffer `cur`; after the n-th MFMA,
-  // the n-th read of the next sub-step (into buffer cur ^ 1, from `next`)
-  // and, when LOADS, the LDS-direct loads of the slice at ld_k0 into stage
-  // ld_st, spread over the sub-step.  Spreading reads and loads over the MFMA stream hides their
+  // the n-th read of the next sub-step (into buffer cur ^ 1, from A stage
+  // nsa and B stage nsb) and, when LOADS, the LDS-direct loads of A at
+  // k = ld_ka into A stage ld_sa and of B at k = ld_kb into B stage ld_sb
+  // (A's first), spread over the sub-step.  Spreading reads and loads over the MFMA stream hides their
   // issue cycles under MFMA execution and keeps at most one sub-step of
   // reads (<= 15, the lgkmcnt limit) in flight.
-  auto substep = [&](auto loads_c, int cur, int nst, int nsub, int ld_st, int ld_k0) {
+  auto substep = [&](auto loads_c, int cur, int nsa, int nsb, int nsub, int ld_sa, int ld_sb,
+                     int ld_ka, int ld_kb) {
     constexpr bool LOADS = decltype(loads_c)::value;
-    const bool kin = ld_k0 + 8 * lchunk < k_lim;
-    const uint32_t ld_base = lds32 + ld_st * Cfg::STAGE_BYTES;
+    const bool kin_a = ld_ka + 8 * lchunk < k_lim, kin_b = ld_kb + 8 * lchunk < k_lim;
+    const uint32_t ld_abase = lds32 + a_off(ld_sa), ld_bbase = lds32 + b_off(ld_sb);
 #pragma unroll
     for (int n = 0; n < FM * FN; ++n) {
       const int i = n / FN, j = n % FN;
       acc[i][j] = MMA::mma(fa[cur][i], fb[cur][j], acc[i][j]);
-      if (n < NRD) read_one(cur ^ 1, nst, nsub, n);
+      if (n < NRD) read_one(cur ^ 1, nsa, nsb, nsub, n);
       if constexpr (LOADS) {
         // load q goes after MFMA q * FM * FN / NLD: spread evenly, since a CU
         // moves 64 B per clock from L2 and a burst of loads would stall the
@@ -543,44 +558,64 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
         for (int q = 0; q < NLD; ++q) {
           if (q * FM * FN / NLD != n) continue;
           if (q < Cfg::A_LOADS)
-            load_lds16(ra, ld_base + (4 * q + w) * 1024,
-                       kin ? a_lane + q * a_step + 2 * ld_k0 : kOutOfRange);
+            load_lds16(ra, ld_abase + (4 * q + w) * 1024,
+                       kin_a ? a_lane + q * a_step + 2 * ld_ka : kOutOfRange);
           else
-            load_b(ld_base, q - Cfg::A_LOADS, ld_k0, kin);
+            load_b(ld_bbase, q - Cfg::A_LOADS, ld_kb, kin_b);
         }
       }
       fence();
     }
   };
 
-  // Pipeline, per slice kt in stage st = kt & 1 (sub-steps s = 0 .. SUBS-1):
+  // Pipeline, per slice kt in A stage sa = kt mod A_ST and B stage
+  // sb = kt mod B_ST (sub-steps s = 0 .. SUBS-1):
   //   s < SUBS-1: MFMAs of sub-step s | reads of sub-step s+1;
   //   then: wait for this wave's loads of slice kt+1 and barrier (after it,
-  //     slice kt+1 is in LDS for every wave, and every wave's reads of stage
-  //     st have returned -- the last sub-step needs them now anyway);
-  //   s = SUBS-1: MFMAs | reads of sub-step 0 of kt+1 | loads of slice
-  //     kt+2 -> stage st.
+  //     slice kt+1 is in LDS for every wave, and every wave's reads of
+  //     stages sa, sb have returned -- the last sub-step needs them now);
+  //   s = SUBS-1: MFMAs | reads of sub-step 0 of kt+1 | loads of A for
+  //     slice kt+A_ST -> A stage sa, then of B for slice kt+B_ST -> B stage sb.
+  // Slice kt's batch is [A(kt+A_ST), B(kt+B_ST)].  At the wait of slice kt the
+  // newest loads are those of batch kt-1, [A(kt+1), B(kt+B_ST-1)]: with
+  // B_ST = 2 everything must land (vmcnt 0); with B_ST = 3, B(kt+2) may stay
+  // in flight (vmcnt B_LOADS), B(kt+1) being older.  The prologue issues the
+  // same sequence for the batches before slice 0: [B(0)] when B_ST = 3, then
+  // [A(0), B(B_ST-2)], [A(1), B(B_ST-1)].
   // Slices at or past K are fetched with out-of-range offsets: they move no
   // data, fill the idle stage with zeros and keep the loop free of branches.
-  load_stage(0, kb0 * BK);
-  load_stage(1, (kb0 + 1) * BK);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");
+  if constexpr (B_ST == 3) load_b_stage(0, kb0 * BK);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    load_a_stage(j, (kb0 + j) * BK);
+    load_b_stage(j + B_ST - 2, (kb0 + j + B_ST - 2) * BK);
+  }
+  // slice 0 landed: with B_ST = 2 the loads after B(0) are A(1), B(1); with
+  // B_ST = 3 the loads after A(0) are B(1), A(1), B(2)
+  constexpr int INIT_WAIT = B_ST == 2 ? NLD : NLD + Cfg::B_LOADS;
+  constexpr int LOOP_WAIT = B_ST == 2 ? 0 : Cfg::B_LOADS;
+  static_assert(INIT_WAIT <= 63, "loads in flight must fit the vmcnt counter");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INIT_WAIT) : "memory");
   __syncthreads();
   {
 #pragma unroll
-    for (int r = 0; r < NRD; ++r) read_one(0, 0, 0, r);
+    for (int r = 0; r < NRD; ++r) read_one(0, 0, 0, 0, r);
   }
+  int sa = 0, sb = 0;
   for (int kt = kb0; kt < kb1; ++kt) {
-    const int st = (kt - kb0) & 1;
+    const int nsa = sa ^ 1, nsb = sb + 1 == B_ST ? 0 : sb + 1;
 #pragma unroll
     for (int sub = 0; sub < SUBS - 1; ++sub) {
       fence();
-      substep(std::false_type(), sub & 1, st, sub + 1, 0, 0);
+      substep(std::false_type(), sub & 1, sa, sb, sub + 1, 0, 0, 0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOOP_WAIT) : "memory");
     __syncthreads();
     fence();
-    substep(std::true_type(), (SUBS - 1) & 1, st ^ 1, 0, st, (kt + 2) * BK);
+    substep(std::true_type(), (SUBS - 1) & 1, nsa, nsb, 0, sa, sb, (kt + A_ST) * BK,
+            (kt + B_ST) * BK);
+    sa = nsa;
+    sb = nsb;
   }
 
   if constexpr (SPLIT) {
