@@ -15,7 +15,11 @@ using tile::Mfma32;
 // wave tile 128 x 112, 16x16x32 MFMAs; B one LDS stage deeper than A
 typedef tile::Tile<256, 224, Mfma16, 2, 3> Tile224;
 typedef tile::Tile<256, 256, Mfma32> Tile256;  // wave tile 128 x 128, 32x32x16 MFMAs
-typedef tile::Tile<128, 128, Mfma16> Tile128;  // wave tile 64 x 64, 16x16x32 MFMAs
+// wave tile 64 x 64, 16x16x32 MFMAs: three stages of A and of B (96 KiB) for
+// grids of at most one workgroup per CU; two of each (64 KiB, two workgroups
+// per CU) for larger grids
+typedef tile::Tile<128, 128, Mfma16, 3, 3> Tile128;
+typedef tile::Tile<128, 128, Mfma16, 2, 2> Tile128x2;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // Both operands K-contiguous with 16-byte aligned rows; offsets inside one
@@ -51,7 +55,7 @@ bool small_grid(const GemmArgs& a) { return 2 * cdiv(a.M, 256) * cdiv(a.N, 224) 
 // runs grids too large to split.
 template <typename Cfg>
 int splits_for(const GemmArgs& a) {
-  if (std::is_same<Cfg, Tile256>::value) return 1;
+  if (std::is_same<Cfg, Tile256>::value || std::is_same<Cfg, Tile128x2>::value) return 1;
   const int64_t tiles = cdiv(a.M, Cfg::BM) * cdiv(a.N, Cfg::BN);
   const int64_t nk = cdiv(a.K, 64);
   int64_t s = kCus / tiles;
@@ -70,7 +74,7 @@ template <typename Cfg>
 hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
   const int tm = (int)cdiv(a.M, Cfg::BM), tn = (int)cdiv(a.N, Cfg::BN);
   const int splits = splits_for<Cfg>(a);
-  if constexpr (!std::is_same<Cfg, Tile256>::value) {
+  if constexpr (std::is_same<Cfg, Tile224>::value || std::is_same<Cfg, Tile128>::value) {
    if (splits > 1) {
     // scratch: one counter per tile in the fixed counter area, then each
     // split's fp32 partial tile
@@ -106,7 +110,10 @@ hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
 // K of at most kShortK slices take 128 x 128 tiles: four times the tiles,
 // so fewer or no K splits, and a lower fixed cost per tile (measured on
 // 1024^3, 2048^3, 1024 x 1024 x 4096 and 512 x 512 x 8192: 1.6 to 3.2 times
-// faster than 256 x 224 with split K).  With longer K the larger tile's
+// faster than 256 x 224 with split K).  Up to 256 of them run with three
+// stages per operand, one workgroup per CU (2048^3: 18.3 us against 24.0
+// with two stages); more run with two stages, two workgroups per CU
+// (4096 x 1792 x 4096: 50.4 us against 57.1 with three).  With longer K the larger tile's
 // lower bytes per FLOP win (4096 x 896 x 16384, 2048 x 1024 x 16384), and so
 // does 256 x 224 with split K.  Other grids run in ceil(tiles / 256) waves
 // over the 256 CUs, each wave costing about one tile's MFMA work: the shape
@@ -115,15 +122,19 @@ hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
 int64_t cost(const GemmArgs& a, int64_t bm, int64_t bn) {
   return cdiv(cdiv(a.M, bm) * cdiv(a.N, bn), kCus) * bm * bn;
 }
-enum class Shape { T128, T224, T256 };
+enum class Shape { T128, T128x2, T224, T256 };
 Shape shape_of(const GemmArgs& a) {
-  if (small_grid(a)) return cdiv(a.K, 64) <= kShortK ? Shape::T128 : Shape::T224;
+  if (small_grid(a)) {
+    if (cdiv(a.K, 64) > kShortK) return Shape::T224;
+    return cdiv(a.M, 128) * cdiv(a.N, 128) <= kCus ? Shape::T128 : Shape::T128x2;
+  }
   return cost(a, 256, 224) < cost(a, 256, 256) ? Shape::T224 : Shape::T256;
 }
 
 hipError_t launch(Op op, const GemmArgs& a, hipStream_t s) {
   switch (shape_of(a)) {
     case Shape::T128: return launch_cfg<Tile128>(op, a, s);
+    case Shape::T128x2: return launch_cfg<Tile128x2>(op, a, s);
     case Shape::T224: return launch_cfg<Tile224>(op, a, s);
     default: return launch_cfg<Tile256>(op, a, s);
   }
@@ -141,6 +152,7 @@ const char* const kNames128[] = {"tile_nt_128x128", "tile_nt_128x128", "tile_nt_
 const char* name_of(const GemmArgs& a) {
   switch (shape_of(a)) {
     case Shape::T128: return kNames128[splits_for<Tile128>(a)];
+    case Shape::T128x2: return "tile_nt_128x128_2stage";
     case Shape::T224: return kNames224[splits_for<Tile224>(a)];
     default: return "tile_nt_256x256";
   }

@@ -72,8 +72,9 @@ struct Mfma16 {
   __device__ static Acc mma(T8 a, T8 b, Acc c) { return mfma16x16x32(a, b, c); }
 };
 
-// A_ST / B_ST: LDS stages of the A and B operand tiles (2 or 3; B may run
-// one slice deeper than A, so a slow B line has two slices to arrive).
+// A_ST / B_ST: LDS stages of the A and B operand tiles (at least 2; B at
+// least as deep as A).  With S stages an operand's loads have S - 1 slices
+// to arrive.
 template <int BM_, int BN_, typename MMA_, int A_ST_ = 2, int B_ST_ = 2>
 struct Tile {
   typedef MMA_ MMA;
@@ -93,7 +94,7 @@ struct Tile {
   static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole loads per wave");
   static_assert(FM + FN <= 15, "a sub-step's reads must fit the lgkmcnt counter");
   static_assert(SUBS % 2 == 0, "fragment buffers alternate per sub-step");
-  static_assert(A_ST == 2 && (B_ST == 2 || B_ST == 3), "B at most one stage deeper than A");
+  static_assert(A_ST >= 2 && B_ST >= A_ST, "at least two stages, B at least as deep as A");
   static_assert(LDS_BYTES <= 160 * 1024, "stages must fit the LDS");
 };
 
@@ -576,24 +577,23 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   //     stages sa, sb have returned -- the last sub-step needs them now);
   //   s = SUBS-1: MFMAs | reads of sub-step 0 of kt+1 | loads of A for
   //     slice kt+A_ST -> A stage sa, then of B for slice kt+B_ST -> B stage sb.
-  // Slice kt's batch is [A(kt+A_ST), B(kt+B_ST)].  At the wait of slice kt the
-  // newest loads are those of batch kt-1, [A(kt+1), B(kt+B_ST-1)]: with
-  // B_ST = 2 everything must land (vmcnt 0); with B_ST = 3, B(kt+2) may stay
-  // in flight (vmcnt B_LOADS), B(kt+1) being older.  The prologue issues the
-  // same sequence for the batches before slice 0: [B(0)] when B_ST = 3, then
-  // [A(0), B(B_ST-2)], [A(1), B(B_ST-1)].
+  // Slice j's batch is [A(j+A_ST), B(j+B_ST)]; the prologue issues the
+  // batches j = -B_ST .. -1 the same way (the parts with a slice >= 0).  At
+  // the wait of slice kt, A(kt+1) is in batch kt+1-A_ST and B(kt+1) in batch
+  // kt+1-B_ST (the same one when B_ST == A_ST, then after A(kt+1)); what may
+  // stay in flight is everything issued after the later of the two: the
+  // batches kt+2-A_ST .. kt-1, plus batch kt+1-A_ST's B loads when B is
+  // deeper.  Before slice 0 likewise, with one more batch.
   // Slices at or past K are fetched with out-of-range offsets: they move no
   // data, fill the idle stage with zeros and keep the loop free of branches.
-  if constexpr (B_ST == 3) load_b_stage(0, kb0 * BK);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    load_a_stage(j, (kb0 + j) * BK);
-    load_b_stage(j + B_ST - 2, (kb0 + j + B_ST - 2) * BK);
+  for (int j = -B_ST; j < 0; ++j) {
+    if (j + A_ST >= 0) load_a_stage(j + A_ST, (kb0 + j + A_ST) * BK);
+    if (j + B_ST >= 0) load_b_stage(j + B_ST, (kb0 + j + B_ST) * BK);
   }
-  // slice 0 landed: with B_ST = 2 the loads after B(0) are A(1), B(1); with
-  // B_ST = 3 the loads after A(0) are B(1), A(1), B(2)
-  constexpr int INIT_WAIT = B_ST == 2 ? NLD : NLD + Cfg::B_LOADS;
-  constexpr int LOOP_WAIT = B_ST == 2 ? 0 : Cfg::B_LOADS;
+  constexpr int B_TAIL = B_ST > A_ST ? Cfg::B_LOADS : 0;
+  constexpr int INIT_WAIT = B_TAIL + (A_ST - 1) * NLD;
+  constexpr int LOOP_WAIT = B_TAIL + (A_ST - 2) * NLD;
   static_assert(INIT_WAIT <= 63, "loads in flight must fit the vmcnt counter");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INIT_WAIT) : "memory");
   __syncthreads();
@@ -603,7 +603,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   }
   int sa = 0, sb = 0;
   for (int kt = kb0; kt < kb1; ++kt) {
-    const int nsa = sa ^ 1, nsb = sb + 1 == B_ST ? 0 : sb + 1;
+    const int nsa = sa + 1 == A_ST ? 0 : sa + 1, nsb = sb + 1 == B_ST ? 0 : sb + 1;
 #pragma unroll
     for (int sub = 0; sub < SUBS - 1; ++sub) {
       fence();

@@ -277,8 +277,9 @@ EXPECTED_PLANS = {
 # The plan for each shape of the benchmark's sweep (bf16, B stored N x K) and
 # for the boundaries of the small-grid rule: small grids (at most half the
 # CUs in 256 x 224 tiles) with K of at most 128 slices of 64 take 128 x 128
-# tiles; with longer K, 256 x 224 with split K; larger grids 256 x 224 or
-# 256 x 256 by wave quantisation.
+# tiles (two-stage when there are more than 256 of them); with longer K,
+# 256 x 224 with split K; larger grids 256 x 224 or 256 x 256 by wave
+# quantisation.
 SWEEP_PLANS = [
     (4096, 7168, 7168, "tile_nt_256x224"),
     (4096, 896, 16384, "tile_nt_256x224_splitk4"),
@@ -290,6 +291,8 @@ SWEEP_PLANS = [
     (1024, 1024, 8200, "tile_nt_256x224_splitk8"),
     (2048, 2048, 8192, "tile_nt_128x128"),
     (4096, 4096, 1024, "tile_nt_256x256"),
+    (4096, 1792, 4096, "tile_nt_128x128_2stage"),
+    (4096, 1024, 4096, "tile_nt_128x128"),
 ]
 
 

@@ -326,7 +326,8 @@ def test_tile_nt_split_k(fmt, case):
 
 # (M, N, K, expected plan): small grids with K of at most 128 slices take
 # 128 x 128 tiles, split K across up to 8 workgroups per tile (at least 16
-# slices each); every split count, ragged tails; checked in full.
+# slices each); every split count, ragged tails; checked in full.  Grids of
+# more than 256 such tiles take the two-stage version (two workgroups per CU).
 SPLITK128_CASES = [
     (1000, 1000, 1000, "tile_nt_128x128"),
     (300, 500, 2048, "tile_nt_128x128_splitk2"),
@@ -336,6 +337,7 @@ SPLITK128_CASES = [
     (96, 700, 6504, "tile_nt_128x128_splitk6"),
     (65, 100, 7496, "tile_nt_128x128_splitk7"),
     (200, 300, 8192, "tile_nt_128x128_splitk8"),
+    (2200, 2000, 200, "tile_nt_128x128_2stage"),
 ]
 
 
