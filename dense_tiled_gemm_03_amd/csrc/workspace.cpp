@@ -1,15 +1,20 @@
 // Device scratch for kernels that combine partial results of several
-// workgroups (the split-K skinny kernel): one buffer per (device, stream),
-// allocated on first use, grown on demand and kept until the process ends.
+// workgroups (the split-K skinny and tile kernels): one buffer per (device,
+// stream), allocated on first use, grown on demand and kept until the
+// process ends.  A buffer that has been outgrown is retired, not freed: a
+// graph captured on the stream may still hold kernels that use it, and
+// replaying such a graph must not touch freed memory.  Each growth at least
+// doubles the size, so the retired buffers of a stream add up to less than
+// its current one.
 //
 // Contract with the kernels: the first kWorkspaceCounterBytes of the buffer
 // (the completion counters) are zero whenever a kernel that uses them
 // starts, and every such kernel leaves them zero when it ends; partial
 // results live only past that area, so a call with few counters and large
 // partials never leaves data where a later call with more counters looks.
-// A fresh buffer is cleared on the stream before any kernel runs on it.  Work on one stream is
-// ordered, so calls on one stream never share the buffer at the same time;
-// each stream has its own buffer.
+// A fresh buffer is cleared on the stream before any kernel runs on it.
+// Work on one stream is ordered, so calls on one stream never share the
+// buffer at the same time; each stream has its own buffer.
 #include <hip/hip_runtime.h>
 
 #include <map>
@@ -45,13 +50,10 @@ void* stream_workspace(hipStream_t stream, size_t bytes) {
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
     return nullptr;
-  if (b.ptr != nullptr) {
-    // earlier kernels on this stream may still use the old buffer
-    if (hipStreamSynchronize(stream) != hipSuccess) return nullptr;
-    (void)hipFree(b.ptr);
-    b = Buffer{};
-  }
-  const size_t want = (bytes + 0xFFFFF) & ~size_t(0xFFFFF);  // whole MiB
+  // whole MiB, at least twice the buffer it replaces; the old one stays
+  // allocated (earlier kernels or captured graphs may still use it)
+  size_t want = (bytes + 0xFFFFF) & ~size_t(0xFFFFF);
+  if (want < 2 * b.bytes) want = 2 * b.bytes;
   void* p = nullptr;
   if (hipMalloc(&p, want) != hipSuccess) {
     (void)hipGetLastError();
@@ -61,7 +63,7 @@ void* stream_workspace(hipStream_t stream, size_t bytes) {
     (void)hipFree(p);
     return nullptr;
   }
-  b.ptr = p;
+  b.ptr = p;  // the outgrown buffer, if any, is retired: never freed
   b.bytes = want;
   return p;
 }

@@ -28,9 +28,11 @@
  *  - Scratch: products with M <= 64, and products whose output tiles would
  *    fill fewer than half the CUs, split K across workgroups and combine the
  *    partial results through a device buffer the library owns, one per
- *    (device, stream), allocated on the first such call on that stream (and
- *    grown, after synchronising the stream, when a later call needs more) and
- *    kept until the process ends: a fixed 16 KiB area of completion counters,
+ *    (device, stream), allocated on the first such call on that stream,
+ *    grown (at least doubling) when a later call needs more, and kept until
+ *    the process ends -- an outgrown buffer is not freed either, since a
+ *    graph captured earlier may still use it: a fixed 16 KiB area of
+ *    completion counters,
  *    then the fp32 partial tiles -- about 32 KiB per 64 x 128 block of C per
  *    K split (7.3 MiB for 64 x 7168 x 7168).  Such a call made while the
  *    stream is being captured into a graph, or when the buffer cannot be had,

@@ -533,6 +533,45 @@ def test_split_k_graph_capture():
         assert np.array_equal(C2.cpu().numpy().view(np.uint16), c_eager)
 
 
+
+def test_split_k_graph_survives_scratch_growth():
+    """A graph captured with split K on a stream whose scratch exists keeps
+    working after a larger split-K call on that stream has grown the
+    scratch: the outgrown buffer stays allocated.  Replays give the eager
+    result bit for bit (integer inputs)."""
+    M, N, K = 1024, 1024, 4096
+    w = configs.Workload("t", "bf16", M, N, K, "nk", "normal", 79, 0)
+    d = configs.make_inputs(w, int_r=32)
+    A, B = H.dev(d["A"]), H.dev(d["B"])
+    H.log("split-K graph across scratch growth")
+    c_eager, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+    assert plan.startswith("tile_nt_128x128_splitk"), plan
+    warm = torch.cuda.Stream()
+    C = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    with torch.cuda.stream(warm):
+        H.tg.tg_gemm_bf16(M, N, K, A.data_ptr(), K, 1, B.data_ptr(), 1, K, C.data_ptr(), N, 1,
+                          warm.cuda_stream)
+    torch.cuda.synchronize()
+    g = _capture_skinny(warm, M, N, K, A, B, C)
+    torch.cuda.synchronize()
+    # a split-K call with much larger partials on the same stream grows its scratch
+    Mb, Nb, Kb = 4096, 896, 16384
+    wb = configs.Workload("shard", "bf16", Mb, Nb, Kb, "nk", "normal", 80, 0)
+    db = configs.make_inputs(wb, int_r=32)
+    Ab, Bb = H.dev(db["A"]), H.dev(db["B"])
+    with torch.cuda.stream(warm):
+        cb, plan_b = H.run16("bf16", Mb, Nb, Kb, Ab, Kb, 1, Bb, 1, Kb, stream=warm.cuda_stream)
+    assert plan_b == "tile_nt_256x224_splitk4", plan_b
+    rows = gen.sample_rows(Mb, 32, 80)
+    C_ref, _ = oracle.gemm("bf16", Mb, Nb, Kb, db["A"], Kb, 1, db["B"], 1, Kb, rows=rows)
+    H.assert_bit_exact("bf16", cb[rows], C_ref, "grown scratch")
+    for _ in range(3):
+        C.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy().view(np.uint16), c_eager)
+
 # ------------------------------------------------------ K x N tile kernel
 
 NN_CASES = [(300, 512, 136), (513, 264, 72), (4000, 4000, 136), (256, 256, 64), (65, 8, 8),
