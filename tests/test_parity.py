@@ -249,8 +249,11 @@ def test_fp8_workload_bit_exact():
 # ------------------------------------------------------- tuned tile kernels
 
 # (M, N, K, expected plan): ragged edges in M, N and K (K a multiple of 8 but
-# not of the 64-wide slice), one or both tile shapes of the N x K kernel.
+# not of the 64-wide slice; a single slice, so every slice the deeper stage
+# rings prefetch lies past K), each tile shape of the N x K kernel.
 TILE_CASES = [
+    (4000, 3000, 8, "tile_nt_256x224"),
+    (2200, 2000, 8, "tile_nt_128x128_2stage"),
     (3900, 3100, 72, "tile_nt_256x224"),
     (4000, 3000, 136, "tile_nt_256x224"),
     (4000, 4000, 136, "tile_nt_256x256"),
