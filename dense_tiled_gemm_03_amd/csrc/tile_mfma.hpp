@@ -72,9 +72,8 @@ struct Mfma16 {
   __device__ static Acc mma(T8 a, T8 b, Acc c) { return mfma16x16x32(a, b, c); }
 };
 
-// A_ST / B_ST: LDS stages of the A and B operand tiles (at least 2; B at
-// least as deep as A).  With S stages an operand's loads have S - 1 slices
-// to arrive.
+// A_ST / B_ST: LDS stages of the A and B operand tiles (at least 2 each).
+// With S stages an operand's loads have S - 1 slices to arrive.
 template <int BM_, int BN_, typename MMA_, int A_ST_ = 2, int B_ST_ = 2>
 struct Tile {
   typedef MMA_ MMA;
@@ -94,7 +93,7 @@ struct Tile {
   static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole loads per wave");
   static_assert(FM + FN <= 15, "a sub-step's reads must fit the lgkmcnt counter");
   static_assert(SUBS % 2 == 0, "fragment buffers alternate per sub-step");
-  static_assert(A_ST >= 2 && B_ST >= A_ST, "at least two stages, B at least as deep as A");
+  static_assert(A_ST >= 2 && B_ST >= 2, "at least two stages of each operand");
   static_assert(LDS_BYTES <= 160 * 1024, "stages must fit the LDS");
 };
 
@@ -379,6 +378,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   // byte offsets of A stage s and B stage s in the LDS array
   constexpr int A_ST = Cfg::A_ST, B_ST = Cfg::B_ST;
+  // each slice's batch of loads starts with the shallower ring's
+  constexpr bool A_FIRST = A_ST <= B_ST;
   auto a_off = [](int s) { return s * Cfg::A_BYTES; };
   auto b_off = [](int s) { return A_ST * Cfg::A_BYTES + s * Cfg::B_BYTES; };
   // the array's 32-bit LDS address, for the M0 operand of the LDS-direct loads
@@ -538,7 +539,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   // the n-th read of the next sub-step (into buffer cur ^ 1, from A stage
   // nsa and B stage nsb) and, when LOADS, the LDS-direct loads of A at
   // k = ld_ka into A stage ld_sa and of B at k = ld_kb into B stage ld_sb
-  // (A's first), spread over the sub-step.  Spreading reads and loads over the MFMA stream hides their
+  // (the shallower ring's first; A's when both are as deep), spread over
+  // the sub-step.  Spreading reads and loads over the MFMA stream hides their
   // issue cycles under MFMA execution and keeps at most one sub-step of
   // reads (<= 15, the lgkmcnt limit) in flight.
   auto substep = [&](auto loads_c, int cur, int nsa, int nsb, int nsub, int ld_sa, int ld_sb,
@@ -558,11 +560,14 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
 #pragma unroll
         for (int q = 0; q < NLD; ++q) {
           if (q * FM * FN / NLD != n) continue;
-          if (q < Cfg::A_LOADS)
-            load_lds16(ra, ld_abase + (4 * q + w) * 1024,
-                       kin_a ? a_lane + q * a_step + 2 * ld_ka : kOutOfRange);
+          constexpr int FIRST = A_FIRST ? Cfg::A_LOADS : Cfg::B_LOADS;
+          const bool is_a = A_FIRST ? q < FIRST : q >= FIRST;
+          const int qa = A_FIRST ? q : q - FIRST, qb = A_FIRST ? q - FIRST : q;
+          if (is_a)
+            load_lds16(ra, ld_abase + (4 * qa + w) * 1024,
+                       kin_a ? a_lane + qa * a_step + 2 * ld_ka : kOutOfRange);
           else
-            load_b(ld_bbase, q - Cfg::A_LOADS, ld_kb, kin_b);
+            load_b(ld_bbase, qb, ld_kb, kin_b);
         }
       }
       fence();
@@ -576,24 +581,33 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   //     slice kt+1 is in LDS for every wave, and every wave's reads of
   //     stages sa, sb have returned -- the last sub-step needs them now);
   //   s = SUBS-1: MFMAs | reads of sub-step 0 of kt+1 | loads of A for
-  //     slice kt+A_ST -> A stage sa, then of B for slice kt+B_ST -> B stage sb.
-  // Slice j's batch is [A(j+A_ST), B(j+B_ST)]; the prologue issues the
-  // batches j = -B_ST .. -1 the same way (the parts with a slice >= 0).  At
-  // the wait of slice kt, A(kt+1) is in batch kt+1-A_ST and B(kt+1) in batch
-  // kt+1-B_ST (the same one when B_ST == A_ST, then after A(kt+1)); what may
-  // stay in flight is everything issued after the later of the two: the
-  // batches kt+2-A_ST .. kt-1, plus batch kt+1-A_ST's B loads when B is
-  // deeper.  Before slice 0 likewise, with one more batch.
+  //     slice kt+A_ST -> A stage sa and of B for slice kt+B_ST -> B stage sb.
+  // Slice j's batch is the loads of the shallower ring (A when both are as
+  // deep), then of the deeper one: A(j+A_ST) and B(j+B_ST).  The prologue
+  // issues the batches j = -max(A_ST, B_ST) .. -1 the same way (the parts
+  // with a slice >= 0).  At the wait of slice kt, the shallower operand's
+  // slice kt+1 is in batch kt+1-S (S = its stage count, first in that
+  // batch) and the deeper one's in the same batch after it when the rings
+  // are as deep, else in an older batch; what may stay in flight is
+  // everything issued after: the deeper operand's part of batch kt+1-S
+  // when it is deeper, and the batches kt+2-S .. kt-1.  Before slice 0
+  // likewise, with one more batch.
   // Slices at or past K are fetched with out-of-range offsets: they move no
   // data, fill the idle stage with zeros and keep the loop free of branches.
+  constexpr int DEEP = A_ST > B_ST ? A_ST : B_ST, SHALLOW = A_ST > B_ST ? B_ST : A_ST;
 #pragma unroll
-  for (int j = -B_ST; j < 0; ++j) {
-    if (j + A_ST >= 0) load_a_stage(j + A_ST, (kb0 + j + A_ST) * BK);
-    if (j + B_ST >= 0) load_b_stage(j + B_ST, (kb0 + j + B_ST) * BK);
+  for (int j = -DEEP; j < 0; ++j) {
+    if (A_FIRST) {
+      if (j + A_ST >= 0) load_a_stage(j + A_ST, (kb0 + j + A_ST) * BK);
+      if (j + B_ST >= 0) load_b_stage(j + B_ST, (kb0 + j + B_ST) * BK);
+    } else {
+      if (j + B_ST >= 0) load_b_stage(j + B_ST, (kb0 + j + B_ST) * BK);
+      if (j + A_ST >= 0) load_a_stage(j + A_ST, (kb0 + j + A_ST) * BK);
+    }
   }
-  constexpr int B_TAIL = B_ST > A_ST ? Cfg::B_LOADS : 0;
-  constexpr int INIT_WAIT = B_TAIL + (A_ST - 1) * NLD;
-  constexpr int LOOP_WAIT = B_TAIL + (A_ST - 2) * NLD;
+  constexpr int DEEP_TAIL = A_ST == B_ST ? 0 : (A_ST > B_ST ? Cfg::A_LOADS : Cfg::B_LOADS);
+  constexpr int INIT_WAIT = DEEP_TAIL + (SHALLOW - 1) * NLD;
+  constexpr int LOOP_WAIT = DEEP_TAIL + (SHALLOW - 2) * NLD;
   static_assert(INIT_WAIT <= 63, "loads in flight must fit the vmcnt counter");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INIT_WAIT) : "memory");
   __syncthreads();
