@@ -17,10 +17,11 @@
 //    registers: 128 x 112 with 16x16x32 MFMAs, 128 x 128 with 32x32x16;
 //  - K slice of 64: one LDS row is 128 bytes (eight 16-byte chunks); tiles
 //    go HBM/L2 -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging);
-//    two LDS stages of A and two or three of B, the next slice's loads (and
-//    with three B stages the one after's B) in flight while the current one
-//    is multiplied -- the 256 x 224 tile's B gets the third stage (148 KiB in
-//    all), which gives a B line that misses L2 two slices to arrive;
+//    a ring of LDS stages per operand (Tile's A_ST, B_ST), the loads of the
+//    next slices in flight while the current one is multiplied: 256 x 224
+//    keeps two stages of A and three of B (148 KiB; a B line that misses L2
+//    has two slices to arrive), 128 x 128 three of each when one workgroup
+//    runs per CU, the others two of each;
 //  - LDS chunk swizzle: chunk c of row r sits at chunk position
 //    c ^ ((r >> 1) & 7); with it the ds_read_b128 patterns of both MFMA
 //    shapes (rows l % 16 or l % 32, chunks by lane group) are free of bank
@@ -376,10 +377,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, SUBS = Cfg::SUBS, DIM = MMA::DIM;
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
-  // byte offsets of A stage s and B stage s in the LDS array
   constexpr int A_ST = Cfg::A_ST, B_ST = Cfg::B_ST;
   // each slice's batch of loads starts with the shallower ring's
   constexpr bool A_FIRST = A_ST <= B_ST;
+  // byte offsets of A stage s and B stage s in the LDS array
   auto a_off = [](int s) { return s * Cfg::A_BYTES; };
   auto b_off = [](int s) { return A_ST * Cfg::A_BYTES + s * Cfg::B_BYTES; };
   // the array's 32-bit LDS address, for the M0 operand of the LDS-direct loads
