@@ -22,10 +22,13 @@
 //  - registers: the A fragments of two slices alternate; each B fragment is
 //    re-read for the next slice right after its last use in this one (so a
 //    wave fits in 256 VGPRs with no accumulation registers);
-//  - LDS: a 3-stage ring; a stage holds the A tile (256 rows x 128 bytes),
-//    the B tile (128 x 128 bytes), the slice's 256 A-row scales and the
-//    tile's B scale, all filled by LDS-direct loads (full 128-byte lines
-//    for A and B), two slices ahead of use;
+//  - LDS: a ring of A stages (the A tile, 256 rows x 128 bytes, and the
+//    slice's 256 A-row scales) and a ring of B stages (the B tile, 128 x 128
+//    bytes, and the tile's B scale), three of each (156 KiB), all filled by
+//    LDS-direct loads (full 128-byte lines for A and B), two slices ahead of
+//    use; every wave issues the same eight loads per slice in the same
+//    places, so one wait count serves all waves (measured with two A stages
+//    and three to five B stages: slower, A needs its depth here);
 //  - fragment reads: lane l of a 16x16x128 operand supplies row l % 16 and
 //    32 k-bytes; lane group g = l / 16 takes 16-byte chunks g and g + 4 of
 //    the 128-byte row (A and B use the same k assignment, so the sum is the
@@ -51,18 +54,25 @@ using tile::waitcnt_imm;
 constexpr int F_BM = 256, F_BN = 128, F_BK = 128;    // tile, k per slice (bytes)
 constexpr int F_WAVES = 8;                            // 4 along M x 2 along N
 constexpr int F_FM = 4, F_FN = 4;                     // 16x16 blocks per wave
-constexpr int F_STAGES = 3;
 constexpr int F_A_BYTES = F_BM * F_BK;                // 32 KiB
 constexpr int F_B_BYTES = F_BN * F_BK;                // 16 KiB
-constexpr int F_SA_OFF = F_A_BYTES + F_B_BYTES;       // 256 fp32 A scales
-constexpr int F_SB_OFF = F_SA_OFF + F_BM * 4;         // 4 waves x 64 lanes x 4 bytes
-constexpr int F_STAGE = F_SB_OFF + 4 * 256;           // 50176 bytes
+// An A stage holds the A codes, then a scale area of 8 waves x 256 bytes
+// whose first 1 KiB are the tile's 256 fp32 A-row scales (waves 0-3); a B
+// stage the B codes, then the same kind of area with the B scale at wave 4's
+// slot.  Each wave issues one scale load into each ring per slice (out of
+// range, i.e. zeros into its own unread slot, where it has nothing to load),
+// so every wave's batch has the same loads in the same places.
+constexpr int F_SCALES = F_WAVES * 256;               // scale area of a stage
+constexpr int F_ASTAGE = F_A_BYTES + F_SCALES;        // 34 KiB
+constexpr int F_BSTAGE = F_B_BYTES + F_SCALES;        // 18 KiB
 constexpr int F_A_LD = F_A_BYTES / 1024 / F_WAVES;    // 4 loads per wave
 constexpr int F_B_LD = F_B_BYTES / 1024 / F_WAVES;    // 2 loads per wave
-constexpr int F_NLD = F_A_LD + F_B_LD + 1;            // + a scale load
+constexpr int F_APART = 1 + F_A_LD;                   // A-ring loads per wave per slice
+constexpr int F_BPART = F_B_LD + 1;                   // B-ring loads per wave per slice
+constexpr int F_NLD = F_APART + F_BPART;
 constexpr int F_LAG = 2;                              // MFMAs between a block and its fold-in
 constexpr int F_NMMA = F_FM * F_FN;                   // MFMAs per wave per slice
-static_assert(F_STAGES * F_STAGE <= 160 * 1024, "LDS");
+constexpr int F_AS = 3, F_BS = 3;                     // stages of the A and B rings
 
 // Global -> LDS loads with a wave-uniform scalar offset: lane l reads
 // [voff + soff, + 16) (or + 4) of the buffer into LDS bytes [lds + 16 l, + 16)
@@ -85,11 +95,19 @@ __device__ __forceinline__ void load_lds4s(const i32x4& desc, uint32_t lds, uint
 }
 
 // One 256 x 128 output tile (tile row tm, tile column tn): the K loop and the
-// epilogue.
+// epilogue.  AS / BS: stages of the A ring (A codes + A scales) and of the B
+// ring (B codes + B scale); with S stages an operand's loads have S - 1
+// slices to arrive.
+template <int AS, int BS>
 __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn) {
-  __shared__ __attribute__((aligned(1024))) char lds[F_STAGES * F_STAGE];
+  static_assert(AS >= 2 && BS >= AS, "at least two stages, B at least as deep as A");
+  static_assert(AS * F_ASTAGE + BS * F_BSTAGE <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[AS * F_ASTAGE + BS * F_BSTAGE];
   const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+  // byte offsets of A stage s and B stage s
+  auto a_off = [](int st) { return st * F_ASTAGE; };
+  auto b_off = [](int st) { return AS * F_ASTAGE + st * F_BSTAGE; };
 
   const int64_t m0 = (int64_t)tm * F_BM, n0 = (int64_t)tn * F_BN;
   const int lane = threadIdx.x & 63;
@@ -114,9 +132,10 @@ __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn)
   // Loads of a slice (k0 bytes in): the tile's 8-row groups g = w + 8 q of A
   // (q < 4) and of B (q < 2), rows 8 g + (l >> 3), lane l fetching the chunk
   // that belongs at LDS position l & 7: logical chunk
-  // (l & 7) ^ (4 (g & 1) + (l >> 4)), and g & 1 = w & 1.  Then one 4-byte
-  // load: waves 0-3 the A-row scales of rows 64 w .., wave 4 the B scale
-  // (lane 0), waves 5-7 nothing (out of range).
+  // (l & 7) ^ (4 (g & 1) + (l >> 4)), and g & 1 = w & 1.  And two 4-byte
+  // scale loads: into the A stage, waves 0-3 the A-row scales of rows 64 w ..;
+  // into the B stage, wave 4 the B scale (lane 0); every other wave and
+  // lane reads out of range (zeros into its own unread slot).
   const uint32_t lrow = 8 * w + (lane >> 3);
   const uint32_t lchunk = (lane & 7) ^ (4 * (w & 1) + (lane >> 4));
   const uint32_t a_lane = lrow * lda + 16 * lchunk, b_lane = lrow * ldb + 16 * lchunk;
@@ -132,25 +151,30 @@ __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn)
   for (int i = 0; i < F_B_LD; ++i)
     bv[i] = (int)(lrow + 64 * i) < rows_b ? b_lane + 64 * i * ldb : kOutOfRange;
   const int sa_row = 64 * w + lane;
-  const uint32_t s_lane =
-      w < 4 ? (sa_row < rows_a ? (uint32_t)sa_row * (uint32_t)a.ssam * 4 : kOutOfRange)
-            : (w == 4 && lane == 0 ? 0u : kOutOfRange);
-  const i32x4 rs = w < 4 ? rsa : rsb;
-  const uint32_t s_lds = w < 4 ? F_SA_OFF + 256 * w : F_SB_OFF + 256 * (w - 4);
-  const uint32_t s_step = (uint32_t)(w < 4 ? a.ssak : a.ssbk) * 4;
-  // load q of slice kb into stage st; chunks past K and slices past the
-  // last scale block read zeros
-  auto load_one = [&](int q, int st, int kb) {
-    const uint32_t base = lds32 + st * F_STAGE;
-    const uint32_t k0 = (uint32_t)(kb * F_BK);
-    const bool kin = (int)k0 + 16 * (int)lchunk < K;
-    if (q < F_A_LD) {
-      load_lds16s(ra, base + (w + 8 * q) * 1024, kin ? av[q] : kOutOfRange, k0);
-    } else if (q < F_A_LD + F_B_LD) {
-      const int i = q - F_A_LD;
-      load_lds16s(rb, base + F_A_BYTES + (w + 8 * i) * 1024, kin ? bv[i] : kOutOfRange, k0);
+  const uint32_t sa_lane =
+      w < 4 && sa_row < rows_a ? (uint32_t)sa_row * (uint32_t)a.ssam * 4 : kOutOfRange;
+  const uint32_t sb_lane = w == 4 && lane == 0 ? 0u : kOutOfRange;
+  // Load q of a batch that fills A stage sa with slice kb_a and B stage sb
+  // with slice kb_b: the A-scale load, the A loads, the B loads, the
+  // B-scale load.  Chunks past K and slices past the last scale block read
+  // zeros.  (q is a compile-time index.)
+  auto load_one = [&](int q, int sa, int kb_a, int sb, int kb_b) {
+    if (q == 0) {
+      load_lds4s(rsa, lds32 + a_off(sa) + F_A_BYTES + 256 * w, kb_a < nkb ? sa_lane : kOutOfRange,
+                 (uint32_t)(kb_a * a.ssak) * 4);
+    } else if (q < F_APART) {
+      const uint32_t k0 = (uint32_t)(kb_a * F_BK);
+      const bool kin = (int)k0 + 16 * (int)lchunk < K;
+      load_lds16s(ra, lds32 + a_off(sa) + (w + 8 * (q - 1)) * 1024, kin ? av[q - 1] : kOutOfRange,
+                  k0);
+    } else if (q < F_APART + F_B_LD) {
+      const int i = q - F_APART;
+      const uint32_t k0 = (uint32_t)(kb_b * F_BK);
+      const bool kin = (int)k0 + 16 * (int)lchunk < K;
+      load_lds16s(rb, lds32 + b_off(sb) + (w + 8 * i) * 1024, kin ? bv[i] : kOutOfRange, k0);
     } else {
-      load_lds4s(rs, base + s_lds, kb < nkb ? s_lane : kOutOfRange, (uint32_t)kb * s_step);
+      load_lds4s(rsb, lds32 + b_off(sb) + F_B_BYTES + 256 * w, kb_b < nkb ? sb_lane : kOutOfRange,
+                 (uint32_t)(kb_b * a.ssbk) * 4);
     }
   };
 
@@ -158,8 +182,8 @@ __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn)
   // reads chunks g and g + 4 at positions chunk ^ ((l >> 1) & 7).
   const int sw = (lane >> 1) & 7, g = lane >> 4;
   const int rd0 = (lane & 15) * F_BK + ((g ^ sw) * 16), rd1 = (lane & 15) * F_BK + (((g + 4) ^ sw) * 16);
-  const int a_rd = 64 * wm * F_BK, b_rd = F_A_BYTES + 64 * wn * F_BK;
-  const int sa_rd = F_SA_OFF + (64 * wm + 4 * g) * 4;   // + 64 * i bytes for block i
+  const int a_rd = 64 * wm * F_BK, b_rd = 64 * wn * F_BK;
+  const int sa_rd = F_A_BYTES + (64 * wm + 4 * g) * 4;   // + 64 * i bytes for block i
 
   f32x4 acc[F_FM][F_FN];
 #pragma unroll
@@ -177,23 +201,24 @@ __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn)
     const i32x4 hi = *reinterpret_cast<const i32x4*>(p + rd1);
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  auto read_a = [&](int buf, int st, int i) { fa[buf][i] = rd32(lds + st * F_STAGE + a_rd + i * 16 * F_BK); };
-  auto read_b = [&](int st, int j) { fb[j] = rd32(lds + st * F_STAGE + b_rd + j * 16 * F_BK); };
-  auto read_s = [&](int st) {
-    const char* base = lds + st * F_STAGE;
+  auto read_a = [&](int buf, int st, int i) { fa[buf][i] = rd32(lds + a_off(st) + a_rd + i * 16 * F_BK); };
+  auto read_b = [&](int st, int j) { fb[j] = rd32(lds + b_off(st) + b_rd + j * 16 * F_BK); };
+  auto read_s = [&](int sta, int stb) {
+    const char* abase = lds + a_off(sta);
 #pragma unroll
-    for (int i = 0; i < F_FM; ++i) sa[i] = *reinterpret_cast<const f32x4*>(base + sa_rd + 64 * i);
-    sb = *reinterpret_cast<const float*>(base + F_SB_OFF);
+    for (int i = 0; i < F_FM; ++i) sa[i] = *reinterpret_cast<const f32x4*>(abase + sa_rd + 64 * i);
+    sb = *reinterpret_cast<const float*>(lds + b_off(stb) + F_B_BYTES + 256 * 4);
   };
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
   // One slice (A fragments in buffer cur; B fragments and scales of this
   // slice in fb / sa / sb): MFMA n covers block (i, j) = (n % F_FM, n / F_FM)
   // and the fold-in of MFMA n - F_LAG follows it.  Reads of the next slice
-  // (stage nst): B fragment j after its last use here, A fragments into
-  // buffer cur ^ 1 and the scales spread over the slice; the loads of
-  // slice kb_ld into stage ld_st are spread over the MFMAs.
-  auto slice = [&](int cur, int nst, int ld_st, int kb_ld) {
+  // (A stage nsa, B stage nsb): B fragment j after its last use here, A
+  // fragments into buffer cur ^ 1 and the scales spread over the slice; the
+  // batch of loads (A(kb_a) -> A stage ld_sa, B(kb_b) -> B stage ld_sb) is
+  // spread over the MFMAs.
+  auto slice = [&](int cur, int nsa, int nsb, int ld_sa, int kb_a, int ld_sb, int kb_b) {
     f32x4 p[F_LAG + 1];
     float s[F_FM][4];
 #pragma unroll
@@ -205,7 +230,7 @@ __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn)
       if (n < F_NMMA) {
         const int i = n % F_FM, j = n / F_FM;
         p[n % (F_LAG + 1)] = mfma16x16x128_e4m3(fa[cur][i], fb[j], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-        if (i == F_FM - 1) read_b(nst, j);
+        if (i == F_FM - 1) read_b(nsb, j);
       }
       if (n >= F_LAG) {
         const int m = n - F_LAG, i = m % F_FM, j = m / F_FM;
@@ -213,44 +238,59 @@ __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn)
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[i][j][v] += s[i][v] * pm[v];
       }
-      if (n == 1 || n == 5 || n == 9 || n == 13) read_a(cur ^ 1, nst, n / 4);
-      if (n == 10) read_s(nst);
+      if (n == 1 || n == 5 || n == 9 || n == 13) read_a(cur ^ 1, nsa, n / 4);
+      if (n == 10) read_s(nsa, nsb);
 #pragma unroll
       for (int q = 0; q < F_NLD; ++q)
-        if (q * F_NMMA / F_NLD == n) load_one(q, ld_st, kb_ld);
+        if (q * F_NMMA / F_NLD == n) load_one(q, ld_sa, kb_a, ld_sb, kb_b);
       fence();
     }
   };
 
-  // Pipeline over 128-wide slices kb (stage kb % 3): at the start of slice
-  // kb, wait for this wave's loads of slice kb + 1 (slice kb + 2's may stay
-  // in flight) and for all its reads (slice kb's fragments and scales are
-  // in registers), then barrier: slice kb + 1 is in LDS for every wave and
-  // no wave reads stage kb % 3 any more; the slice then reads slice kb + 1
-  // and loads slice kb + 3 into stage kb % 3.  Slices at or past K load out
-  // of range (zeros, no traffic).  A fragment buffers alternate per slice:
-  // two slices per trip (a slice past K adds zeros).
+  // Pipeline over 128-wide slices kb (A stage kb % AS, B stage kb % BS).
+  // Slice kb's batch loads A(kb + AS) into A stage kb % AS and B(kb + BS)
+  // into B stage kb % BS: slice kb's own fragments and scales were read
+  // during slice kb - 1, so at the barrier that opens slice kb nobody reads
+  // those stages any more.  At the start of slice kb, slice kb + 1 must have
+  // landed: A(kb + 1) heads batch kb + 1 - AS, and B(kb + 1) is in the same
+  // batch (after it) when BS == AS, else in an older one; what may stay in
+  // flight is what this wave issued after it: the B part of that batch when
+  // B is deeper, and the batches kb + 2 - AS .. kb - 1.  The prologue issues the
+  // batches before slice 0 (kb = -BS .. -1, the parts with a slice >= 0) the
+  // same way, then waits for slice 0 and reads it.  Slices at or past K load
+  // out of range (zeros, no traffic).  A fragment buffers alternate per
+  // slice: two slices per trip (a slice past K adds zeros).
 #pragma unroll
-  for (int q = 0; q < F_NLD; ++q) load_one(q, 0, 0);
+  for (int j = -BS; j < 0; ++j) {
 #pragma unroll
-  for (int q = 0; q < F_NLD; ++q) load_one(q, 1, 1);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(F_NLD) : "memory");
+    for (int q = 0; q < F_NLD; ++q)
+      if (q < F_APART ? j + AS >= 0 : j + BS >= 0)
+        load_one(q, j + AS >= 0 ? j + AS : 0, j + AS, j + BS >= 0 ? j + BS : 0, j + BS);
+  }
+  constexpr int B_TAIL = BS > AS ? F_BPART : 0;
+  // loads after A(0)'s part: the B part of its batch (when B is deeper) and
+  // AS - 1 full batches
+  constexpr int INIT_WAIT = B_TAIL + (AS - 1) * F_NLD, LOOP_WAIT = B_TAIL + (AS - 2) * F_NLD;
+  static_assert(INIT_WAIT <= 63, "loads in flight must fit the vmcnt counter");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INIT_WAIT) : "memory");
   asm volatile("s_barrier" ::: "memory");
 #pragma unroll
   for (int i = 0; i < F_FM; ++i) read_a(0, 0, i);
 #pragma unroll
   for (int j = 0; j < F_FN; ++j) read_b(0, j);
-  read_s(0);
-#pragma unroll
-  for (int q = 0; q < F_NLD; ++q) load_one(q, 2, 2);
+  read_s(0, 0);
+  int sta = 0, stb = 0;  // stages of slice kb
   for (int kb = 0; kb < nkb; kb += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = kb + h;
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(F_NLD, 0));
+      const int nsa = sta + 1 == AS ? 0 : sta + 1, nsb = stb + 1 == BS ? 0 : stb + 1;
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(LOOP_WAIT, 0));
       asm volatile("s_barrier" ::: "memory");
       fence();
-      slice(h, (k + 1) % F_STAGES, k % F_STAGES, k + 3);
+      slice(h, nsa, nsb, sta, k + AS, stb, k + BS);
+      sta = nsa;
+      stb = nsb;
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -273,7 +313,7 @@ __global__ __launch_bounds__(64 * F_WAVES) void gemm_fp8_tile(GemmArgs a, int ti
                                                                 int tiles_n) {
   int tm, tn;
   tile::tile_coords(tiles_m, tiles_n, 4, tm, tn);
-  fp8_tile_body(a, tm, tn);
+  fp8_tile_body<F_AS, F_BS>(a, tm, tn);
 }
 
 // Grouped products (see gemm_grouped.hip): the tile's group re-bases A and
@@ -288,7 +328,7 @@ __global__ __launch_bounds__(64 * F_WAVES) void gemm_fp8_grouped(GemmArgs a, Gro
   ag.B = static_cast<const uint8_t*>(a.B) + g * gt.sbg;
   ag.SB = a.SB + g * gt.ssbg;
   ag.C = static_cast<__bf16*>(a.C) + gt.row0[g] * a.scm;
-  fp8_tile_body(ag, tm, tn);
+  fp8_tile_body<F_AS, F_BS>(ag, tm, tn);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
