@@ -18,7 +18,8 @@
 //    16 x 16;
 //  - one v_mfma_scale_f32_16x16x128_f8f6f4 (unit block exponents) per
 //    block and slice, blocks taken column by column; the fold-in of a block
-//    runs two MFMAs after it;
+//    runs three MFMAs after it (measured: 532 us on 4096 x 7168 x 16384,
+//    against 537 with two, 545 with one and 534 with four);
 //  - registers: the A fragments of two slices alternate; each B fragment is
 //    re-read for the next slice right after its last use in this one (so a
 //    wave fits in 256 VGPRs with no accumulation registers);
@@ -70,7 +71,7 @@ constexpr int F_B_LD = F_B_BYTES / 1024 / F_WAVES;    // 2 loads per wave
 constexpr int F_APART = 1 + F_A_LD;                   // A-ring loads per wave per slice
 constexpr int F_BPART = F_B_LD + 1;                   // B-ring loads per wave per slice
 constexpr int F_NLD = F_APART + F_BPART;
-constexpr int F_LAG = 2;                              // MFMAs between a block and its fold-in
+constexpr int F_LAG = 3;                              // MFMAs between a block and its fold-in
 constexpr int F_NMMA = F_FM * F_FN;                   // MFMAs per wave per slice
 constexpr int F_AS = 3, F_BS = 3;                     // stages of the A and B rings
 
