@@ -4,7 +4,8 @@
 // (six-piece section).  Products with too few tiles to fill the CUs take
 // 128 x 128 tiles when K is short, and split K across the workgroups of a
 // tile (a one-GPU shard of that product, 4096 x 896 x 16384, has 64 tiles
-// of 256 x 224, each split 4 ways).
+// of 256 x 224, each split 4 ways).  Grids of one whole wave and a partial
+// one may split only the partial wave's tiles.
 #include "tile_mfma.hpp"
 
 namespace tg {
@@ -70,9 +71,43 @@ int splits_for(const GemmArgs& a) {
   return s < 2 ? 1 : (int)s;
 }
 
+// Grids of one whole wave of 256 x 224 tiles and a partial one: the split
+// of the partial wave's tiles over K that tile::tail_splits finds cheapest
+// (1: none).  256 x 256 grids run unsplit: their combine holds 256
+// accumulators per thread and spills, and splitting their partial waves
+// measured no faster.
+template <typename Cfg>
+int tail_for(const GemmArgs& a) {
+  if (!std::is_same<Cfg, Tile224>::value) return 1;
+  return tile::tail_splits(cdiv(a.M, Cfg::BM) * cdiv(a.N, Cfg::BN), cdiv(a.K, 64), kCus);
+}
+
 template <typename Cfg>
 hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
   const int tm = (int)cdiv(a.M, Cfg::BM), tn = (int)cdiv(a.N, Cfg::BN);
+  if constexpr (std::is_same<Cfg, Tile224>::value) {
+    const int splits = tail_for<Cfg>(a);
+    if (splits > 1) {
+      // scratch: one counter per split tile in the fixed counter area, then
+      // each split's fp32 partial tile
+      const int tiles = tm * tn, tail = tiles % (int)kCus, full = tiles - tail;
+      const size_t part_bytes = (size_t)Cfg::BM * Cfg::BN * 4 * splits * tail;
+      char* ws = static_cast<char*>(stream_workspace(s, kWorkspaceCounterBytes + part_bytes));
+      if (ws != nullptr) {
+        int* counters = reinterpret_cast<int*>(ws);
+        float* part = reinterpret_cast<float*>(ws + kWorkspaceCounterBytes);
+        const dim3 grid((unsigned)(full + tail * splits)), block(256);
+        if (op == Op::BF16)
+          hipLaunchKernelGGL((tile::gemm16_tile_tail<__bf16, Cfg>), grid, block, 0, s, a, tm, tn,
+                             full, splits, part, counters);
+        else
+          hipLaunchKernelGGL((tile::gemm16_tile_tail<_Float16, Cfg>), grid, block, 0, s, a, tm,
+                             tn, full, splits, part, counters);
+        return hipGetLastError();
+      }
+      // no scratch to be had (stream capture, allocation failure): unsplit
+    }
+  }
   const int splits = splits_for<Cfg>(a);
   if constexpr (std::is_same<Cfg, Tile224>::value || std::is_same<Cfg, Tile128>::value) {
    if (splits > 1) {
@@ -116,11 +151,15 @@ hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
 // (4096 x 1792 x 4096: 50.4 us against 57.1 with three).  With longer K the larger tile's
 // lower bytes per FLOP win (4096 x 896 x 16384, 2048 x 1024 x 16384), and so
 // does 256 x 224 with split K.  Other grids run in ceil(tiles / 256) waves
-// over the 256 CUs, each wave costing about one tile's MFMA work: the shape
-// with the smaller waves x tile area (4096 x 7168: 256 x 224 gives 512 tiles
-// = 2 full waves, 256 x 256 gives 448 tiles = 1.75 waves rounded up to 2).
-int64_t cost(const GemmArgs& a, int64_t bm, int64_t bn) {
-  return cdiv(cdiv(a.M, bm) * cdiv(a.N, bn), kCus) * bm * bn;
+// over the 256 CUs, each wave costing about one tile's MFMA work (with
+// 256 x 224, a partial second wave may have its tiles split over K:
+// tail_for).  The shape with the smaller waves x tile area wins, 256 x 256
+// on ties (4096 x 7168: 256 x 224 gives 512 tiles = 2 full waves, 256 x 256
+// gives 448 tiles = 1.75 waves rounded up to 2).
+double cost(const GemmArgs& a, int64_t bm, int64_t bn) {
+  const int64_t tiles = cdiv(a.M, bm) * cdiv(a.N, bn), nk = cdiv(a.K, 64);
+  const int s = bn == 224 ? tile::tail_splits(tiles, nk, kCus) : 1;
+  return tile::tail_waves(tiles, nk, kCus, s) * double(bm * bn);
 }
 enum class Shape { T128, T128x2, T224, T256 };
 Shape shape_of(const GemmArgs& a) {
@@ -149,11 +188,19 @@ const char* const kNames128[] = {"tile_nt_128x128", "tile_nt_128x128", "tile_nt_
                                  "tile_nt_128x128_splitk3", "tile_nt_128x128_splitk4",
                                  "tile_nt_128x128_splitk5", "tile_nt_128x128_splitk6",
                                  "tile_nt_128x128_splitk7", "tile_nt_128x128_splitk8"};
+// ... and by the split count of the tiles of a partial last wave (2 .. 8)
+const char* const kTails224[] = {"", "", "tile_nt_256x224_tail2", "tile_nt_256x224_tail3",
+                                 "tile_nt_256x224_tail4", "tile_nt_256x224_tail5",
+                                 "tile_nt_256x224_tail6", "tile_nt_256x224_tail7",
+                                 "tile_nt_256x224_tail8"};
 const char* name_of(const GemmArgs& a) {
   switch (shape_of(a)) {
     case Shape::T128: return kNames128[splits_for<Tile128>(a)];
     case Shape::T128x2: return "tile_nt_128x128_2stage";
-    case Shape::T224: return kNames224[splits_for<Tile224>(a)];
+    case Shape::T224: {
+      const int t = tail_for<Tile224>(a);
+      return t > 1 ? kTails224[t] : kNames224[splits_for<Tile224>(a)];
+    }
     default: return "tile_nt_256x256";
   }
 }

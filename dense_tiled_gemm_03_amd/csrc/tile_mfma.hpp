@@ -167,6 +167,29 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm_siz
   tile_of(xcd_id(), tiles_m, tiles_n, gm_size, tm, tn);
 }
 
+// Grids with a partial last wave: workgroups for `full` whole tiles, then
+// split units (each one split of a tile past the whole ones).  Workgroup b
+// of G runs on XCD b % 8 as the b / 8-th of that XCD; every XCD takes its
+// share of the whole tiles first and its share of the split units after
+// them, so the split units fill the last wave on every XCD.  Ids stay
+// contiguous per XCD.  Returns true and the tile id for a whole tile, false
+// and the unit's index for a split unit.  (Each XCD's workgroup count is at
+// least its share of whole tiles: G >= full.)
+__host__ __device__ inline bool tail_unit(int b, int G, int full, int& id) {
+  const int x = b % kXcds, l = b / kXcds;
+  const int per = G / kXcds, rem = G % kXcds;
+  const int fper = full / kXcds, frem = full % kXcds;
+  const int fx = fper + (x < frem ? 1 : 0);                // whole tiles on XCD x
+  const int before_f = x * fper + (x < frem ? x : frem);   // ... on the XCDs before x
+  if (l < fx) {
+    id = before_f + l;
+    return true;
+  }
+  const int before = x * per + (x < rem ? x : rem);        // workgroups on the XCDs before x
+  id = (before - before_f) + (l - fx);
+  return false;
+}
+
 // Split of K across the workgroups of one tile: this workgroup's split of
 // `splits`, the tile's id, and the scratch that combines the partial tiles
 // (per-tile counters, fp32 partial tiles).  splits == 1: no split.
@@ -294,6 +317,41 @@ __device__ __forceinline__ void group_coords(const GroupTable& gt, int bm, int g
 // Split K: at most this many workgroups share one output tile.
 constexpr int kMaxSplits = 8;
 
+// Time, in waves of whole tiles over `cus` CUs, of a grid of `tiles` tiles
+// of nk K slices each whose tiles past the first wave are split s ways
+// (s = 1: no split): one wave, then ceil(tail * s / cus) waves of 1/s of a
+// tile, plus the combine, which costs about two K slices per split past
+// the first (the last split of a tile reads the others' partials).
+inline double tail_waves(int64_t tiles, int64_t nk, int64_t cus, int s) {
+  const int64_t whole = tiles / cus, tail = tiles % cus;
+  if (s == 1 || tail == 0) return double((tiles + cus - 1) / cus);
+  return double(whole) + double((tail * s + cus - 1) / cus) / s + 2.0 * (s - 1) / double(nk);
+}
+
+// Split count for the tiles past the first wave of a grid of more than one
+// and less than two waves: the cheapest by tail_waves (the smallest on
+// ties, 1 when nothing beats the unsplit grid) among those that leave every
+// split at least 8 K slices.  Larger grids run unsplit: the chip is
+// power-limited, so a partial last wave runs at a higher clock than a full
+// one and loses less than its idle CUs suggest, and measured splits of the
+// last of two or three waves gained nothing (4096 x 7168 x 16384 in
+// 256 x 256 tiles, 6144 x 6144 x 4096), while one wave and a tail gained
+// about 10% (4352 x 4096 x 4096: 158 us unsplit, 142 us with the 67 tiles
+// past the first wave split 2 ways).
+inline int tail_splits(int64_t tiles, int64_t nk, int64_t cus) {
+  if (tiles <= cus || tiles >= 2 * cus) return 1;
+  int best = 1;
+  double best_w = tail_waves(tiles, nk, cus, 1);
+  for (int s = 2; s <= kMaxSplits && nk / s >= 8; ++s) {
+    const double w = tail_waves(tiles, nk, cus, s);
+    if (w < best_w) {
+      best = s;
+      best_w = w;
+    }
+  }
+  return best;
+}
+
 // Float4s of a split's partial that one part of the combine loads per other
 // split: the largest divisor of nq with at most `budget` float4s in flight
 // per part across the S - 1 other splits.
@@ -364,6 +422,14 @@ __device__ __forceinline__ void sum_splits(Acc (&acc)[FM][FN], __amdgpu_buffer_r
   }
 }
 
+// The LDS array of the tile stages: one per size, so that the bodies of one
+// tile shape inlined into one kernel (whole and split tiles) share it.
+template <int BYTES>
+__device__ __forceinline__ char* tile_lds() {
+  __shared__ __attribute__((aligned(1024))) char lds[BYTES];
+  return lds;
+}
+
 // One output tile (tile row tm, tile column tn) of C = A * B: the K loop
 // and the epilogue.  BKN = false: B stored N x K (sbk = 1); true: B stored
 // K x N (sbn = 1).
@@ -376,7 +442,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   typedef typename MMA::Acc Acc;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, SUBS = Cfg::SUBS, DIM = MMA::DIM;
-  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  char* const lds = tile_lds<Cfg::LDS_BYTES>();
   constexpr int A_ST = Cfg::A_ST, B_ST = Cfg::B_ST;
   // each slice's batch of loads starts with the shallower ring's
   constexpr bool A_FIRST = A_ST <= B_ST;
@@ -738,6 +804,25 @@ __global__ __launch_bounds__(256) void gemm16_tile_splitk(GemmArgs a, int tiles_
   int tm, tn;
   tile_of(tile, tiles_m, tiles_n, Cfg::GM, tm, tn);
   tile_body<T, Cfg, false, true>(a, tm, tn, SplitK{splits, id % splits, tile, part, counters});
+}
+
+// Grids of one whole wave and a partial one: `full` whole tiles, then the
+// remaining tiles split `splits` ways over K (workgroup order as in
+// tail_unit), combined through scratch as in gemm16_tile_splitk (the partials
+// and counters are indexed by the tile's place among the split ones).
+template <typename T, typename Cfg>
+__global__ __launch_bounds__(256) void gemm16_tile_tail(GemmArgs a, int tiles_m, int tiles_n,
+                                                        int full, int splits, float* part,
+                                                        int* counters) {
+  int id;
+  const bool whole = tail_unit(blockIdx.x, gridDim.x, full, id);
+  int tm, tn;
+  tile_of(whole ? id : full + id / splits, tiles_m, tiles_n, Cfg::GM, tm, tn);
+  if (whole)
+    tile_body<T, Cfg, false>(a, tm, tn);
+  else
+    tile_body<T, Cfg, false, true>(a, tm, tn,
+                                   SplitK{splits, id % splits, id / splits, part, counters});
 }
 
 }  // namespace tile

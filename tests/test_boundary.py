@@ -211,6 +211,11 @@ def test_grouped_noop_and_plans(lib):
     assert _grouped(lib, "plan", G=129, off=list(range(0, 130 * 2, 2))) == "per_group"
     assert _grouped(lib, "plan", off=[0, 2048, 4096], N=4096, ldc=4096,
                     sbg=4096 * 128) == "grouped_tile_nt_256x256"
+    # 8192 rows in 8 uneven groups x 4096 x 7168: 684 tiles of 256 x 224
+    # (3 waves) against 576 of 256 x 256 (also 3)
+    off = [0, 1246, 2575, 3497, 4713, 5522, 6122, 6748, 8192]
+    assert _grouped(lib, "plan", G=8, off=off, N=4096, K=7168, lda=7168, ldb=7168,
+                    sbg=4096 * 7168, ldc=4096) == "grouped_tile_nt_256x224"
 
 
 def _grouped8(lib, plan=False, **kw):
@@ -293,6 +298,13 @@ SWEEP_PLANS = [
     (4096, 4096, 1024, "tile_nt_256x256"),
     (4096, 1792, 4096, "tile_nt_128x128_2stage"),
     (4096, 1024, 4096, "tile_nt_128x128"),
+    # one whole wave and a partial one: the partial wave's tiles split over K
+    (4352, 4096, 1024, "tile_nt_256x224_tail2"),
+    (4400, 4000, 2056, "tile_nt_256x224_tail3"),
+    (4300, 4000, 4104, "tile_nt_256x224_tail5"),
+    (4352, 4096, 4096, "tile_nt_256x224_tail3"),
+    (4352, 4096, 448, "tile_nt_256x224"),      # K too short to split
+    (6144, 6144, 2048, "tile_nt_256x224"),     # three waves: unsplit
 ]
 
 

@@ -75,6 +75,9 @@ CASES = [
     ([0, 100, 100, 357, 600, 601], 250, 64),       # an empty group, tiny and ragged groups
     ([0, 256, 512, 768], 224, 72),                 # tile-aligned groups
     ([0, 37, 400, 401, 1100], 129, 1000),          # ragged everything
+    # more than one wave of tiles (330 and 385 of 256 x 224)
+    ([0, 5000, 9000, 16700], 1024, 1032),
+    ([0, 3000, 3001, 9000, 16700], 1000, 2056),
 ]
 
 
@@ -109,13 +112,15 @@ def test_grouped_per_group_path():
 
 
 def test_grouped_workload_sampled():
-    """The benchmark's 8-expert product at full size, on 256 seeded rows:
-    within the bound on N(0,1)/sqrt(K) inputs, bit-exact on integers."""
+    """The benchmark's 8-expert product at full size, on 256 seeded rows and
+    rows of the last group: within the bound on N(0,1)/sqrt(K) inputs,
+    bit-exact on integers."""
     w = configs.GROUPED
     sizes = configs.group_sizes(w["rows"], w["G"], w["seed"])
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     N, K = w["N"], w["K"]
-    rows = gen.sample_rows(w["rows"], 256, w["seed"])
+    rows = np.union1d(gen.sample_rows(w["rows"], 256, w["seed"]),
+                      np.arange(offsets[-2], offsets[-1], 29))
     A, B = _inputs("bf16", w["rows"], w["G"], N, K, w["seed"])
     c, plan = _run("bf16", offsets, N, K, A, B, K, K)
     assert plan == "grouped_tile_nt_256x224", plan

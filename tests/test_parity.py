@@ -299,14 +299,16 @@ SPLITK_CASES = [
 ]
 
 
-def _check16_rows(fmt, M, N, K, seed, int_r=None):
-    """B stored N x K; the GPU result on sampled rows (and the last row)."""
+def _check16_rows(fmt, M, N, K, seed, int_r=None, extra_rows=()):
+    """B stored N x K; the GPU result on sampled rows (and the last row, and
+    `extra_rows`)."""
     draw = (lambda shape, st: gen.integers(shape, seed, st, int_r, fmt)) if int_r \
         else (lambda shape, st: gen.normal(shape, seed, st, fmt))
     A, B = draw((M, K), 0), draw((N, K), 1)
     H.log(f"gemm {fmt} M={M} N={N} K={K} rows int_r={int_r}")
     c, plan = H.run16(fmt, M, N, K, H.dev(A), K, 1, H.dev(B), 1, K)
-    rows = np.union1d(gen.sample_rows(M, 48, seed), [M - 1])
+    rows = np.union1d(np.union1d(gen.sample_rows(M, 48, seed), [M - 1]),
+                      np.asarray(extra_rows, dtype=np.int64))
     C_ref, S = oracle.gemm(fmt, M, N, K, A, K, 1, B, 1, K, rows=rows)
     what = f"{fmt} {M}x{N}x{K} rows [{plan}]"
     if int_r:
@@ -325,6 +327,39 @@ def test_tile_nt_split_k(fmt, case):
     r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
     plan = _check16_rows(fmt, M, N, K, seed=1600 + M + N + K, int_r=r)
     assert plan == want, plan
+
+
+# (M, N, K, expected plan): grids of one whole wave (256 workgroups) of
+# 256 x 224 tiles and a partial one split the partial wave's tiles over K --
+# whole tiles and split tiles in one launch; ragged M, N and K; 2 and 3
+# splits.  Checked in full.
+TAIL_CASES = [
+    (4352, 4096, 1024, "tile_nt_256x224_tail2"),
+    (4400, 4000, 2056, "tile_nt_256x224_tail3"),
+]
+
+
+@pytest.mark.parametrize("case", TAIL_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in TAIL_CASES])
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_tile_nt_tail(fmt, case):
+    M, N, K, want = case
+    plan = _check16(fmt, M, N, K, "nk", seed=1900 + M + N + K)
+    assert plan == want, plan
+    r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
+    plan = _check16(fmt, M, N, K, "nk", seed=2000 + M + N + K, int_r=r)
+    assert plan == want, plan
+
+
+def test_tile_nt_tail5_rows():
+    """4300 x 4000 x 4104: 306 tiles of 256 x 224, the last 50 (tile rows 12
+    to 16) split 5 ways; sampled rows plus rows of every split tile row,
+    bound and bit-exact."""
+    M, N, K = 4300, 4000, 4104
+    extra = list(range(3072, M, 37))
+    plan = _check16_rows("bf16", M, N, K, seed=2101, extra_rows=extra)
+    assert plan == "tile_nt_256x224_tail5", plan
+    plan = _check16_rows("bf16", M, N, K, seed=2102, int_r=63, extra_rows=extra)
+    assert plan == "tile_nt_256x224_tail5", plan
 
 
 # (M, N, K, expected plan): small grids with K of at most 128 slices take
