@@ -25,16 +25,19 @@
  *    is rounded once to the output type, round-to-nearest-even.
  *  - A, B, C (and scales) are DEVICE pointers owned by the caller; they must
  *    stay valid until the work enqueued on `stream` has completed.
- *  - Scratch: products with M <= 64, and products whose output tiles would
- *    fill fewer than half the CUs, split K across workgroups and combine the
+ *  - Scratch: products with M <= 64, products whose output tiles would fill
+ *    fewer than half the CUs, and products of one whole wave of 256 x 224
+ *    tiles plus a partial one (the partial wave's tiles) split K across
+ *    workgroups and combine the
  *    partial results through a device buffer the library owns, one per
  *    (device, stream), allocated on the first such call on that stream,
  *    grown (at least doubling) when a later call needs more, and kept until
  *    the process ends -- an outgrown buffer is not freed either, since a
  *    graph captured earlier may still use it: a fixed 16 KiB area of
  *    completion counters,
- *    then the fp32 partial tiles -- about 32 KiB per 64 x 128 block of C per
- *    K split (7.3 MiB for 64 x 7168 x 7168).  Such a call made while the
+ *    then the fp32 partial tiles -- 4 bytes per element of C per K split of
+ *    each split tile (7.3 MiB for 64 x 7168 x 7168, 44 MiB for 4352 x 4096
+ *    x 4096).  Such a call made while the
  *    stream is being captured into a graph, or when the buffer cannot be had,
  *    runs without splitting K instead.  No other call allocates.
  *  - Calls are asynchronous: they enqueue on `stream` (a hipStream_t; NULL is
