@@ -417,6 +417,36 @@ def test_split_k_shard_shape():
 
 
 
+def test_tail_after_split_k_and_repeatable():
+    """The partial-wave split shares the stream's scratch with split K: the
+    4096 x 896 x 16384 shard (64 tiles split 4 ways) and then 4352 x 4096 x
+    4096 (67 tiles past the first wave split 3 ways) on one stream, integer
+    inputs bit-exact on sampled rows and rows of the split tiles; normal
+    inputs bit-identical over two runs on two streams."""
+    M, N, K = 4352, 4096, 4096
+    rows = np.union1d(gen.sample_rows(M, 64, 7), np.arange(3072, M, 53))
+    ws = configs.Workload("shard", "bf16", 4096, 896, 16384, "nk", "integers", 3, 0)
+    wt = configs.Workload("tail", "bf16", M, N, K, "nk", "normal_sqrtk", 8, 0)
+    ds = configs.make_inputs(ws, int_r=16)
+    dt = configs.make_inputs(wt, int_r=32)
+    H.log("split-K shard then partial-wave split, one stream")
+    _, plan = H.run16("bf16", 4096, 896, 16384, H.dev(ds["A"]), 16384, 1, H.dev(ds["B"]), 1,
+                      16384)
+    assert plan == "tile_nt_256x224_splitk4", plan
+    c, plan = H.run16("bf16", M, N, K, H.dev(dt["A"]), K, 1, H.dev(dt["B"]), 1, K)
+    assert plan == "tile_nt_256x224_tail3", plan
+    C_ref, _ = oracle.gemm("bf16", M, N, K, dt["A"], K, 1, dt["B"], 1, K, rows=rows)
+    H.assert_bit_exact("bf16", c[rows], C_ref, f"tail after split K [{plan}]")
+    dn = configs.make_inputs(wt)
+    A, B = H.dev(dn["A"]), H.dev(dn["B"])
+    c1, _ = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c2, _ = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(c1, c2)
+
+
 def test_split_k_scratch_reused_by_more_tiles():
     """Two split-K products in a row on one stream: 64 tiles of 256 x 224
     split 4 ways (large partials, few counters), then 80 tiles split 3 ways,
