@@ -12,7 +12,9 @@ torch / numpy dtype conversions (tests/test_codecs.py); the fp8 block
 quantiser against torch's e4m3fn cast, numpy's fp32 division, the block
 invariants of its definition and the input generator's own quantiser; the
 product with fp8 output against an identity product and numpy's integer
-matmul.
+matmul; the acceptance bound against its stated constants, the unit
+roundoffs of torch's format descriptions and an fp32-accumulating model of
+the GPU arithmetic.
 """
 from __future__ import annotations
 
@@ -56,6 +58,8 @@ class Oracle:
         lib.tg_oracle_decode.restype = None
         lib.tg_oracle_quant_fp8.argtypes = [i64, i64, vp, i64, i64, vp, i64, vp, i64, i64]
         lib.tg_oracle_quant_fp8.restype = c_int
+        lib.tg_oracle_bound.argtypes = [c_int, vp, i64, vp]
+        lib.tg_oracle_bound.restype = None
         lib.tg_oracle_init()
         self.lib = lib
 
@@ -127,6 +131,14 @@ class Oracle:
         self.lib.tg_oracle_round(FMT[fmt], _p(x), x.size, _p(out))
         return out
 
+    def bound(self, fmt_out: str, S: np.ndarray) -> np.ndarray:
+        """Per-element acceptance bound on |C_gpu - C_ref| (see oracle.c):
+        four unit roundoffs of the output format times S = sum_k |a||b|."""
+        S = np.ascontiguousarray(S, dtype=np.float64)
+        out = np.empty(S.shape, np.float64)
+        self.lib.tg_oracle_bound(FMT[fmt_out], _p(S), S.size, _p(out))
+        return out
+
     def decode(self, fmt: str, codes: np.ndarray) -> np.ndarray:
         """Exact fp64 values of fp16 / bf16 / e4m3fn codes."""
         dt = np.uint8 if fmt == "e4m3fn" else np.uint16
@@ -185,4 +197,4 @@ def decode(fmt, codes):
 
 def bound(fmt_out: str, S: np.ndarray) -> np.ndarray:
     """Per-element tolerance: 4*2^-8*S for bf16 output, 4*2^-11*S for fp16."""
-    return (4.0 * 2.0 ** -8 if fmt_out == "bf16" else 4.0 * 2.0 ** -11) * S
+    return default().bound(fmt_out, S)

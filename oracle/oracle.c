@@ -303,3 +303,17 @@ void tg_oracle_round(int fmt, const double* x, int64_t n, uint16_t* out) {
       out[t] = encode_exact(round_to_format(x[t], 8, -126, ldexp(255.0, 120)), 8, 7);
   }
 }
+
+/* ---- the acceptance bound -------------------------------------------------
+ * Per-element tolerance on |C_gpu - C_ref| for a product accumulated in fp32
+ * and rounded once to the output format: four unit roundoffs of the output
+ * format times S = sum_k |a||b|.  A binary format with p significant bits
+ * (the implicit one included) has unit roundoff 2^-p: bf16 has p = 8, fp16
+ * p = 11, so the tolerance is 4 * 2^-8 * S and 4 * 2^-11 * S.  It covers the
+ * output rounding (at most 2^-p |C| <= 2^-p S) plus fp32 summation in any
+ * order (at most about K * 2^-24 * S, 2^-10 S at K = 16384) with room left;
+ * S = 0 gives 0, so an all-zero sum must come out exactly zero. */
+void tg_oracle_bound(int fmt, const double* S, int64_t n, double* out) {
+  const int p = fmt == FMT_F16 ? 11 : 8;
+  for (int64_t t = 0; t < n; ++t) out[t] = ldexp(4.0, -p) * S[t];
+}

@@ -471,9 +471,60 @@ def pin_gemm_quant_integers(orc):
             assert np.array_equal(Q[i, j * 128:(j + 1) * 128], want), (i, j)
 
 
+# ---------------------------------------------------------- acceptance bound
+
+def pin_bound_constants(orc):
+    """The tolerance is 4 * 2^-8 * S for bf16 output and 4 * 2^-11 * S for
+    fp16 output (the constants written out here), i.e. four unit roundoffs of
+    the output format, the unit roundoff being half the format's epsilon as
+    torch describes it; S = 0 gives a zero tolerance."""
+    rng = np.random.default_rng(21)
+    S = np.concatenate([[0.0, 1.0, 3.0, 1e-30, 1e30], rng.exponential(5.0, 1000)])
+    for fmt, const, dtype in (("bf16", 4.0 * 2.0 ** -8, torch.bfloat16),
+                              ("f16", 4.0 * 2.0 ** -11, torch.float16)):
+        got = orc.bound(fmt, S)
+        assert np.array_equal(got, const * S), f"bound constant {fmt}"
+        unit = torch.finfo(dtype).eps / 2.0
+        assert np.array_equal(got, 4.0 * unit * S), f"bound vs unit roundoff {fmt}"
+        assert got[0] == 0.0
+
+
+def _fp32_sequential(a: np.ndarray, b: np.ndarray, order) -> np.ndarray:
+    """sum_k a[i,k] b[k,j] accumulated in fp32 (products exact for 16-bit
+    inputs) in the given k order: a model of the GPU's accumulation."""
+    acc = np.zeros((a.shape[0], b.shape[1]), np.float32)
+    for k in order:
+        acc = (acc + np.outer(a[:, k], b[k, :]).astype(np.float32)).astype(np.float32)
+    return acc
+
+
+def pin_bound_model(orc):
+    """An fp32-accumulating product rounded once to the output format stays
+    within the tolerance (in ascending, descending and shuffled k order, at
+    K = 16384 and on cancelling sums), while a result off by 2^-5 * S does
+    not: the bound admits the arithmetic the method allows and no more."""
+    rng = np.random.default_rng(22)
+    for fmt in ("bf16", "f16"):
+        for K in (16384, 1000):
+            M, N = 3, 4
+            a = lib_decode(fmt, lib_encode(fmt, rng.standard_normal((M, K)) / np.sqrt(K)))
+            b = lib_decode(fmt, lib_encode(fmt, rng.standard_normal((K, N))))
+            a[0, :] = np.abs(a[0, :])                 # a row of same-sign terms
+            c_ref = a @ b
+            S = np.abs(a) @ np.abs(b)
+            tol = orc.bound(fmt, S)
+            for order in (range(K), range(K - 1, -1, -1), rng.permutation(K)):
+                c32 = _fp32_sequential(a, b, order).astype(np.float64)
+                got = lib_decode(fmt, lib_encode(fmt, c32 if fmt == "f16" else
+                                                 c32.astype(np.float32)))
+                assert np.all(np.abs(got - c_ref) <= tol), f"model outside bound {fmt} K={K}"
+            assert np.all(2.0 ** -5 * S > tol), f"bound too loose {fmt}"
+
+
 ALL_PINS = [pin_identity, pin_selection, pin_rank1, pin_all_ones, pin_bruteforce_integers,
             pin_bruteforce_rationals, pin_numpy_matmul, pin_layout_invariance, pin_row_subset,
             pin_nonnegative_s_equals_c, pin_fp8_unit_codes, pin_fp8_bruteforce,
             pin_fp8_layout_and_rows, pin_decoders, pin_rounding, pin_quant_codes_match_torch,
             pin_quant_scales_and_bounds, pin_quant_edge_blocks, pin_quant_block_relation,
-            pin_quant_matches_generator, pin_gemm_quant_identity, pin_gemm_quant_integers]
+            pin_quant_matches_generator, pin_gemm_quant_identity, pin_gemm_quant_integers,
+            pin_bound_constants, pin_bound_model]

@@ -44,6 +44,10 @@ MUTATIONS = [
      "return (uint8_t)lo;"),
     ("quantiser amax of the first column only", "for (int64_t k = k0; k < k1; ++k) {\n          float a",
      "for (int64_t k = k0; k < k0 + 1; ++k) {\n          float a"),
+    ("bound constants of bf16 and fp16 swapped", "const int p = fmt == FMT_F16 ? 11 : 8;",
+     "const int p = fmt == FMT_F16 ? 8 : 11;"),
+    ("bound of eight unit roundoffs", "ldexp(4.0, -p) * S[t]", "ldexp(8.0, -p) * S[t]"),
+    ("bound of one unit roundoff", "ldexp(4.0, -p) * S[t]", "ldexp(1.0, -p) * S[t]"),
 ]
 
 
