@@ -21,7 +21,8 @@ EXPORTS = ("tg_status_string", "tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8_block
            "tg_gemm_plan", "tg_quant_fp8_1x128", "tg_quant_fp8_128x128", "tg_gemm_grouped_f16",
            "tg_gemm_grouped_bf16", "tg_gemm_grouped_plan", "tg_gemm_grouped_fp8_blockscaled",
            "tg_gemm_grouped_fp8_plan", "tg_gemm_f16_quant_fp8", "tg_gemm_bf16_quant_fp8",
-           "tg_gemm_quant_fp8_plan")
+           "tg_gemm_quant_fp8_plan", "tg_gemm_f16_ws", "tg_gemm_bf16_ws", "tg_gemm_workspace_size",
+           "tg_gemm_plan_ws")
 
 
 class TgError(RuntimeError):
@@ -54,6 +55,16 @@ def load():
     lib.tg_gemm_fp8_blockscaled.restype = c_int
     lib.tg_gemm_plan.argtypes = [c_int, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64]
     lib.tg_gemm_plan.restype = ctypes.c_char_p
+    sz = ctypes.c_size_t
+    for name in ("tg_gemm_f16_ws", "tg_gemm_bf16_ws"):
+        getattr(lib, name).argtypes = sig16[:-1] + [vp, sz, vp]
+        getattr(lib, name).restype = c_int
+    lib.tg_gemm_workspace_size.argtypes = [c_int, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp,
+                                           i64, i64, ctypes.POINTER(sz)]
+    lib.tg_gemm_workspace_size.restype = c_int
+    lib.tg_gemm_plan_ws.argtypes = [c_int, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64,
+                                    sz]
+    lib.tg_gemm_plan_ws.restype = ctypes.c_char_p
     sigg = [i64, vp, i64, i64, vp, i64, vp, i64, i64, vp, i64]
     for name in ("tg_gemm_grouped_f16", "tg_gemm_grouped_bf16"):
         getattr(lib, name).argtypes = sigg + [vp]
@@ -102,6 +113,32 @@ def tg_gemm_f16(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, stream=0):
 
 def tg_gemm_bf16(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, stream=0):
     return _check(load().tg_gemm_bf16(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, stream))
+
+
+def tg_gemm_f16_ws(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, workspace, workspace_bytes,
+                   stream=0):
+    return _check(load().tg_gemm_f16_ws(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, workspace,
+                                        workspace_bytes, stream))
+
+
+def tg_gemm_bf16_ws(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, workspace, workspace_bytes,
+                    stream=0):
+    return _check(load().tg_gemm_bf16_ws(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn,
+                                         workspace, workspace_bytes, stream))
+
+
+def tg_gemm_workspace_size(op, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn):
+    """Workspace bytes of the call's split plan (0: none)."""
+    out = ctypes.c_size_t(0)
+    _check(load().tg_gemm_workspace_size(op, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn,
+                                         ctypes.byref(out)))
+    return out.value
+
+
+def tg_gemm_plan_ws(op, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, workspace_bytes):
+    r = load().tg_gemm_plan_ws(op, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn,
+                               workspace_bytes)
+    return None if r is None else r.decode()
 
 
 def tg_gemm_fp8_blockscaled(M, N, K, A, sam, sak, SA, ssam, ssak, B, sbk, sbn, SB, ssbn, ssbk,

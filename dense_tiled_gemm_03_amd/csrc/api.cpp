@@ -84,13 +84,21 @@ const Variant* select(const Call& c) {
   return nullptr;  // unreachable: the generic kernels accept every call
 }
 
-tg_status run(const Call& c, tg_stream_t stream) {
+// A caller's workspace: none (bytes == 0), or a 256-byte aligned device
+// buffer.  TG_SUCCESS when usable.
+tg_status check_workspace(const void* ws, size_t bytes) {
+  if (bytes == 0) return TG_SUCCESS;
+  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) return TG_ERR_INVALID_VALUE;
+  return TG_SUCCESS;
+}
+
+tg_status run(const Call& c, const Scratch& ws, tg_stream_t stream) {
   tg_status st = validate(c);
   if (st != TG_SUCCESS) return st;
   if (c.a.M == 0 || c.a.N == 0) return TG_SUCCESS;
   const Variant* v = select(c);
   if (v == nullptr) return TG_ERR_UNSUPPORTED;
-  hipError_t e = v->launch(c.op, c.a, static_cast<hipStream_t>(stream));
+  hipError_t e = v->launch(c.op, c.a, ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TG_SUCCESS : TG_ERR_LAUNCH;
 }
 
@@ -101,6 +109,22 @@ Call make16(Op op, int64_t M, int64_t N, int64_t K, const void* A, int64_t sam, 
   c.a = GemmArgs{M, N, K, A, sam, sak, B, sbk, sbn, nullptr, 0, 0, nullptr, 0, 0, C, scm};
   c.scn = scn;
   return c;
+}
+
+// The call tg_gemm_plan / tg_gemm_workspace_size describe (op 0..2); false
+// for an unknown op.
+bool describe(int op, int64_t M, int64_t N, int64_t K, const void* A, int64_t sam, int64_t sak,
+              const void* B, int64_t sbk, int64_t sbn, void* C, int64_t scm, int64_t scn,
+              Call& c) {
+  if (op < 0 || op > 2) return false;
+  c = make16(static_cast<Op>(op), M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn);
+  if (c.op == Op::FP8) {
+    // scale pointers do not affect the choice; stand-ins pass the null checks
+    static const float dummy = 0.0f;
+    c.a.SA = &dummy;
+    c.a.SB = &dummy;
+  }
+  return true;
 }
 
 }  // namespace
@@ -121,14 +145,15 @@ const char* tg_status_string(tg_status s) {
 tg_status tg_gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t sam, int64_t sak,
                       const void* B, int64_t sbk, int64_t sbn, void* C, int64_t scm, int64_t scn,
                       tg_stream_t stream) {
-  return tg::run(tg::make16(tg::Op::F16, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn), stream);
+  return tg::run(tg::make16(tg::Op::F16, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn),
+                 tg::Scratch{nullptr, 0}, stream);
 }
 
 tg_status tg_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t sam, int64_t sak,
                        const void* B, int64_t sbk, int64_t sbn, void* C, int64_t scm, int64_t scn,
                        tg_stream_t stream) {
   return tg::run(tg::make16(tg::Op::BF16, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn),
-                 stream);
+                 tg::Scratch{nullptr, 0}, stream);
 }
 
 tg_status tg_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const void* A, int64_t sam,
@@ -140,25 +165,65 @@ tg_status tg_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const void* A
   c.op = tg::Op::FP8;
   c.a = tg::GemmArgs{M, N, K, A, sam, sak, B, sbk, sbn, SA, ssam, ssak, SB, ssbn, ssbk, C, scm};
   c.scn = scn;
-  return tg::run(c, stream);
+  return tg::run(c, tg::Scratch{nullptr, 0}, stream);
+}
+
+tg_status tg_gemm_f16_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t sam,
+                         int64_t sak, const void* B, int64_t sbk, int64_t sbn, void* C,
+                         int64_t scm, int64_t scn, void* workspace, size_t workspace_bytes,
+                         tg_stream_t stream) {
+  const tg::Call c = tg::make16(tg::Op::F16, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn);
+  tg_status st = tg::validate(c);
+  if (st == TG_SUCCESS) st = tg::check_workspace(workspace, workspace_bytes);
+  if (st != TG_SUCCESS) return st;
+  return tg::run(c, tg::Scratch{static_cast<char*>(workspace), workspace_bytes}, stream);
+}
+
+tg_status tg_gemm_bf16_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t sam,
+                          int64_t sak, const void* B, int64_t sbk, int64_t sbn, void* C,
+                          int64_t scm, int64_t scn, void* workspace, size_t workspace_bytes,
+                          tg_stream_t stream) {
+  const tg::Call c = tg::make16(tg::Op::BF16, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn);
+  tg_status st = tg::validate(c);
+  if (st == TG_SUCCESS) st = tg::check_workspace(workspace, workspace_bytes);
+  if (st != TG_SUCCESS) return st;
+  return tg::run(c, tg::Scratch{static_cast<char*>(workspace), workspace_bytes}, stream);
+}
+
+tg_status tg_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K, const void* A,
+                                 int64_t sam, int64_t sak, const void* B, int64_t sbk,
+                                 int64_t sbn, void* C, int64_t scm, int64_t scn, size_t* bytes) {
+  tg::Call c;
+  if (bytes == nullptr || !tg::describe(op, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, c))
+    return TG_ERR_INVALID_VALUE;
+  const tg_status st = tg::validate(c);
+  if (st != TG_SUCCESS) return st;
+  *bytes = 0;
+  if (M == 0 || N == 0) return TG_SUCCESS;
+  const tg::Variant* v = tg::select(c);
+  if (v != nullptr && v->scratch_bytes != nullptr) *bytes = v->scratch_bytes(c.a);
+  return TG_SUCCESS;
+}
+
+const char* tg_gemm_plan_ws(int op, int64_t M, int64_t N, int64_t K, const void* A, int64_t sam,
+                            int64_t sak, const void* B, int64_t sbk, int64_t sbn, void* C,
+                            int64_t scm, int64_t scn, size_t workspace_bytes) {
+  tg::Call c;
+  if (!tg::describe(op, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, c)) return nullptr;
+  if (tg::validate(c) != TG_SUCCESS) return nullptr;
+  if (M == 0 || N == 0) return "none";
+  const tg::Variant* v = tg::select(c);
+  if (v == nullptr) return nullptr;
+  // a stand-in address: only the size decides the plan
+  alignas(256) static char stand_in;
+  const tg::Scratch ws{workspace_bytes > 0 ? &stand_in : nullptr, workspace_bytes};
+  return v->plan_name ? v->plan_name(c.a, ws) : v->name;
 }
 
 const char* tg_gemm_plan(int op, int64_t M, int64_t N, int64_t K, const void* A, int64_t sam,
                          int64_t sak, const void* B, int64_t sbk, int64_t sbn, void* C,
                          int64_t scm, int64_t scn) {
-  if (op < 0 || op > 2) return nullptr;
-  tg::Call c = tg::make16(static_cast<tg::Op>(op), M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn);
-  if (c.op == tg::Op::FP8) {
-    // scale pointers do not affect the choice; stand-ins pass the null checks
-    static const float dummy = 0.0f;
-    c.a.SA = &dummy;
-    c.a.SB = &dummy;
-  }
-  if (tg::validate(c) != TG_SUCCESS) return nullptr;
-  if (M == 0 || N == 0) return "none";
-  const tg::Variant* v = tg::select(c);
-  if (v == nullptr) return nullptr;
-  return v->plan_name ? v->plan_name(c.a) : v->name;
+  return tg_gemm_plan_ws(op, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, 0);
 }
 
 }  // extern "C"

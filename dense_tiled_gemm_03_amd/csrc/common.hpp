@@ -26,14 +26,38 @@ struct GemmArgs {
   int64_t scm;
 };
 
-// A kernel family: whether it takes a call, and how to launch it.
+// Device scratch a call may use to combine the partial results of several
+// workgroups (split K): `bytes` bytes at `ptr`, owned by the caller, or none
+// (ptr == nullptr).  Layout shared by every kernel that uses it: the first
+// kWorkspaceCounterBytes hold up to kWorkspaceCounters completion counters
+// (ints), which must be zero when a kernel starts and which every kernel
+// leaves zero; partial results start at kWorkspaceCounterBytes, so no call's
+// partials can land on a later call's counters.
+struct Scratch {
+  char* ptr;
+  size_t bytes;
+};
+constexpr int kWorkspaceCounters = 4096;
+constexpr size_t kWorkspaceCounterBytes = kWorkspaceCounters * sizeof(int);
+
+// A kernel family: whether it takes a call, and how to launch it.  Families
+// with a split-K plan run it when `ws` holds at least scratch_bytes(a)
+// bytes, and their allocation-free plan otherwise.
 struct Variant {
   const char* name;
   bool (*accepts)(Op op, const GemmArgs& a);
-  hipError_t (*launch)(Op op, const GemmArgs& a, hipStream_t s);
-  // Name of the instantiation a call would run (tile shape); NULL: `name`.
-  const char* (*plan_name)(const GemmArgs& a);
+  hipError_t (*launch)(Op op, const GemmArgs& a, const Scratch& ws, hipStream_t s);
+  // Name of the plan a call would run with scratch `ws`; NULL: `name`.
+  const char* (*plan_name)(const GemmArgs& a, const Scratch& ws);
+  // Scratch bytes of the split-K plan (0: the family has none for this
+  // call); NULL: never any.
+  size_t (*scratch_bytes)(const GemmArgs& a);
 };
+
+// True when `ws` can hold `need` bytes of scratch (need > 0).
+inline bool scratch_fits(const Scratch& ws, size_t need) {
+  return need > 0 && ws.ptr != nullptr && ws.bytes >= need;
+}
 
 // Defined by each kernel source file (host functions; see the tables in api.cpp).
 const Variant* variant_generic16();
@@ -55,18 +79,6 @@ struct GroupTable {
   int64_t row0[kMaxGroups + 1];
   int tile0[kMaxGroups + 1];
 };
-
-// Scratch of at least `bytes` for kernels on `stream` (current device).  NULL
-// when it cannot be had (allocation failure, or the stream is being captured).
-// Every kernel that uses it lays it out the same way, whatever the sizes of
-// earlier calls on the stream: the first kWorkspaceCounterBytes hold up to
-// kWorkspaceCounters completion counters (ints), zero whenever a kernel starts
-// and left zero by every kernel; partial results start at
-// kWorkspaceCounterBytes, so no call's partials can land on a later call's
-// counters.
-constexpr int kWorkspaceCounters = 4096;
-constexpr size_t kWorkspaceCounterBytes = kWorkspaceCounters * sizeof(int);
-void* stream_workspace(hipStream_t stream, size_t bytes);
 
 // Host-side checks of a product's sizes, strides and pointers (C with row
 // stride scm and column stride scn); TG_SUCCESS when the call is valid.

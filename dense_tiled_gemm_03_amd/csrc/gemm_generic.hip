@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_generic(GemmArgs a, int64_t tile
 
 bool accepts_any(Op, const GemmArgs&) { return true; }
 
-hipError_t launch16(Op op, const GemmArgs& a, hipStream_t s) {
+hipError_t launch16(Op op, const GemmArgs& a, const Scratch&, hipStream_t s) {
   const int64_t tn = cdiv(a.N, GT), tiles = cdiv(a.M, GT) * tn;
   if (op == Op::BF16)
     hipLaunchKernelGGL(gemm16_generic<__bf16>, dim3(tiles), dim3(256), 0, s, a, tn);
@@ -129,7 +129,7 @@ hipError_t launch16(Op op, const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fp8(Op, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_fp8(Op, const GemmArgs& a, const Scratch&, hipStream_t s) {
   const int64_t tn = cdiv(a.N, GT), tiles = cdiv(a.M, GT) * tn;
   hipLaunchKernelGGL(gemm_fp8_generic, dim3(tiles), dim3(256), 0, s, a, tn);
   return hipGetLastError();
@@ -138,11 +138,11 @@ hipError_t launch_fp8(Op, const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 const Variant* variant_generic16() {
-  static const Variant v = {"generic16_64x64", accepts_any, launch16, nullptr};
+  static const Variant v = {"generic16_64x64", accepts_any, launch16, nullptr, nullptr};
   return &v;
 }
 const Variant* variant_generic_fp8() {
-  static const Variant v = {"generic_fp8_64x64", accepts_any, launch_fp8, nullptr};
+  static const Variant v = {"generic_fp8_64x64", accepts_any, launch_fp8, nullptr, nullptr};
   return &v;
 }
 

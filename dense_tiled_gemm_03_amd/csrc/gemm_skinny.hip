@@ -263,6 +263,152 @@ __global__ __launch_bounds__(256) void gemm16_skinny(GemmArgs a, int splits, flo
   }
 }
 
+// The allocation-free skinny plan: each workgroup owns a 32-column strip of
+// C (all rows, up to 64) over the whole of K, so nothing is combined across
+// workgroups; its 4 waves split each 64-wide K slice instead, wave w taking
+// the slice's k16 step w, and their four fp32 partial tiles are added in
+// wave order through LDS at the end.  Same loads, swizzle, descriptors and
+// edges as gemm16_skinny, with a 12-stage ring of 12 KiB slices (8 KiB of
+// A, 4 KiB of B): each workgroup reads all of A (from L2, shared by every
+// strip) and its 32 rows of B.
+constexpr int WN = 32;                     // columns of C per workgroup
+constexpr int WSTAGES = 12;                // LDS ring depth
+constexpr int WSTAGE = (SM + WN) * ROWB;   // 12 KiB
+constexpr int WLD = (SM + WN) / 8 / 4;     // 1 KiB loads per wave per slice: 3
+constexpr int WRED_PITCH = WN + 4;         // fp32 row pitch of the partial tiles in LDS
+static_assert((WSTAGES - 1) * WLD <= 63, "loads in flight must fit the vmcnt counter");
+static_assert(4 * SM * WRED_PITCH * 4 <= WSTAGES * WSTAGE, "partial tiles must fit the ring");
+
+template <typename T>
+__global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
+  typedef typename Elem<T>::x8 T8;
+  __shared__ __attribute__((aligned(1024))) char lds[WSTAGES * WSTAGE];  // 144 KiB
+  const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * WN;
+  const int K = (int)a.K;
+  const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
+  const int rows_b = (int)min<int64_t>(WN, a.N - n0);
+  const T* Bb = static_cast<const T*>(a.B) + n0 * a.sbn;
+  const i32x4 ra = make_desc(a.A, (uint32_t)((((int)a.M - 1) * lda + K) * 2));
+  const i32x4 rb = make_desc(Bb, (uint32_t)(((rows_b - 1) * ldb + K) * 2));
+  const int count = (K + SK - 1) / SK;
+
+  // The stage's 8-row groups 0 .. 7 hold A's rows, 8 .. 11 the strip's B
+  // rows; wave w loads groups 3w .. 3w + 2.  Lane l writes stage row
+  // 8g + (l >> 3) at chunk position l & 7, i.e. logical chunk
+  // (l & 7) ^ (4 (g & 1) + (l >> 4)).
+  const uint32_t lrow = lane >> 3;
+  const uint32_t lc0 = (lane & 7) ^ (lane >> 4), lc1 = (lane & 7) ^ (4 + (lane >> 4));
+  auto load_slice = [&](int slot, int slice) {
+    if (slice >= count) return;  // nothing past K
+    const int k0 = slice * SK;
+    const uint32_t stage = lds32 + slot * WSTAGE;
+#pragma unroll
+    for (int j = 0; j < WLD; ++j) {
+      const int g = WLD * w + j;  // wave-uniform
+      const uint32_t c = (g & 1) ? lc1 : lc0;
+      const bool kin = k0 + 8 * (int)c < K;
+      if (g < SM / 8) {
+        const uint32_t off = (8 * g + lrow) * lda * 2 + 2 * k0 + 16 * c;
+        load_lds16(ra, stage + g * 1024, kin ? off : kOutOfRange);
+      } else {
+        const uint32_t off = (8 * (g - SM / 8) + lrow) * ldb * 2 + 2 * k0 + 16 * c;
+        load_lds16_nt(rb, stage + g * 1024, kin ? off : kOutOfRange);
+      }
+    }
+  };
+
+  // Wave w's fragments of a slice (32x32x16, its k16 step w): A rows
+  // (l & 31) and 32 + (l & 31), B rows (l & 31), chunk 2w + (l >> 5) at
+  // position chunk ^ ((l >> 1) & 7).
+  const int rd = (lane & 31) * ROWB + (((2 * w + (lane >> 5)) ^ ((lane >> 1) & 7)) * 16);
+  f32x16 acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+  T8 fa0[2], fa1[2], fb[2];
+  auto read_slice = [&](int buf, int slot) {
+    const char* base = lds + slot * WSTAGE;
+    fa0[buf] = *reinterpret_cast<const T8*>(base + rd);
+    fa1[buf] = *reinterpret_cast<const T8*>(base + 32 * ROWB + rd);
+    fb[buf] = *reinterpret_cast<const T8*>(base + SM * ROWB + rd);
+  };
+  // As in gemm16_skinny: wait for slice i + 1 and for every wave's reads of
+  // slice i, refill slice i's slot with slice i + WSTAGES, read slice i + 1,
+  // multiply slice i.
+  auto step = [&](int i, int cur) {
+    if (i + WSTAGES - 1 < count)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((WSTAGES - 2) * WLD) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+    load_slice(i % WSTAGES, i + WSTAGES);
+    if (i + 1 < count) read_slice(cur ^ 1, (i + 1) % WSTAGES);
+    __builtin_amdgcn_sched_barrier(0);
+    acc[0] = mfma32x32x16(fa0[cur], fb[cur], acc[0]);
+    acc[1] = mfma32x32x16(fa1[cur], fb[cur], acc[1]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int p = 0; p < WSTAGES; ++p) load_slice(p, p);
+  if (WSTAGES <= count)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((WSTAGES - 1) * WLD) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_barrier" ::: "memory");
+  read_slice(0, 0);
+  int i = 0;
+  for (; i + 1 < count; i += 2) {
+    step(i, 0);
+    step(i + 1, 1);
+  }
+  if (i < count) step(i, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // The four waves' partial tiles through LDS: wave w's lane l holds column
+  // l & 31, rows 32i + 8(v/4) + 4(l >> 5) + (v % 4).
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = 32 * i2 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      red[(w * SM + row) * WRED_PITCH + (lane & 31)] = acc[i2][v];
+    }
+  __syncthreads();
+  // Thread t, step e: float4 q = 256 e + t of the 64 x 32 tile (row q >> 3,
+  // columns 4 (q & 7) .. + 3), the sum of the four partials in wave order.
+  typedef typename Elem<T>::x4 T4;
+  T* Cb = static_cast<T*>(a.C);
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int q = 256 * e + t, row = q >> 3, col = 4 * (q & 7);
+    f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww)
+      x += *reinterpret_cast<const f32x4*>(red + (ww * SM + row) * WRED_PITCH + col);
+    if (row >= a.M) continue;
+    T* C = Cb + (int64_t)row * a.scm + n0 + col;
+    T4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = to_out<T>(x[j]);
+    if (n0 + col + 4 <= a.N && (reinterpret_cast<uintptr_t>(C) & 7) == 0) {
+      *reinterpret_cast<T4*>(C) = o;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (n0 + col + j < a.N) C[j] = o[j];
+    }
+  }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // At most 64 rows, both operands K-contiguous with 16-byte aligned rows;
@@ -288,26 +434,47 @@ int choose_splits(const GemmArgs& a) {
   return s < 1 ? 1 : (int)s;
 }
 
-hipError_t launch(Op op, const GemmArgs& a, hipStream_t stream) {
+// Scratch of the split plan: one counter per strip in the fixed counter
+// area, then each split's 64 x 128 fp32 partial tile (0: no split).
+size_t scratch_bytes(const GemmArgs& a) {
   const int64_t strips = cdiv(a.N, SN);
-  int splits = choose_splits(a);
-  float* part = nullptr;
-  int* counters = nullptr;
-  if (splits > 1) {
-    // one counter per strip at the start of the scratch, partial tiles after
-    // the fixed counter area
-    const size_t bytes = kWorkspaceCounterBytes + (size_t)strips * splits * SM * SN * 4;
-    char* ws = strips <= kWorkspaceCounters
-                   ? static_cast<char*>(stream_workspace(stream, bytes))
-                   : nullptr;
-    if (ws == nullptr) {
-      splits = 1;  // no scratch to be had: one workgroup per strip, no combining
-    } else {
-      counters = reinterpret_cast<int*>(ws);
-      part = reinterpret_cast<float*>(ws + kWorkspaceCounterBytes);
-    }
+  const int splits = choose_splits(a);
+  if (splits == 1 || strips > kWorkspaceCounters) return 0;
+  return kWorkspaceCounterBytes + (size_t)strips * splits * SM * SN * 4;
+}
+
+// Plans: with scratch for the split, 64 x 128 strips split K across
+// workgroups; without it, 32-column strips over all of K (waves split each
+// slice); when no split is wanted (short K, or enough strips), 64 x 128
+// strips unsplit.
+enum class Skinny { Strip128, Split128, Strip32 };
+Skinny choose(const GemmArgs& a, const Scratch& ws, int& splits) {
+  splits = choose_splits(a);
+  if (splits == 1) return Skinny::Strip128;
+  if (scratch_fits(ws, scratch_bytes(a))) return Skinny::Split128;
+  splits = 1;
+  return Skinny::Strip32;
+}
+
+hipError_t launch(Op op, const GemmArgs& a, const Scratch& ws, hipStream_t stream) {
+  int splits;
+  const Skinny plan = choose(a, ws, splits);
+  const dim3 block(256);
+  if (plan == Skinny::Strip32) {
+    const dim3 grid((unsigned)cdiv(a.N, WN));
+    if (op == Op::BF16)
+      hipLaunchKernelGGL(gemm16_skinny_wsplit<__bf16>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(gemm16_skinny_wsplit<_Float16>, grid, block, 0, stream, a);
+    return hipGetLastError();
   }
-  const dim3 grid((unsigned)(strips * splits)), block(256);
+  int* counters = nullptr;
+  float* part = nullptr;
+  if (plan == Skinny::Split128) {
+    counters = reinterpret_cast<int*>(ws.ptr);
+    part = reinterpret_cast<float*>(ws.ptr + kWorkspaceCounterBytes);
+  }
+  const dim3 grid((unsigned)(cdiv(a.N, SN) * splits));
   if (op == Op::BF16)
     hipLaunchKernelGGL(gemm16_skinny<__bf16>, grid, block, 0, stream, a, splits, part, counters);
   else
@@ -316,10 +483,21 @@ hipError_t launch(Op op, const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+const char* const kSplitNames[] = {"", "skinny_64x128", "skinny_64x128_splitk2",
+                                   "skinny_64x128_splitk3", "skinny_64x128_splitk4",
+                                   "skinny_64x128_splitk5", "skinny_64x128_splitk6",
+                                   "skinny_64x128_splitk7", "skinny_64x128_splitk8"};
+const char* name_of(const GemmArgs& a, const Scratch& ws) {
+  int splits;
+  const Skinny plan = choose(a, ws, splits);
+  if (plan == Skinny::Strip32) return "skinny_64x32";
+  return splits <= 8 ? kSplitNames[splits] : "skinny_64x128_splitk";
+}
+
 }  // namespace
 
 const Variant* variant_skinny16() {
-  static const Variant v = {"skinny_64x128", accepts, launch, nullptr};
+  static const Variant v = {"skinny", accepts, launch, name_of, scratch_bytes};
   return &v;
 }
 

@@ -350,7 +350,7 @@ bool accepts(Op op, const GemmArgs& a) {
   return true;
 }
 
-hipError_t launch(Op, const GemmArgs& a, hipStream_t s) {
+hipError_t launch(Op, const GemmArgs& a, const Scratch&, hipStream_t s) {
   const int tm = (int)cdiv(a.M, F_BM), tn = (int)cdiv(a.N, F_BN);
   hipLaunchKernelGGL(gemm_fp8_tile, dim3(tm * tn), dim3(64 * F_WAVES), 0, s, a, tm, tn);
   return hipGetLastError();
@@ -461,7 +461,7 @@ tg_status run_grouped(const Grouped8& c, tg_stream_t stream) {
 }  // namespace
 
 const Variant* variant_tile_fp8() {
-  static const Variant v = {"tile_fp8_256x128", accepts, launch, nullptr};
+  static const Variant v = {"tile_fp8_256x128", accepts, launch, nullptr, nullptr};
   return &v;
 }
 

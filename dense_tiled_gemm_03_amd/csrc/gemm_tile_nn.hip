@@ -27,7 +27,7 @@ bool accepts(Op op, const GemmArgs& a) {
   return true;
 }
 
-hipError_t launch(Op op, const GemmArgs& a, hipStream_t s) {
+hipError_t launch(Op op, const GemmArgs& a, const Scratch&, hipStream_t s) {
   const int tm = (int)cdiv(a.M, Tile256::BM), tn = (int)cdiv(a.N, Tile256::BN);
   const dim3 grid(tm * tn), block(256);
   if (op == Op::BF16)
@@ -40,7 +40,7 @@ hipError_t launch(Op op, const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 const Variant* variant_tile_nn16() {
-  static const Variant v = {"tile_nn_256x256", accepts, launch, nullptr};
+  static const Variant v = {"tile_nn_256x256", accepts, launch, nullptr, nullptr};
   return &v;
 }
 

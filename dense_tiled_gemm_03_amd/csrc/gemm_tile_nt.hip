@@ -71,67 +71,113 @@ int splits_for(const GemmArgs& a) {
   return s < 2 ? 1 : (int)s;
 }
 
-// Grids of one whole wave of 256 x 224 tiles and a partial one: the split
-// of the partial wave's tiles over K that tile::tail_splits finds cheapest
-// (1: none).  256 x 256 grids run unsplit: their combine holds 256
-// accumulators per thread and spills, and splitting their partial waves
-// measured no faster.
-template <typename Cfg>
-int tail_for(const GemmArgs& a) {
-  if (!std::is_same<Cfg, Tile224>::value) return 1;
-  return tile::tail_splits(cdiv(a.M, Cfg::BM) * cdiv(a.N, Cfg::BN), cdiv(a.K, 64), kCus);
+// Tile choice.  Small grids (at most half the CUs in 256 x 224 tiles) take
+// 128 x 128 tiles when K is at most kShortK slices, or when no scratch is
+// at hand to split K: four times the tiles, so fewer or no K splits, and a
+// lower fixed cost per tile (measured on 1024^3, 2048^3, 1024 x 1024 x 4096
+// and 512 x 512 x 8192: 1.6 to 3.2 times faster than 256 x 224 with split
+// K).  Up to 256 of them run with three stages per operand, one workgroup per
+// CU (2048^3: 18.3 us against 24.0 with two stages); more run with two
+// stages, two workgroups per CU (4096 x 1792 x 4096: 50.4 us against 57.1
+// with three).  With longer K the larger tile's lower bytes per FLOP win
+// (4096 x 896 x 16384, 2048 x 1024 x 16384) when it may split K.  Other
+// grids run in ceil(tiles / 256) waves over the 256 CUs, each wave costing
+// about one tile's MFMA work (with 256 x 224 and scratch, a partial second
+// wave may have its tiles split over K: tile::tail_splits).  The shape with
+// the smaller waves x tile area wins, 256 x 256 on ties (4096 x 7168:
+// 256 x 224 gives 512 tiles = 2 full waves, 256 x 256 gives 448 tiles =
+// 1.75 waves rounded up to 2).
+double cost(const GemmArgs& a, int64_t bm, int64_t bn, bool split_ok) {
+  const int64_t tiles = cdiv(a.M, bm) * cdiv(a.N, bn), nk = cdiv(a.K, 64);
+  const int s = bn == 224 && split_ok ? tile::tail_splits(tiles, nk, kCus) : 1;
+  return tile::tail_waves(tiles, nk, kCus, s) * double(bm * bn);
 }
+enum class Shape { T128, T128x2, T224, T256 };
 
-template <typename Cfg>
-hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
-  const int tm = (int)cdiv(a.M, Cfg::BM), tn = (int)cdiv(a.N, Cfg::BN);
-  if constexpr (std::is_same<Cfg, Tile224>::value) {
-    const int splits = tail_for<Cfg>(a);
-    if (splits > 1) {
-      // scratch: one counter per split tile in the fixed counter area, then
-      // each split's fp32 partial tile
-      const int tiles = tm * tn, tail = tiles % (int)kCus, full = tiles - tail;
-      const size_t part_bytes = (size_t)Cfg::BM * Cfg::BN * 4 * splits * tail;
-      char* ws = static_cast<char*>(stream_workspace(s, kWorkspaceCounterBytes + part_bytes));
-      if (ws != nullptr) {
-        int* counters = reinterpret_cast<int*>(ws);
-        float* part = reinterpret_cast<float*>(ws + kWorkspaceCounterBytes);
-        const dim3 grid((unsigned)(full + tail * splits)), block(256);
-        if (op == Op::BF16)
-          hipLaunchKernelGGL((tile::gemm16_tile_tail<__bf16, Cfg>), grid, block, 0, s, a, tm, tn,
-                             full, splits, part, counters);
-        else
-          hipLaunchKernelGGL((tile::gemm16_tile_tail<_Float16, Cfg>), grid, block, 0, s, a, tm,
-                             tn, full, splits, part, counters);
-        return hipGetLastError();
-      }
-      // no scratch to be had (stream capture, allocation failure): unsplit
+// A call's plan: tile shape, K splits per tile (splits > 1 with tail: only
+// the tiles past the first whole wave are split) and its scratch bytes.
+struct Plan {
+  Shape shape;
+  int splits;
+  bool tail;
+  size_t bytes;
+};
+
+Plan plan_of(const GemmArgs& a, bool split_ok) {
+  Plan p{Shape::T256, 1, false, 0};
+  if (small_grid(a)) {
+    if (split_ok && cdiv(a.K, 64) > kShortK) {
+      p.shape = Shape::T224;
+      p.splits = splits_for<Tile224>(a);
+    } else if (cdiv(a.M, 128) * cdiv(a.N, 128) <= kCus) {
+      p.shape = Shape::T128;
+      p.splits = split_ok ? splits_for<Tile128>(a) : 1;
+    } else {
+      p.shape = Shape::T128x2;
+    }
+  } else if (cost(a, 256, 224, split_ok) < cost(a, 256, 256, split_ok)) {
+    p.shape = Shape::T224;
+    if (split_ok) {
+      p.splits = tile::tail_splits(cdiv(a.M, 256) * cdiv(a.N, 224), cdiv(a.K, 64), kCus);
+      p.tail = p.splits > 1;
     }
   }
-  const int splits = splits_for<Cfg>(a);
+  if (p.splits > 1) {
+    // one counter per split tile in the fixed counter area (at most 4096),
+    // then each split's fp32 partial tile
+    const int64_t bm = p.shape == Shape::T224 ? 256 : 128, bn = p.shape == Shape::T224 ? 224 : 128;
+    const int64_t tiles = cdiv(a.M, bm) * cdiv(a.N, bn);
+    const int64_t split_tiles = p.tail ? tiles % kCus : tiles;
+    if (split_tiles > kWorkspaceCounters) {
+      p.splits = 1;
+      p.tail = false;
+    } else {
+      p.bytes = kWorkspaceCounterBytes + (size_t)(bm * bn * 4) * p.splits * split_tiles;
+    }
+  }
+  return p;
+}
+
+// The split plan when `ws` holds its scratch, else the allocation-free one.
+Plan choose(const GemmArgs& a, const Scratch& ws) {
+  const Plan p = plan_of(a, true);
+  if (p.bytes == 0 || scratch_fits(ws, p.bytes)) return p;
+  return plan_of(a, false);
+}
+
+size_t scratch_bytes(const GemmArgs& a) { return plan_of(a, true).bytes; }
+
+template <typename Cfg>
+hipError_t launch_cfg(Op op, const GemmArgs& a, const Plan& p, const Scratch& ws, hipStream_t s) {
+  const int tm = (int)cdiv(a.M, Cfg::BM), tn = (int)cdiv(a.N, Cfg::BN);
   if constexpr (std::is_same<Cfg, Tile224>::value || std::is_same<Cfg, Tile128>::value) {
-   if (splits > 1) {
-    // scratch: one counter per tile in the fixed counter area, then each
-    // split's fp32 partial tile
-    const size_t tiles = (size_t)tm * tn;
-    const size_t part_bytes = (size_t)Cfg::BM * Cfg::BN * 4 * splits * tiles;
-    char* ws = tiles <= (size_t)kWorkspaceCounters
-                   ? static_cast<char*>(stream_workspace(s, kWorkspaceCounterBytes + part_bytes))
-                   : nullptr;
-    if (ws != nullptr) {
-      int* counters = reinterpret_cast<int*>(ws);
-      float* part = reinterpret_cast<float*>(ws + kWorkspaceCounterBytes);
-      const dim3 grid((unsigned)(tiles * splits)), block(256);
+    if (p.splits > 1) {
+      int* counters = reinterpret_cast<int*>(ws.ptr);
+      float* part = reinterpret_cast<float*>(ws.ptr + kWorkspaceCounterBytes);
+      const dim3 block(256);
+      if (p.tail) {
+        if constexpr (std::is_same<Cfg, Tile224>::value) {
+          // whole tiles of the first wave, then the split tiles' units
+          const int tiles = tm * tn, tail = tiles % (int)kCus, full = tiles - tail;
+          const dim3 grid((unsigned)(full + tail * p.splits));
+          if (op == Op::BF16)
+            hipLaunchKernelGGL((tile::gemm16_tile_tail<__bf16, Cfg>), grid, block, 0, s, a, tm,
+                               tn, full, p.splits, part, counters);
+          else
+            hipLaunchKernelGGL((tile::gemm16_tile_tail<_Float16, Cfg>), grid, block, 0, s, a, tm,
+                               tn, full, p.splits, part, counters);
+          return hipGetLastError();
+        }
+      }
+      const dim3 grid((unsigned)(tm * tn * p.splits));
       if (op == Op::BF16)
         hipLaunchKernelGGL((tile::gemm16_tile_splitk<__bf16, Cfg>), grid, block, 0, s, a, tm, tn,
-                           splits, part, counters);
+                           p.splits, part, counters);
       else
         hipLaunchKernelGGL((tile::gemm16_tile_splitk<_Float16, Cfg>), grid, block, 0, s, a, tm,
-                           tn, splits, part, counters);
+                           tn, p.splits, part, counters);
       return hipGetLastError();
     }
-    // no scratch to be had (stream capture, allocation failure): unsplit
-   }
   }
   const dim3 grid(tm * tn), block(256);
   if (op == Op::BF16)
@@ -141,41 +187,13 @@ hipError_t launch_cfg(Op op, const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile choice.  Small grids (at most half the CUs in 256 x 224 tiles) with
-// K of at most kShortK slices take 128 x 128 tiles: four times the tiles,
-// so fewer or no K splits, and a lower fixed cost per tile (measured on
-// 1024^3, 2048^3, 1024 x 1024 x 4096 and 512 x 512 x 8192: 1.6 to 3.2 times
-// faster than 256 x 224 with split K).  Up to 256 of them run with three
-// stages per operand, one workgroup per CU (2048^3: 18.3 us against 24.0
-// with two stages); more run with two stages, two workgroups per CU
-// (4096 x 1792 x 4096: 50.4 us against 57.1 with three).  With longer K the larger tile's
-// lower bytes per FLOP win (4096 x 896 x 16384, 2048 x 1024 x 16384), and so
-// does 256 x 224 with split K.  Other grids run in ceil(tiles / 256) waves
-// over the 256 CUs, each wave costing about one tile's MFMA work (with
-// 256 x 224, a partial second wave may have its tiles split over K:
-// tail_for).  The shape with the smaller waves x tile area wins, 256 x 256
-// on ties (4096 x 7168: 256 x 224 gives 512 tiles = 2 full waves, 256 x 256
-// gives 448 tiles = 1.75 waves rounded up to 2).
-double cost(const GemmArgs& a, int64_t bm, int64_t bn) {
-  const int64_t tiles = cdiv(a.M, bm) * cdiv(a.N, bn), nk = cdiv(a.K, 64);
-  const int s = bn == 224 ? tile::tail_splits(tiles, nk, kCus) : 1;
-  return tile::tail_waves(tiles, nk, kCus, s) * double(bm * bn);
-}
-enum class Shape { T128, T128x2, T224, T256 };
-Shape shape_of(const GemmArgs& a) {
-  if (small_grid(a)) {
-    if (cdiv(a.K, 64) > kShortK) return Shape::T224;
-    return cdiv(a.M, 128) * cdiv(a.N, 128) <= kCus ? Shape::T128 : Shape::T128x2;
-  }
-  return cost(a, 256, 224) < cost(a, 256, 256) ? Shape::T224 : Shape::T256;
-}
-
-hipError_t launch(Op op, const GemmArgs& a, hipStream_t s) {
-  switch (shape_of(a)) {
-    case Shape::T128: return launch_cfg<Tile128>(op, a, s);
-    case Shape::T128x2: return launch_cfg<Tile128x2>(op, a, s);
-    case Shape::T224: return launch_cfg<Tile224>(op, a, s);
-    default: return launch_cfg<Tile256>(op, a, s);
+hipError_t launch(Op op, const GemmArgs& a, const Scratch& ws, hipStream_t s) {
+  const Plan p = choose(a, ws);
+  switch (p.shape) {
+    case Shape::T128: return launch_cfg<Tile128>(op, a, p, ws, s);
+    case Shape::T128x2: return launch_cfg<Tile128x2>(op, a, p, ws, s);
+    case Shape::T224: return launch_cfg<Tile224>(op, a, p, ws, s);
+    default: return launch_cfg<Tile256>(op, a, p, ws, s);
   }
 }
 
@@ -193,14 +211,12 @@ const char* const kTails224[] = {"", "", "tile_nt_256x224_tail2", "tile_nt_256x2
                                  "tile_nt_256x224_tail4", "tile_nt_256x224_tail5",
                                  "tile_nt_256x224_tail6", "tile_nt_256x224_tail7",
                                  "tile_nt_256x224_tail8"};
-const char* name_of(const GemmArgs& a) {
-  switch (shape_of(a)) {
-    case Shape::T128: return kNames128[splits_for<Tile128>(a)];
+const char* name_of(const GemmArgs& a, const Scratch& ws) {
+  const Plan p = choose(a, ws);
+  switch (p.shape) {
+    case Shape::T128: return kNames128[p.splits];
     case Shape::T128x2: return "tile_nt_128x128_2stage";
-    case Shape::T224: {
-      const int t = tail_for<Tile224>(a);
-      return t > 1 ? kTails224[t] : kNames224[splits_for<Tile224>(a)];
-    }
+    case Shape::T224: return p.tail ? kTails224[p.splits] : kNames224[p.splits];
     default: return "tile_nt_256x256";
   }
 }
@@ -208,7 +224,7 @@ const char* name_of(const GemmArgs& a) {
 }  // namespace
 
 const Variant* variant_tile_nt16() {
-  static const Variant v = {"tile_nt", accepts, launch, name_of};
+  static const Variant v = {"tile_nt", accepts, launch, name_of, scratch_bytes};
   return &v;
 }
 

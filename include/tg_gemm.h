@@ -25,27 +25,13 @@
  *    is rounded once to the output type, round-to-nearest-even.
  *  - A, B, C (and scales) are DEVICE pointers owned by the caller; they must
  *    stay valid until the work enqueued on `stream` has completed.
- *  - Scratch: products with M <= 64, products whose output tiles would fill
- *    fewer than half the CUs, and products of one whole wave of 256 x 224
- *    tiles plus a partial one (the partial wave's tiles) split K across
- *    workgroups and combine the
- *    partial results through a device buffer the library owns, one per
- *    (device, stream), allocated on the first such call on that stream,
- *    grown (at least doubling) when a later call needs more, and kept until
- *    the process ends -- an outgrown buffer is not freed either, since a
- *    graph captured earlier may still use it: a fixed 16 KiB area of
- *    completion counters,
- *    then the fp32 partial tiles -- 4 bytes per element of C per K split of
- *    each split tile (7.3 MiB for 64 x 7168 x 7168, 44 MiB for 4352 x 4096
- *    x 4096).  Such a call made while the
- *    stream is being captured into a graph, or when the buffer cannot be had,
- *    runs without splitting K instead.  No other call allocates.
- *  - Calls are asynchronous: they enqueue on `stream` (a hipStream_t; NULL is
- *    the null stream) and return.  They are reentrant; calls on different
- *    streams never share scratch.  A call captured into a graph on a stream
- *    whose scratch already exists uses that stream's buffer: replay the
- *    graph where it cannot overlap other split-K work on the capturing
- *    stream (on that stream itself, or synchronised with it).
+ *  - These entry points allocate nothing, keep no state between calls and
+ *    never synchronise: each call validates its arguments on the host,
+ *    enqueues one kernel on `stream` and returns.  They are reentrant and
+ *    may be captured into HIP graphs.  Products that would run faster with
+ *    K split across workgroups (M <= 64, grids that fill few CUs, a partial
+ *    last wave) run allocation-free plans here; the *_ws entry points below
+ *    take a caller-owned workspace for the split plans.
  *  - C must not overlap A, B or the scales (undefined behaviour otherwise).
  *
  * Errors (tg_status)
@@ -66,6 +52,7 @@
 #ifndef TG_GEMM_H
 #define TG_GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -121,6 +108,56 @@ tg_status tg_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
                                   const void* B, int64_t sbk, int64_t sbn,
                                   const float* SB, int64_t ssbn, int64_t ssbk,
                                   void* C, int64_t scm, int64_t scn, tg_stream_t stream);
+
+/* The same products with a caller-owned workspace, for the plans that split
+ * K across the workgroups of an output tile and add their fp32 partial
+ * tiles in split order (deterministic): products with M <= 64 (64 x 128
+ * strips of C, K split so that there is about one workgroup per CU), grids
+ * of output tiles that would fill at most half the CUs (one GPU's share of
+ * a larger product, e.g. 4096 x 896 x 16384: 256 x 224 tiles, K split 4
+ * ways), and grids of one whole wave of 256 x 224 tiles and a partial one
+ * (the partial wave's tiles split).  The split is the K loop of
+ * "TileKernels deep dive" section 3.1 cut into ranges whose tile sums are
+ * added at the end.
+ *   workspace:  device buffer of workspace_bytes bytes, 256-byte aligned,
+ *               owned by the caller.  Its first 16 KiB hold completion
+ *               counters that must be ZERO before the buffer's first use
+ *               (e.g. allocate it with torch.zeros); every call leaves them
+ *               zero again when its kernel completes.  The rest holds fp32
+ *               partial tiles.  Calls whose work overlaps in time must not
+ *               share a workspace (different streams, or graph replays that
+ *               may run concurrently): they would race on the counters and
+ *               partials.  It must not overlap A, B or C.
+ *   workspace_bytes: 0 (no workspace: the call runs exactly as tg_gemm_f16
+ *               / tg_gemm_bf16), or the buffer's size.  A call whose split
+ *               plan needs more than workspace_bytes (tg_gemm_workspace_size)
+ *               runs the allocation-free plan instead; it never fails for
+ *               lack of workspace.
+ * Results: within the same bound as the allocation-free plans, and bit for
+ * bit equal to them when every fp32 partial sum is exact (integer inputs).
+ * Errors: those of tg_gemm_f16, plus TG_ERR_INVALID_VALUE for
+ * workspace_bytes > 0 with a NULL or not 256-byte aligned workspace.
+ * Nothing is allocated; asynchronous on `stream`. */
+tg_status tg_gemm_f16_ws(int64_t M, int64_t N, int64_t K,
+                         const void* A, int64_t sam, int64_t sak,
+                         const void* B, int64_t sbk, int64_t sbn,
+                         void* C, int64_t scm, int64_t scn,
+                         void* workspace, size_t workspace_bytes, tg_stream_t stream);
+tg_status tg_gemm_bf16_ws(int64_t M, int64_t N, int64_t K,
+                          const void* A, int64_t sam, int64_t sak,
+                          const void* B, int64_t sbk, int64_t sbn,
+                          void* C, int64_t scm, int64_t scn,
+                          void* workspace, size_t workspace_bytes, tg_stream_t stream);
+
+/* Workspace bytes the split plan of a call with these arguments uses (0: the
+ * call has no split plan, so a workspace changes nothing).  op: 0 = f16,
+ * 1 = bf16, 2 = fp8 block-scaled (always 0).  Host only: no HIP call.
+ * Errors: TG_ERR_INVALID_VALUE for a NULL `bytes`, an unknown op, or
+ * arguments the product would reject (the same validation). */
+tg_status tg_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K,
+                                 const void* A, int64_t sam, int64_t sak,
+                                 const void* B, int64_t sbk, int64_t sbn,
+                                 void* C, int64_t scm, int64_t scn, size_t* bytes);
 
 /* Grouped product: G independent products sharing N and K, group g with its
  * own row count -- the grouped GEMM of the TileLang examples ("Getting to
@@ -256,11 +293,18 @@ const char* tg_gemm_quant_fp8_plan(int op, int64_t M, int64_t N, int64_t K,
 /* Name of the kernel a call with these arguments would launch ("none" for a
  * no-op, NULL if the arguments are invalid); nothing is launched.  op: 0 =
  * tg_gemm_f16, 1 = tg_gemm_bf16, 2 = tg_gemm_fp8_blockscaled (the scale
- * arguments do not affect the choice).  For tests and benchmarks. */
+ * arguments do not affect the choice).  tg_gemm_plan names the plan of the
+ * allocation-free entry points; tg_gemm_plan_ws the plan of
+ * tg_gemm_f16_ws / tg_gemm_bf16_ws with a workspace of workspace_bytes.
+ * Host only.  For tests and benchmarks. */
 const char* tg_gemm_plan(int op, int64_t M, int64_t N, int64_t K,
                          const void* A, int64_t sam, int64_t sak,
                          const void* B, int64_t sbk, int64_t sbn,
                          void* C, int64_t scm, int64_t scn);
+const char* tg_gemm_plan_ws(int op, int64_t M, int64_t N, int64_t K,
+                            const void* A, int64_t sam, int64_t sak,
+                            const void* B, int64_t sbk, int64_t sbn,
+                            void* C, int64_t scm, int64_t scn, size_t workspace_bytes);
 
 #ifdef __cplusplus
 }

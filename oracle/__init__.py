@@ -60,6 +60,8 @@ class Oracle:
         lib.tg_oracle_quant_fp8.restype = c_int
         lib.tg_oracle_bound.argtypes = [c_int, vp, i64, vp]
         lib.tg_oracle_bound.restype = None
+        lib.tg_oracle_threads.argtypes = [c_int]
+        lib.tg_oracle_threads.restype = None
         lib.tg_oracle_init()
         self.lib = lib
 
@@ -131,6 +133,10 @@ class Oracle:
         self.lib.tg_oracle_round(FMT[fmt], _p(x), x.size, _p(out))
         return out
 
+    def threads(self, n: int) -> None:
+        """Threads of the oracle's parallel row loops (0: every core)."""
+        self.lib.tg_oracle_threads(int(n))
+
     def bound(self, fmt_out: str, S: np.ndarray) -> np.ndarray:
         """Per-element acceptance bound on |C_gpu - C_ref| (see oracle.c):
         four unit roundoffs of the output format times S = sum_k |a||b|."""
@@ -181,6 +187,10 @@ def gemm_fp8_blockscaled(*args, **kw):
 
 def gemm_quant_fp8(*args, **kw):
     return default().gemm_quant_fp8(*args, **kw)
+
+
+def threads(n):
+    default().threads(n)
 
 
 def round_to(fmt, x):

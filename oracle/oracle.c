@@ -30,6 +30,7 @@
  * fast-math and with -ffp-contract=off (no fused multiply-add contraction).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -81,6 +82,10 @@ static void build_tables(void) {
 }
 
 void tg_oracle_init(void) { build_tables(); }
+
+/* Threads of the parallel row loops (n <= 0: every available core).  The
+ * result does not depend on it: each output row is one thread's work. */
+void tg_oracle_threads(int n) { omp_set_num_threads(n > 0 ? n : omp_get_num_procs()); }
 
 /* Decode n codes of a format (1 = fp16, 2 = bf16, 3 = e4m3fn) for tests. */
 void tg_oracle_decode(int fmt, const void* codes, int64_t n, double* out) {

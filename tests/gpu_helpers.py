@@ -55,20 +55,50 @@ def check_guards(buf, off, M, N, scm):
             assert np.all(gap == CANARY), f"write into padding after row {i}"
 
 
+class Workspace:
+    """A caller-owned workspace for the *_ws entry points: zero-filled device
+    memory (the completion counters must start at zero), 256-byte aligned."""
+
+    COUNTER_BYTES = 16384
+
+    def __init__(self, nbytes: int):
+        self.nbytes = int(nbytes)
+        self.buf = torch.zeros(self.nbytes + 256, dtype=torch.uint8, device="cuda")
+        self.ptr = (self.buf.data_ptr() + 255) & ~255
+        self.off = self.ptr - self.buf.data_ptr()
+
+    def counters_zero(self) -> bool:
+        n = min(self.nbytes, self.COUNTER_BYTES)
+        return bool(torch.all(self.buf[self.off:self.off + n] == 0).item())
+
+
 def run16(fmt: str, M, N, K, A, sam, sak, B, sbk, sbn, scm=None, a_off=0, b_off=0,
-          stream=None):
+          stream=None, ws=None):
     """Call tg_gemm_f16 / tg_gemm_bf16 on device tensors A, B (codes, element
-    offsets a_off / b_off); returns (C codes M x N, plan name).  Checks guards."""
+    offsets a_off / b_off); returns (C codes M x N, plan name).  Checks guards.
+    ws=True: call tg_gemm_f16_ws / tg_gemm_bf16_ws with a fresh zeroed
+    workspace of the size the split plan asks for; ws=<Workspace>: with that
+    one.  After a workspace call its counters must be zero again."""
     buf, off, scm = alloc_c(M, N, scm)
     esz = 2
     args = (M, N, K, A.data_ptr() + a_off * esz, sam, sak, B.data_ptr() + b_off * esz, sbk, sbn,
             buf.data_ptr() + off * esz, scm, 1)
     op = tg.OP_BF16 if fmt == "bf16" else tg.OP_F16
-    plan = tg.tg_gemm_plan(op, *args)
-    fn = tg.tg_gemm_bf16 if fmt == "bf16" else tg.tg_gemm_f16
-    fn(*args, torch.cuda.current_stream().cuda_stream if stream is None else stream)
+    st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+    if ws is None or ws is False:
+        plan = tg.tg_gemm_plan(op, *args)
+        fn = tg.tg_gemm_bf16 if fmt == "bf16" else tg.tg_gemm_f16
+        fn(*args, st)
+    else:
+        if ws is True:
+            ws = Workspace(tg.tg_gemm_workspace_size(op, *args))
+        plan = tg.tg_gemm_plan_ws(op, *args, ws.nbytes)
+        fn = tg.tg_gemm_bf16_ws if fmt == "bf16" else tg.tg_gemm_f16_ws
+        fn(*args, ws.ptr, ws.nbytes, st)
     torch.cuda.synchronize()
     check_guards(buf, off, M, N, scm)
+    if ws is not None and ws is not False:
+        assert ws.counters_zero(), "workspace counters left nonzero"
     return c_view(buf, off, M, N, scm), plan
 
 

@@ -269,50 +269,67 @@ def test_plan_names(lib):
 
 
 # The kernel each benchmark workload is planned onto (host-side choice; no
-# launch).  A silent fallback to the general kernel fails here.
+# launch), by the allocation-free entry points and by the workspace ones
+# given all the workspace their split plans ask for.  A silent fallback to
+# the general kernel fails here.
 EXPECTED_PLANS = {
-    "fp16_256": "tile_nn_256x256",
-    "bf16_4096": "tile_nn_256x256",
-    "bf16_4096x7168x16384": "tile_nt_256x224",
-    "bf16_skinny_64x7168x7168": "skinny_64x128",
-    "fp8_4096x7168x16384": "tile_fp8_256x128",
+    "fp16_256": ("tile_nn_256x256", "tile_nn_256x256"),
+    "bf16_4096": ("tile_nn_256x256", "tile_nn_256x256"),
+    "bf16_4096x7168x16384": ("tile_nt_256x224", "tile_nt_256x224"),
+    "bf16_skinny_64x7168x7168": ("skinny_64x32", "skinny_64x128_splitk4"),
+    "fp8_4096x7168x16384": ("tile_fp8_256x128", "tile_fp8_256x128"),
 }
 
 
 # The plan for each shape of the benchmark's sweep (bf16, B stored N x K) and
-# for the boundaries of the small-grid rule: small grids (at most half the
-# CUs in 256 x 224 tiles) with K of at most 128 slices of 64 take 128 x 128
-# tiles (two-stage when there are more than 256 of them); with longer K,
-# 256 x 224 with split K; larger grids 256 x 224 or 256 x 256 by wave
-# quantisation.
+# for the boundaries of the small-grid rule, without and with a workspace:
+# small grids (at most half the CUs in 256 x 224 tiles) take 128 x 128 tiles
+# (two-stage when there are more than 256 of them), with K split when a
+# workspace is given and K is at most 128 slices of 64; with longer K and a
+# workspace, 256 x 224 with split K; larger grids 256 x 224 or 256 x 256 by
+# wave quantisation, and with a workspace a partial second wave of 256 x 224
+# tiles may be split over K.
 SWEEP_PLANS = [
-    (4096, 7168, 7168, "tile_nt_256x224"),
-    (4096, 896, 16384, "tile_nt_256x224_splitk4"),
-    (1024, 1024, 4096, "tile_nt_128x128_splitk4"),
-    (2048, 2048, 2048, "tile_nt_128x128"),
-    (8192, 8192, 8192, "tile_nt_256x256"),
-    (2048, 7168, 16384, "tile_nt_256x224"),
-    (1024, 1024, 8192, "tile_nt_128x128_splitk4"),
-    (1024, 1024, 8200, "tile_nt_256x224_splitk8"),
-    (2048, 2048, 8192, "tile_nt_128x128"),
-    (4096, 4096, 1024, "tile_nt_256x256"),
-    (4096, 1792, 4096, "tile_nt_128x128_2stage"),
-    (4096, 1024, 4096, "tile_nt_128x128"),
+    (4096, 7168, 7168, "tile_nt_256x224", "tile_nt_256x224"),
+    (4096, 896, 16384, "tile_nt_128x128", "tile_nt_256x224_splitk4"),
+    (1024, 1024, 4096, "tile_nt_128x128", "tile_nt_128x128_splitk4"),
+    (2048, 2048, 2048, "tile_nt_128x128", "tile_nt_128x128"),
+    (8192, 8192, 8192, "tile_nt_256x256", "tile_nt_256x256"),
+    (2048, 7168, 16384, "tile_nt_256x224", "tile_nt_256x224"),
+    (1024, 1024, 8192, "tile_nt_128x128", "tile_nt_128x128_splitk4"),
+    (1024, 1024, 8200, "tile_nt_128x128", "tile_nt_256x224_splitk8"),
+    (2048, 2048, 8192, "tile_nt_128x128", "tile_nt_128x128"),
+    (4096, 4096, 1024, "tile_nt_256x256", "tile_nt_256x256"),
+    (4096, 1792, 4096, "tile_nt_128x128_2stage", "tile_nt_128x128_2stage"),
+    (4096, 1024, 4096, "tile_nt_128x128", "tile_nt_128x128"),
     # one whole wave and a partial one: the partial wave's tiles split over K
-    (4352, 4096, 1024, "tile_nt_256x224_tail2"),
-    (4400, 4000, 2056, "tile_nt_256x224_tail3"),
-    (4300, 4000, 4104, "tile_nt_256x224_tail5"),
-    (4352, 4096, 4096, "tile_nt_256x224_tail3"),
-    (4352, 4096, 448, "tile_nt_256x224"),      # K too short to split
-    (6144, 6144, 2048, "tile_nt_256x224"),     # three waves: unsplit
+    (4352, 4096, 1024, "tile_nt_256x224", "tile_nt_256x224_tail2"),
+    (4400, 4000, 2056, "tile_nt_256x224", "tile_nt_256x224_tail3"),
+    (4300, 4000, 4104, "tile_nt_256x224", "tile_nt_256x224_tail5"),
+    (4352, 4096, 4096, "tile_nt_256x224", "tile_nt_256x224_tail3"),
+    (4352, 4096, 448, "tile_nt_256x224", "tile_nt_256x224"),      # K too short to split
+    (6144, 6144, 2048, "tile_nt_256x224", "tile_nt_256x224"),     # three waves: unsplit
 ]
+
+
+def _ws_bytes(op, M, N, K, sbk, sbn):
+    return tg.tg_gemm_workspace_size(op, M, N, K, PA, K, 1, PB, sbk, sbn, PC, N, 1)
 
 
 @pytest.mark.parametrize("case", SWEEP_PLANS, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SWEEP_PLANS])
 def test_sweep_plans(lib, case):
-    M, N, K, want = case
+    M, N, K, want, want_ws = case
     got = tg.tg_gemm_plan(tg.OP_BF16, M, N, K, PA, K, 1, PB, 1, K, PC, N, 1)
     assert got == want
+    need = _ws_bytes(tg.OP_BF16, M, N, K, 1, K)
+    assert (need > 0) == (want != want_ws)
+    args = (tg.OP_BF16, M, N, K, PA, K, 1, PB, 1, K, PC, N, 1)
+    assert tg.tg_gemm_plan_ws(*args, need) == want_ws
+    assert tg.tg_gemm_plan_ws(*args, 1 << 40) == want_ws
+    if need:
+        # one byte short of the split plan's scratch: the allocation-free plan
+        assert tg.tg_gemm_plan_ws(*args, need - 1) == want
+        assert tg.tg_gemm_plan_ws(*args, 0) == want
 
 
 @pytest.mark.parametrize("name", sorted(EXPECTED_PLANS))
@@ -321,5 +338,39 @@ def test_workload_plans(lib, name):
     w = configs.WORKLOADS[name]
     sbk, sbn = configs.b_strides(w.b_layout, w.N, w.K)
     op = {"f16": tg.OP_F16, "bf16": tg.OP_BF16, "fp8": tg.OP_FP8}[w.dtype]
-    got = tg.tg_gemm_plan(op, w.M, w.N, w.K, PA, w.K, 1, PB, sbk, sbn, PC, w.N, 1)
-    assert got == EXPECTED_PLANS[name]
+    args = (op, w.M, w.N, w.K, PA, w.K, 1, PB, sbk, sbn, PC, w.N, 1)
+    assert tg.tg_gemm_plan(*args) == EXPECTED_PLANS[name][0]
+    assert tg.tg_gemm_plan_ws(*args, _ws_bytes(op, w.M, w.N, w.K, sbk, sbn)) == \
+        EXPECTED_PLANS[name][1]
+
+
+def test_workspace_sizes(lib):
+    """The split plans' scratch: a 16 KiB counter area, then 4 bytes per
+    element of each split's partial tile."""
+    assert _ws_bytes(tg.OP_BF16, 64, 7168, 7168, 1, 7168) == 16384 + 56 * 4 * 64 * 128 * 4
+    assert _ws_bytes(tg.OP_BF16, 4096, 896, 16384, 1, 16384) == 16384 + 64 * 4 * 256 * 224 * 4
+    assert _ws_bytes(tg.OP_F16, 1024, 1024, 4096, 1, 4096) == 16384 + 64 * 4 * 128 * 128 * 4
+    assert _ws_bytes(tg.OP_BF16, 4352, 4096, 4096, 1, 4096) == 16384 + 67 * 3 * 256 * 224 * 4
+    assert _ws_bytes(tg.OP_BF16, 4096, 7168, 16384, 1, 16384) == 0
+    assert _ws_bytes(tg.OP_FP8, 64, 7168, 7168, 1, 7168) == 0
+    assert _ws_bytes(tg.OP_BF16, 0, 8, 8, 1, 8) == 0
+    with pytest.raises(tg.TgError):
+        _ws_bytes(tg.OP_BF16, -1, 8, 8, 1, 8)
+    with pytest.raises(tg.TgError):
+        _ws_bytes(5, 8, 8, 8, 1, 8)
+    out = ctypes.c_size_t(0)
+    assert lib.tg_gemm_workspace_size(1, 8, 8, 8, PA, 8, 1, PB, 1, 8, PC, 8, 1, None) == \
+        tg.TG_ERR_INVALID_VALUE
+    assert lib.tg_gemm_workspace_size(1, 8, 8, 8, PA, 8, 1, PB, 1, 8, PC, 8, 1,
+                                      ctypes.byref(out)) == tg.TG_SUCCESS and out.value == 0
+
+
+@pytest.mark.parametrize("name", ["tg_gemm_f16_ws", "tg_gemm_bf16_ws"])
+def test_workspace_invalid(lib, name):
+    fn = getattr(lib, name)
+    args = (64, 7168, 7168, PA, 7168, 1, PB, 1, 7168, PC, 7168, 1)
+    assert fn(*args, 0, 1 << 20, None) == tg.TG_ERR_INVALID_VALUE          # NULL workspace
+    assert fn(*args, PS + 16, 1 << 20, None) == tg.TG_ERR_INVALID_VALUE    # not 256-byte aligned
+    bad = (-1,) + args[1:]
+    assert fn(*bad, PS, 1 << 20, None) == tg.TG_ERR_INVALID_VALUE
+    assert fn(0, *args[1:], PS, 1 << 20, None) == tg.TG_SUCCESS             # no-op

@@ -70,10 +70,10 @@ def _layout_args(fmt, M, N, K, layout, seed, int_r=None):
     raise ValueError(layout)
 
 
-def _check16(fmt, M, N, K, layout, seed, int_r=None, scm=None):
+def _check16(fmt, M, N, K, layout, seed, int_r=None, scm=None, ws=None):
     A, sam, sak, B, sbk, sbn = _layout_args(fmt, M, N, K, layout, seed, int_r)
-    H.log(f"gemm {fmt} M={M} N={N} K={K} layout={layout} int_r={int_r} scm={scm}")
-    c, plan = H.run16(fmt, M, N, K, H.dev(A), sam, sak, H.dev(B), sbk, sbn, scm=scm)
+    H.log(f"gemm {fmt} M={M} N={N} K={K} layout={layout} int_r={int_r} scm={scm} ws={bool(ws)}")
+    c, plan = H.run16(fmt, M, N, K, H.dev(A), sam, sak, H.dev(B), sbk, sbn, scm=scm, ws=ws)
     C_ref, S = oracle.gemm(fmt, M, N, K, A, sam, sak, B, sbk, sbn)
     what = f"{fmt} {M}x{N}x{K} {layout} [{plan}]"
     if int_r:
@@ -135,10 +135,10 @@ def _wl_rows(w):
     return gen.sample_rows(w.M, w.check_rows, w.seed)
 
 
-def _run_workload16(w, d):
+def _run_workload16(w, d, ws=False):
     A, B = H.dev(d["A"]), H.dev(d["B"])
-    H.log(f"workload {w.name}: {w.M}x{w.N}x{w.K} layout={d['layout']}")
-    return H.run16(w.dtype, w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
+    H.log(f"workload {w.name}: {w.M}x{w.N}x{w.K} layout={d['layout']} ws={ws}")
+    return H.run16(w.dtype, w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"], ws=ws)
 
 
 def _oracle16(w, d, rows):
@@ -149,24 +149,30 @@ def _oracle16(w, d, rows):
 WL16 = [k for k in configs.ORDER if configs.WORKLOADS[k].dtype != "fp8"]
 
 
-@pytest.mark.parametrize("name", WL16)
-def test_workload_bound(name):
+# Each workload through the allocation-free entry point and, where it has a
+# split plan (the skinny product), through the workspace entry point too.
+WL16_CALLS = [(k, False) for k in WL16] + [("bf16_skinny_64x7168x7168", True)]
+WL16_IDS = [f"{k}{'-ws' if ws else ''}" for k, ws in WL16_CALLS]
+
+
+@pytest.mark.parametrize("name,ws", WL16_CALLS, ids=WL16_IDS)
+def test_workload_bound(name, ws):
     w = configs.WORKLOADS[name]
     d = configs.make_inputs(w)
-    c, plan = _run_workload16(w, d)
+    c, plan = _run_workload16(w, d, ws)
     rows = _wl_rows(w)
     C_ref, S = _oracle16(w, d, rows)
     H.assert_within_bound(w.dtype, c if rows is None else c[rows], C_ref, S, f"{name} [{plan}]")
 
 
-@pytest.mark.parametrize("name", WL16)
-def test_workload_bit_exact(name):
+@pytest.mark.parametrize("name,ws", WL16_CALLS, ids=WL16_IDS)
+def test_workload_bit_exact(name, ws):
     w = configs.WORKLOADS[name]
     r = int(math.sqrt(2 ** 24 / w.K))
     if w.dtype == "f16":
         r = min(r, 16)
     d = configs.make_inputs(w, int_r=r)
-    c, plan = _run_workload16(w, d)
+    c, plan = _run_workload16(w, d, ws)
     rows = _wl_rows(w)
     C_ref, _ = _oracle16(w, d, rows)
     H.assert_bit_exact(w.dtype, c if rows is None else c[rows], C_ref, f"{name} int r={r} [{plan}]")
@@ -303,14 +309,14 @@ SPLITK_CASES = [
 ]
 
 
-def _check16_rows(fmt, M, N, K, seed, int_r=None, extra_rows=()):
+def _check16_rows(fmt, M, N, K, seed, int_r=None, extra_rows=(), ws=None):
     """B stored N x K; the GPU result on sampled rows (and the last row, and
     `extra_rows`)."""
     draw = (lambda shape, st: gen.integers(shape, seed, st, int_r, fmt)) if int_r \
         else (lambda shape, st: gen.normal(shape, seed, st, fmt))
     A, B = draw((M, K), 0), draw((N, K), 1)
-    H.log(f"gemm {fmt} M={M} N={N} K={K} rows int_r={int_r}")
-    c, plan = H.run16(fmt, M, N, K, H.dev(A), K, 1, H.dev(B), 1, K)
+    H.log(f"gemm {fmt} M={M} N={N} K={K} rows int_r={int_r} ws={bool(ws)}")
+    c, plan = H.run16(fmt, M, N, K, H.dev(A), K, 1, H.dev(B), 1, K, ws=ws)
     rows = np.union1d(np.union1d(gen.sample_rows(M, 48, seed), [M - 1]),
                       np.asarray(extra_rows, dtype=np.int64))
     C_ref, S = oracle.gemm(fmt, M, N, K, A, K, 1, B, 1, K, rows=rows)
@@ -326,11 +332,14 @@ def _check16_rows(fmt, M, N, K, seed, int_r=None, extra_rows=()):
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_tile_nt_split_k(fmt, case):
     M, N, K, want = case
-    plan = _check16_rows(fmt, M, N, K, seed=1500 + M + N + K)
+    plan = _check16_rows(fmt, M, N, K, seed=1500 + M + N + K, ws=True)
     assert plan == want, plan
     r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
-    plan = _check16_rows(fmt, M, N, K, seed=1600 + M + N + K, int_r=r)
+    plan = _check16_rows(fmt, M, N, K, seed=1600 + M + N + K, int_r=r, ws=True)
     assert plan == want, plan
+    # the allocation-free plan of the same call (128 x 128 tiles, unsplit)
+    plan = _check16_rows(fmt, M, N, K, seed=1600 + M + N + K, int_r=r)
+    assert plan.startswith("tile_nt_128x128") and "split" not in plan, plan
 
 
 # (M, N, K, expected plan): grids of one whole wave (256 workgroups) of
@@ -347,11 +356,13 @@ TAIL_CASES = [
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_tile_nt_tail(fmt, case):
     M, N, K, want = case
-    plan = _check16(fmt, M, N, K, "nk", seed=1900 + M + N + K)
+    plan = _check16(fmt, M, N, K, "nk", seed=1900 + M + N + K, ws=True)
     assert plan == want, plan
     r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
-    plan = _check16(fmt, M, N, K, "nk", seed=2000 + M + N + K, int_r=r)
+    plan = _check16(fmt, M, N, K, "nk", seed=2000 + M + N + K, int_r=r, ws=True)
     assert plan == want, plan
+    plan = _check16(fmt, M, N, K, "nk", seed=2000 + M + N + K, int_r=r)
+    assert plan == "tile_nt_256x224", plan
 
 
 def test_tile_nt_tail5_rows():
@@ -360,9 +371,9 @@ def test_tile_nt_tail5_rows():
     bound and bit-exact."""
     M, N, K = 4300, 4000, 4104
     extra = list(range(3072, M, 37))
-    plan = _check16_rows("bf16", M, N, K, seed=2101, extra_rows=extra)
+    plan = _check16_rows("bf16", M, N, K, seed=2101, extra_rows=extra, ws=True)
     assert plan == "tile_nt_256x224_tail5", plan
-    plan = _check16_rows("bf16", M, N, K, seed=2102, int_r=63, extra_rows=extra)
+    plan = _check16_rows("bf16", M, N, K, seed=2102, int_r=63, extra_rows=extra, ws=True)
     assert plan == "tile_nt_256x224_tail5", plan
 
 
@@ -388,11 +399,14 @@ SPLITK128_CASES = [
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_tile_nt_128(fmt, case):
     M, N, K, want = case
-    plan = _check16(fmt, M, N, K, "nk", seed=1700 + M + N + K)
+    plan = _check16(fmt, M, N, K, "nk", seed=1700 + M + N + K, ws=True)
     assert plan == want, plan
     r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
-    plan = _check16(fmt, M, N, K, "nk", seed=1800 + M + N + K, int_r=r)
+    plan = _check16(fmt, M, N, K, "nk", seed=1800 + M + N + K, int_r=r, ws=True)
     assert plan == want, plan
+    if "split" in want:
+        plan = _check16(fmt, M, N, K, "nk", seed=1800 + M + N + K, int_r=r)
+        assert plan == "tile_nt_128x128", plan
 
 
 def test_split_k_shard_shape():
@@ -405,19 +419,25 @@ def test_split_k_shard_shape():
     d = configs.make_inputs(w)
     A, B = H.dev(d["A"]), H.dev(d["B"])
     H.log("split-K shard 4096x896x16384")
-    c1, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+    c1, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K, ws=True)
     assert plan == "tile_nt_256x224_splitk4", plan
     C_ref, S = oracle.gemm("bf16", M, N, K, d["A"], K, 1, d["B"], 1, K, rows=rows)
     H.assert_within_bound("bf16", c1[rows], C_ref, S, f"shard [{plan}]")
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        c2, _ = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+        c2, _ = H.run16("bf16", M, N, K, A, K, 1, B, 1, K, stream=s.cuda_stream, ws=True)
     torch.cuda.synchronize()
     assert np.array_equal(c1, c2)
+    c3, plan3 = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+    assert plan3 == "tile_nt_128x128", plan3
+    H.assert_within_bound("bf16", c3[rows], C_ref, S, f"shard [{plan3}]")
     d = configs.make_inputs(w, int_r=32)
-    c, _ = H.run16("bf16", M, N, K, H.dev(d["A"]), K, 1, H.dev(d["B"]), 1, K)
+    Ai, Bi = H.dev(d["A"]), H.dev(d["B"])
+    c, _ = H.run16("bf16", M, N, K, Ai, K, 1, Bi, 1, K, ws=True)
     C_ref, _ = oracle.gemm("bf16", M, N, K, d["A"], K, 1, d["B"], 1, K, rows=rows)
     H.assert_bit_exact("bf16", c[rows], C_ref, "shard int")
+    c4, _ = H.run16("bf16", M, N, K, Ai, K, 1, Bi, 1, K)
+    assert np.array_equal(c, c4), "split and unsplit plans differ on integer inputs"
 
 
 
@@ -433,36 +453,39 @@ def test_tail_after_split_k_and_repeatable():
     wt = configs.Workload("tail", "bf16", M, N, K, "nk", "normal_sqrtk", 8, 0)
     ds = configs.make_inputs(ws, int_r=16)
     dt = configs.make_inputs(wt, int_r=32)
-    H.log("split-K shard then partial-wave split, one stream")
+    H.log("split-K shard then partial-wave split, one stream, one workspace")
+    shared = H.Workspace(16384 + 64 * 4 * 256 * 224 * 4)
     _, plan = H.run16("bf16", 4096, 896, 16384, H.dev(ds["A"]), 16384, 1, H.dev(ds["B"]), 1,
-                      16384)
+                      16384, ws=shared)
     assert plan == "tile_nt_256x224_splitk4", plan
-    c, plan = H.run16("bf16", M, N, K, H.dev(dt["A"]), K, 1, H.dev(dt["B"]), 1, K)
+    c, plan = H.run16("bf16", M, N, K, H.dev(dt["A"]), K, 1, H.dev(dt["B"]), 1, K, ws=shared)
     assert plan == "tile_nt_256x224_tail3", plan
     C_ref, _ = oracle.gemm("bf16", M, N, K, dt["A"], K, 1, dt["B"], 1, K, rows=rows)
     H.assert_bit_exact("bf16", c[rows], C_ref, f"tail after split K [{plan}]")
     dn = configs.make_inputs(wt)
     A, B = H.dev(dn["A"]), H.dev(dn["B"])
-    c1, _ = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+    c1, _ = H.run16("bf16", M, N, K, A, K, 1, B, 1, K, ws=shared)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        c2, _ = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+        c2, _ = H.run16("bf16", M, N, K, A, K, 1, B, 1, K, stream=s.cuda_stream, ws=True)
     torch.cuda.synchronize()
     assert np.array_equal(c1, c2)
 
 
 def test_split_k_scratch_reused_by_more_tiles():
-    """Two split-K products in a row on one stream: 64 tiles of 256 x 224
-    split 4 ways (large partials, few counters), then 80 tiles split 3 ways,
-    which fits the same scratch.  The second call's counters for tiles 64..79 must not
+    """Two split-K products in a row on one stream and one workspace: 64
+    tiles of 256 x 224 split 4 ways (large partials, few counters), then 80
+    tiles split 3 ways, which fits the same workspace.  The second call's counters for tiles 64..79 must not
     start from the first call's partial data: bit-exact on integer inputs."""
     K = 8256
     s = torch.cuda.Stream()
+    shared = H.Workspace(16384 + 64 * 4 * 256 * 224 * 4)
     with torch.cuda.stream(s):
         M, N = 2048, 1792
         a, b = gen.normal((M, K), 71, 0, "bf16"), gen.normal((N, K), 71, 1, "bf16")
         H.log(f"split-K scratch reuse, first call {M}x{N}x{K}")
-        c, plan = H.run16("bf16", M, N, K, H.dev(a), K, 1, H.dev(b), 1, K)
+        c, plan = H.run16("bf16", M, N, K, H.dev(a), K, 1, H.dev(b), 1, K, stream=s.cuda_stream,
+                          ws=shared)
         assert plan == "tile_nt_256x224_splitk4", plan
         rows = gen.sample_rows(M, 128, 71)
         C_ref, S = oracle.gemm("bf16", M, N, K, a, K, 1, b, 1, K, rows=rows)
@@ -470,7 +493,8 @@ def test_split_k_scratch_reused_by_more_tiles():
         N = 2240
         a, b = gen.integers((M, K), 72, 0, 64, "bf16"), gen.integers((N, K), 72, 1, 64, "bf16")
         H.log(f"split-K scratch reuse, second call {M}x{N}x{K}")
-        c, plan = H.run16("bf16", M, N, K, H.dev(a), K, 1, H.dev(b), 1, K)
+        c, plan = H.run16("bf16", M, N, K, H.dev(a), K, 1, H.dev(b), 1, K, stream=s.cuda_stream,
+                          ws=shared)
         assert plan == "tile_nt_256x224_splitk3", plan
         rows = np.union1d(gen.sample_rows(M, 128, 72), np.arange(1024, 2048, 61))
         C_ref, _ = oracle.gemm("bf16", M, N, K, a, K, 1, b, 1, K, rows=rows)
@@ -479,170 +503,143 @@ def test_split_k_scratch_reused_by_more_tiles():
 
 # ------------------------------------------------------------ skinny kernel
 
-# (M, N, K): one split (short K) and split-K across workgroups (K of 16 or
+# (M, N, K): no split wanted (short K), and K split across workgroups with a
+# workspace / across the waves of 32-column strips without one (K of 16 or
 # more 64-wide slices), ragged N strips, K not a multiple of the slice.
 SKINNY_CASES = [(1, 100, 64), (17, 300, 200), (64, 64, 8), (64, 33, 1000), (40, 7168, 1024),
-                (63, 95, 4104), (64, 1000, 2056), (64, 7168, 520)]
-SKINNY = "skinny_64x128"
+                (63, 95, 4104), (64, 1000, 2056), (64, 7168, 520), (64, 7168, 7168)]
 
 
 @pytest.mark.parametrize("case", SKINNY_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SKINNY_CASES])
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_skinny(fmt, case):
     M, N, K = case
-    plan = _check16(fmt, M, N, K, "nk", seed=800 + M + N + K)
-    assert plan == SKINNY, plan
     r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
-    plan = _check16(fmt, M, N, K, "nk", seed=900 + M + N + K, int_r=r)
-    assert plan == SKINNY, plan
+    c_int = {}
+    for ws in (False, True):
+        plan = _check16(fmt, M, N, K, "nk", seed=800 + M + N + K, ws=ws)
+        assert plan.startswith("skinny_64x"), plan
+        if ws:
+            assert plan.startswith("skinny_64x128"), plan
+        plan = _check16(fmt, M, N, K, "nk", seed=900 + M + N + K, int_r=r, ws=ws)
+        assert plan.startswith("skinny_64x"), plan
+        A, sam, sak, B, sbk, sbn = _layout_args(fmt, M, N, K, "nk", 900 + M + N + K, r)
+        c_int[ws], _ = H.run16(fmt, M, N, K, H.dev(A), sam, sak, H.dev(B), sbk, sbn, ws=ws)
+    assert np.array_equal(c_int[False], c_int[True]), "skinny plans differ on integer inputs"
 
 
 def test_skinny_padded():
-    plan = _check16("bf16", 50, 70, 136, "padded", seed=41)
-    assert plan == SKINNY, plan
-    plan = _check16("bf16", 64, 300, 3000, "padded", seed=42)
-    assert plan == SKINNY, plan
+    for ws in (False, True):
+        plan = _check16("bf16", 50, 70, 136, "padded", seed=41, ws=ws)
+        assert plan.startswith("skinny_64x"), plan
+        plan = _check16("bf16", 64, 300, 3000, "padded", seed=42, ws=ws)
+        assert plan.startswith("skinny_64x"), plan
 
 
 def test_skinny_split_k_deterministic_and_per_stream():
     """The split-K combination adds the partial tiles in a fixed order: two
     runs agree bit for bit, on the default stream and on a second stream
-    (which has scratch of its own), with calls of other shapes in between."""
+    (with a workspace of its own), with calls of other shapes in between;
+    the allocation-free plan is repeatable too."""
     w = configs.WORKLOADS["bf16_skinny_64x7168x7168"]
     d = configs.make_inputs(w)
     A, B = H.dev(d["A"]), H.dev(d["B"])
     H.log("skinny determinism / second stream")
-    c1, plan = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
-    assert plan == SKINNY, plan
-    _check16("bf16", 64, 1000, 2056, "nk", seed=61)
+    ws1 = H.Workspace(16384 + 56 * 4 * 64 * 128 * 4)
+    c1, plan = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"], ws=ws1)
+    assert plan == "skinny_64x128_splitk4", plan
+    _check16("bf16", 64, 1000, 2056, "nk", seed=61, ws=ws1)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        c2, _ = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
+        c2, _ = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"],
+                        stream=s.cuda_stream, ws=True)
     torch.cuda.synchronize()
-    c3, _ = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
+    c3, _ = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"], ws=ws1)
     assert np.array_equal(c1, c2) and np.array_equal(c1, c3)
+    c4, plan4 = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
+    c5, _ = H.run16("bf16", w.M, w.N, w.K, A, w.K, 1, B, d["sbk"], d["sbn"])
+    assert plan4 == "skinny_64x32", plan4
+    assert np.array_equal(c4, c5)
 
 
-def _capture_skinny(stream, M, N, K, A, B, C):
+def _capture(stream, M, N, K, A, B, C, ws=None):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
-        st = H.tg.tg_gemm_bf16(M, N, K, A.data_ptr(), K, 1, B.data_ptr(), 1, K, C.data_ptr(), N, 1,
-                               stream.cuda_stream)
+        if ws is None:
+            H.tg.tg_gemm_bf16(M, N, K, A.data_ptr(), K, 1, B.data_ptr(), 1, K, C.data_ptr(), N, 1,
+                              stream.cuda_stream)
+        else:
+            H.tg.tg_gemm_bf16_ws(M, N, K, A.data_ptr(), K, 1, B.data_ptr(), 1, K, C.data_ptr(), N,
+                                 1, ws.ptr, ws.nbytes, stream.cuda_stream)
     return g
 
 
-def test_skinny_graph_capture():
-    """Under stream capture the skinny kernel allocates nothing: on a stream
-    without scratch it runs unsplit, on one that already has scratch it uses
-    it.  Both graphs, replayed several times with eager work in between,
-    give the eager result bit for bit (integer inputs: every split order
+def _graph_case(M, N, K, seed, want_ws, want_free):
+    """Graphs captured from the allocation-free entry point and from the
+    workspace one (its own workspace), replayed several times with eager
+    split-K work on another workspace in between, each replay checked
+    against the eager result bit for bit (integer inputs: every split order
     sums exactly)."""
-    M, N, K = 64, 2048, 4096
-    w = configs.Workload("t", "bf16", M, N, K, "nk", "normal", 77, 0)
-    d = configs.make_inputs(w, int_r=48)
-    A, B = H.dev(d["A"]), H.dev(d["B"])
-    H.log("skinny graph capture")
-    c_eager, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
-    assert plan == SKINNY, plan
-    C_ref, _ = oracle.gemm("bf16", M, N, K, d["A"], K, 1, d["B"], 1, K)
-    H.assert_bit_exact("bf16", c_eager, C_ref, "skinny eager")
-    fresh, warm = torch.cuda.Stream(), torch.cuda.Stream()
-    C1 = torch.zeros((M, N), dtype=torch.int16, device="cuda")
-    C2 = torch.zeros((M, N), dtype=torch.int16, device="cuda")
-    # give `warm` its scratch with an eager call first
-    with torch.cuda.stream(warm):
-        H.tg.tg_gemm_bf16(M, N, K, A.data_ptr(), K, 1, B.data_ptr(), 1, K, C2.data_ptr(), N, 1,
-                          warm.cuda_stream)
-    torch.cuda.synchronize()
-    g1 = _capture_skinny(fresh, M, N, K, A, B, C1)
-    g2 = _capture_skinny(warm, M, N, K, A, B, C2)
-    torch.cuda.synchronize()
-    for _ in range(3):
-        C1.zero_()
-        C2.zero_()
-        torch.cuda.synchronize()
-        g1.replay()
-        g2.replay()
-        torch.cuda.synchronize()
-        c1 = C1.cpu().numpy().view(np.uint16)
-        c2 = C2.cpu().numpy().view(np.uint16)
-        assert np.array_equal(c1, c_eager) and np.array_equal(c2, c_eager)
-
-
-def test_split_k_graph_capture():
-    """The split-K tile kernel under stream capture: on a stream without
-    scratch it runs unsplit, on one whose scratch is already large enough it
-    splits.  Replayed several times with eager work in between, both graphs
-    give the eager result bit for bit (integer inputs)."""
-    M, N, K = 1024, 1024, 4096
-    w = configs.Workload("t", "bf16", M, N, K, "nk", "normal", 78, 0)
+    w = configs.Workload("t", "bf16", M, N, K, "nk", "normal", seed, 0)
     d = configs.make_inputs(w, int_r=32)
     A, B = H.dev(d["A"]), H.dev(d["B"])
-    H.log("split-K graph capture")
-    c_eager, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
-    assert plan.startswith("tile_nt_128x128_splitk"), plan
+    c_eager, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K, ws=True)
+    assert plan == want_ws, plan
     C_ref, _ = oracle.gemm("bf16", M, N, K, d["A"], K, 1, d["B"], 1, K)
-    H.assert_bit_exact("bf16", c_eager, C_ref, "split-K eager")
-    fresh, warm = torch.cuda.Stream(), torch.cuda.Stream()
+    H.assert_bit_exact("bf16", c_eager, C_ref, f"eager [{plan}]")
+    c_free, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
+    assert plan == want_free, plan
+    assert np.array_equal(c_free, c_eager)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     C1 = torch.zeros((M, N), dtype=torch.int16, device="cuda")
     C2 = torch.zeros((M, N), dtype=torch.int16, device="cuda")
-    with torch.cuda.stream(warm):
-        H.tg.tg_gemm_bf16(M, N, K, A.data_ptr(), K, 1, B.data_ptr(), 1, K, C2.data_ptr(), N, 1,
-                          warm.cuda_stream)
+    gws = H.Workspace(H.tg.tg_gemm_workspace_size(H.tg.OP_BF16, M, N, K, A.data_ptr(), K, 1,
+                                                  B.data_ptr(), 1, K, C2.data_ptr(), N, 1))
     torch.cuda.synchronize()
-    g1 = _capture_skinny(fresh, M, N, K, A, B, C1)
-    g2 = _capture_skinny(warm, M, N, K, A, B, C2)
+    g1 = _capture(s1, M, N, K, A, B, C1)
+    g2 = _capture(s2, M, N, K, A, B, C2, gws)
     torch.cuda.synchronize()
+    other = H.Workspace(gws.nbytes)
     for _ in range(3):
         C1.zero_()
         C2.zero_()
-        H.run16("bf16", 300, 500, 4096, A, K, 1, B, 1, K)   # eager split-K work in between
+        H.run16("bf16", M, N, K, A, K, 1, B, 1, K, ws=other)   # eager split-K work in between
         torch.cuda.synchronize()
         g1.replay()
         g2.replay()
         torch.cuda.synchronize()
         assert np.array_equal(C1.cpu().numpy().view(np.uint16), c_eager)
         assert np.array_equal(C2.cpu().numpy().view(np.uint16), c_eager)
+        assert gws.counters_zero()
 
 
+def test_skinny_graph_capture():
+    H.log("skinny graph capture")
+    _graph_case(64, 2048, 4096, 77, "skinny_64x128_splitk4", "skinny_64x32")
 
-def test_split_k_graph_survives_scratch_growth():
-    """A graph captured with split K on a stream whose scratch exists keeps
-    working after a larger split-K call on that stream has grown the
-    scratch: the outgrown buffer stays allocated.  Replays give the eager
-    result bit for bit (integer inputs)."""
-    M, N, K = 1024, 1024, 4096
+
+def test_split_k_graph_capture():
+    H.log("split-K graph capture")
+    _graph_case(1024, 1024, 4096, 78, "tile_nt_128x128_splitk4", "tile_nt_128x128")
+
+
+def test_workspace_short_runs_allocation_free_plan():
+    """A workspace one byte short of the split plan's need: the call runs the
+    allocation-free plan and leaves the workspace untouched."""
+    M, N, K = 64, 2048, 4096
     w = configs.Workload("t", "bf16", M, N, K, "nk", "normal", 79, 0)
     d = configs.make_inputs(w, int_r=32)
     A, B = H.dev(d["A"]), H.dev(d["B"])
-    H.log("split-K graph across scratch growth")
-    c_eager, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K)
-    assert plan.startswith("tile_nt_128x128_splitk"), plan
-    warm = torch.cuda.Stream()
-    C = torch.zeros((M, N), dtype=torch.int16, device="cuda")
-    with torch.cuda.stream(warm):
-        H.tg.tg_gemm_bf16(M, N, K, A.data_ptr(), K, 1, B.data_ptr(), 1, K, C.data_ptr(), N, 1,
-                          warm.cuda_stream)
-    torch.cuda.synchronize()
-    g = _capture_skinny(warm, M, N, K, A, B, C)
-    torch.cuda.synchronize()
-    # a split-K call with much larger partials on the same stream grows its scratch
-    Mb, Nb, Kb = 4096, 896, 16384
-    wb = configs.Workload("shard", "bf16", Mb, Nb, Kb, "nk", "normal", 80, 0)
-    db = configs.make_inputs(wb, int_r=32)
-    Ab, Bb = H.dev(db["A"]), H.dev(db["B"])
-    with torch.cuda.stream(warm):
-        cb, plan_b = H.run16("bf16", Mb, Nb, Kb, Ab, Kb, 1, Bb, 1, Kb, stream=warm.cuda_stream)
-    assert plan_b == "tile_nt_256x224_splitk4", plan_b
-    rows = gen.sample_rows(Mb, 32, 80)
-    C_ref, _ = oracle.gemm("bf16", Mb, Nb, Kb, db["A"], Kb, 1, db["B"], 1, Kb, rows=rows)
-    H.assert_bit_exact("bf16", cb[rows], C_ref, "grown scratch")
-    for _ in range(3):
-        C.zero_()
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        assert np.array_equal(C.cpu().numpy().view(np.uint16), c_eager)
+    need = H.tg.tg_gemm_workspace_size(H.tg.OP_BF16, M, N, K, A.data_ptr(), K, 1, B.data_ptr(),
+                                       1, K, A.data_ptr(), N, 1)
+    short = H.Workspace(need - 1)
+    short.buf.fill_(0)
+    H.log("workspace one byte short")
+    c, plan = H.run16("bf16", M, N, K, A, K, 1, B, 1, K, ws=short)
+    assert plan == "skinny_64x32", plan
+    assert int(short.buf.count_nonzero().item()) == 0
+    C_ref, _ = oracle.gemm("bf16", M, N, K, d["A"], K, 1, d["B"], 1, K)
+    H.assert_bit_exact("bf16", c, C_ref, "short workspace")
 
 # ------------------------------------------------------ K x N tile kernel
 
