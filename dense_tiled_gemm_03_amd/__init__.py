@@ -16,13 +16,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtg_gemm.so")
 
 TG_SUCCESS, TG_ERR_INVALID_VALUE, TG_ERR_UNSUPPORTED, TG_ERR_LAUNCH = 0, 1, 2, 3
+TG_ERR_SCRATCH_LIMIT = 4
 OP_F16, OP_BF16, OP_FP8 = 0, 1, 2
 EXPORTS = ("tg_status_string", "tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8_blockscaled",
            "tg_gemm_plan", "tg_quant_fp8_1x128", "tg_quant_fp8_128x128", "tg_gemm_grouped_f16",
            "tg_gemm_grouped_bf16", "tg_gemm_grouped_plan", "tg_gemm_grouped_fp8_blockscaled",
            "tg_gemm_grouped_fp8_plan", "tg_gemm_f16_quant_fp8", "tg_gemm_bf16_quant_fp8",
            "tg_gemm_quant_fp8_plan", "tg_gemm_f16_ws", "tg_gemm_bf16_ws", "tg_gemm_workspace_size",
-           "tg_gemm_plan_ws")
+           "tg_gemm_plan_ws", "tg_gemm_bf16_static_scratch")
 
 
 class TgError(RuntimeError):
@@ -59,6 +60,8 @@ def load():
     for name in ("tg_gemm_f16_ws", "tg_gemm_bf16_ws"):
         getattr(lib, name).argtypes = sig16[:-1] + [vp, sz, vp]
         getattr(lib, name).restype = c_int
+    lib.tg_gemm_bf16_static_scratch.argtypes = sig16
+    lib.tg_gemm_bf16_static_scratch.restype = c_int
     lib.tg_gemm_workspace_size.argtypes = [c_int, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp,
                                            i64, i64, ctypes.POINTER(sz)]
     lib.tg_gemm_workspace_size.restype = c_int
@@ -125,6 +128,11 @@ def tg_gemm_bf16_ws(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, workspace, w
                     stream=0):
     return _check(load().tg_gemm_bf16_ws(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn,
                                          workspace, workspace_bytes, stream))
+
+
+def tg_gemm_bf16_static_scratch(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, stream=0):
+    return _check(load().tg_gemm_bf16_static_scratch(M, N, K, A, sam, sak, B, sbk, sbn, C, scm,
+                                                     scn, stream))
 
 
 def tg_gemm_workspace_size(op, M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn):

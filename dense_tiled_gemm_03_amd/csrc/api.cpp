@@ -138,6 +138,9 @@ const char* tg_status_string(tg_status s) {
     case TG_ERR_INVALID_VALUE: return "TG_ERR_INVALID_VALUE: invalid argument";
     case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED: unsupported layout or size";
     case TG_ERR_LAUNCH: return "TG_ERR_LAUNCH: kernel launch failed";
+    case TG_ERR_SCRATCH_LIMIT:
+      return "TG_ERR_SCRATCH_LIMIT: the call's split plan needs more scratch than the fixed "
+             "64 MiB array holds";
     default: return "unknown tg_status";
   }
 }

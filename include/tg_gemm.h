@@ -64,7 +64,8 @@ enum {
   TG_SUCCESS = 0,
   TG_ERR_INVALID_VALUE = 1,
   TG_ERR_UNSUPPORTED = 2,
-  TG_ERR_LAUNCH = 3
+  TG_ERR_LAUNCH = 3,
+  TG_ERR_SCRATCH_LIMIT = 4
 };
 
 /* A hipStream_t, passed as an opaque pointer; NULL = the null stream. */
@@ -158,6 +159,27 @@ tg_status tg_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K,
                                  const void* A, int64_t sam, int64_t sak,
                                  const void* B, int64_t sbk, int64_t sbn,
                                  void* C, int64_t scm, int64_t scn, size_t* bytes);
+
+/* For callers that cannot allocate device memory at all (code under HIP
+ * graph capture that may not create buffers, tight serving loops, harnesses
+ * that forbid allocation): tg_gemm_bf16_ws with its workspace taken from a
+ * fixed 64 MiB device array inside the library instead of a caller's
+ * buffer.  Same arguments, plans and results as tg_gemm_bf16_ws given 64 MiB
+ * of workspace (that covers every split plan of the skinny and tile kernels
+ * except partial-wave splits of many tiles).  The array is a file-scope
+ * device variable: each GPU the library runs on holds its own copy until the
+ * process ends; the first call on a device looks up that copy's address and
+ * clears its counters (a small kernel on `stream`).  Every call on one GPU
+ * shares that GPU's array: calls whose work may overlap in time on one GPU
+ * (different streams, concurrent graph replays) race on it and give
+ * undefined results.  Nothing is allocated.  Errors: those of
+ * tg_gemm_bf16_ws; TG_ERR_SCRATCH_LIMIT, with no side effects, when the
+ * call's split plan needs more than 64 MiB (tg_gemm_workspace_size), and
+ * TG_ERR_LAUNCH when the array's address cannot be had. */
+tg_status tg_gemm_bf16_static_scratch(int64_t M, int64_t N, int64_t K,
+                                      const void* A, int64_t sam, int64_t sak,
+                                      const void* B, int64_t sbk, int64_t sbn,
+                                      void* C, int64_t scm, int64_t scn, tg_stream_t stream);
 
 /* Grouped product: G independent products sharing N and K, group g with its
  * own row count -- the grouped GEMM of the TileLang examples ("Getting to

@@ -37,7 +37,7 @@ def test_exports_every_declared_function(lib):
 
 def test_status_strings(lib):
     for code, tag in ((0, "TG_SUCCESS"), (1, "TG_ERR_INVALID_VALUE"), (2, "TG_ERR_UNSUPPORTED"),
-                      (3, "TG_ERR_LAUNCH")):
+                      (3, "TG_ERR_LAUNCH"), (4, "TG_ERR_SCRATCH_LIMIT")):
         assert tg.tg_status_string(code).startswith(tag)
     assert "unknown" in tg.tg_status_string(99)
 
@@ -374,3 +374,18 @@ def test_workspace_invalid(lib, name):
     bad = (-1,) + args[1:]
     assert fn(*bad, PS, 1 << 20, None) == tg.TG_ERR_INVALID_VALUE
     assert fn(0, *args[1:], PS, 1 << 20, None) == tg.TG_SUCCESS             # no-op
+
+
+def test_static_scratch_host_checks(lib):
+    """The fixed-scratch entry point validates and sizes on the host before
+    any HIP call: invalid arguments, a split plan larger than its 64 MiB
+    array (4096 x 4896 x 4096: 96 tiles past the first wave split 5 ways,
+    105 MiB) and empty calls return without touching the device."""
+    fn = lib.tg_gemm_bf16_static_scratch
+    assert fn(4096, 4896, 4096, PA, 4096, 1, PB, 1, 4096, PC, 4896, 1, None) == \
+        tg.TG_ERR_SCRATCH_LIMIT
+    assert tg.tg_gemm_workspace_size(tg.OP_BF16, 4096, 4896, 4096, PA, 4096, 1, PB, 1, 4096, PC,
+                                     4896, 1) > 64 << 20
+    assert fn(-1, 8, 8, PA, 8, 1, PB, 1, 8, PC, 8, 1, None) == tg.TG_ERR_INVALID_VALUE
+    assert fn(8, 8, 8, PA, 8, 1, PB, 1, 8, PC, 8, 2, None) == tg.TG_ERR_UNSUPPORTED
+    assert fn(0, 8, 8, PA, 8, 1, PB, 1, 8, PC, 8, 1, None) == tg.TG_SUCCESS
