@@ -615,7 +615,7 @@ def _graph_case(M, N, K, seed, want_ws, want_free):
 
 def test_skinny_graph_capture():
     H.log("skinny graph capture")
-    _graph_case(64, 2048, 4096, 77, "skinny_64x128_splitk4", "skinny_64x32")
+    _graph_case(64, 2048, 4096, 77, "skinny_64x128_splitk8", "skinny_64x32")
 
 
 def test_split_k_graph_capture():
