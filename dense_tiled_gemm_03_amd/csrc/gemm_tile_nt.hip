@@ -7,6 +7,7 @@
 // of 256 x 224, each split 4 ways).  Grids of one whole wave and a partial
 // one may split only the partial wave's tiles.
 #include "tile_mfma.hpp"
+#include "tile_pp.hpp"
 
 namespace tg {
 namespace {
@@ -21,6 +22,9 @@ typedef tile::Tile<256, 256, Mfma32> Tile256;  // wave tile 128 x 128, 32x32x16 
 // per CU) for larger grids
 typedef tile::Tile<128, 128, Mfma16, 3, 3> Tile128;
 typedef tile::Tile<128, 128, Mfma16, 2, 2> Tile128x2;
+// unsplit 256 x 224 and 256 x 256 tiles run the eight-wave ping-pong form
+typedef tile::PPTile<224> PP224;
+typedef tile::PPTile<256> PP256;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // Both operands K-contiguous with 16-byte aligned rows; offsets inside one
@@ -179,11 +183,25 @@ hipError_t launch_cfg(Op op, const GemmArgs& a, const Plan& p, const Scratch& ws
       return hipGetLastError();
     }
   }
-  const dim3 grid(tm * tn), block(256);
-  if (op == Op::BF16)
-    hipLaunchKernelGGL((tile::gemm16_tile<__bf16, Cfg, false>), grid, block, 0, s, a, tm, tn);
-  else
-    hipLaunchKernelGGL((tile::gemm16_tile<_Float16, Cfg, false>), grid, block, 0, s, a, tm, tn);
+  const dim3 grid(tm * tn);
+  if constexpr (std::is_same<Cfg, Tile224>::value || std::is_same<Cfg, Tile256>::value) {
+    // whole-K tiles of the large shapes: eight waves, two per SIMD taking
+    // turns at the matrix core (measured in one process on 4096 x 7168 x
+    // 16384: 637 us against 693 for the four-wave 256 x 224 kernel; 8192^3:
+    // 694 us against 803 for the four-wave 256 x 256 kernel; bit-identical)
+    typedef typename std::conditional<std::is_same<Cfg, Tile224>::value, PP224, PP256>::type PP;
+    if (op == Op::BF16)
+      hipLaunchKernelGGL((tile::gemm16_pp<__bf16, PP>), grid, dim3(512), 0, s, a, tm, tn);
+    else
+      hipLaunchKernelGGL((tile::gemm16_pp<_Float16, PP>), grid, dim3(512), 0, s, a, tm, tn);
+  } else {
+    if (op == Op::BF16)
+      hipLaunchKernelGGL((tile::gemm16_tile<__bf16, Cfg, false>), grid, dim3(256), 0, s, a, tm,
+                         tn);
+    else
+      hipLaunchKernelGGL((tile::gemm16_tile<_Float16, Cfg, false>), grid, dim3(256), 0, s, a, tm,
+                         tn);
+  }
   return hipGetLastError();
 }
 

@@ -1,0 +1,234 @@
+#pragma once
+// Eight-wave "ping-pong" form of the N x K tile kernel (A row-major M x K,
+// B stored N x K, both K-contiguous): the same tile loop as tile_body in
+// tile_mfma.hpp ("TileKernels deep dive" section 3.1; the first-GEMM listing
+// of "Getting to know TileLang": one output tile per workgroup, operand
+// tiles staged per K slice in a multi-stage pipeline, an fp32 accumulator
+// cast to C once), with the work of each SIMD split between two waves that
+// take turns:
+//  - workgroup tile 256 x BN (BN = 224), 512 threads: waves 0-3 (group 0,
+//    one per SIMD) own columns 0 .. BN/2 - 1 of the tile, waves 4-7 (group
+//    1) the other half; wave q of a group owns rows 64q .. 64q + 63, i.e. a
+//    64 x BN/2 block of fp32 accumulators (4 x 7 blocks of 16x16x32 MFMAs);
+//  - time runs in intervals separated by workgroup barriers.  In each
+//    interval one group multiplies a whole 64-wide K slice from registers
+//    (56 MFMAs per wave, nothing else) while the other group reads the next
+//    slice's fragments from LDS (22 ds_read_b128) and issues its share of
+//    the LDS-direct loads of a later slice; the groups swap every interval
+//    (group 1 runs one interval behind group 0), so each SIMD's matrix core
+//    always has one wave with MFMAs to issue while the other waits on LDS,
+//    memory or the barrier;
+//  - LDS: the rings of the one-group kernel -- two stages of A (the tile's
+//    256 rows, 128 bytes of k per row) and three of B -- with the same chunk
+//    swizzle c ^ ((r >> 1) & 7) (conflict-free 16x16x32 fragment reads);
+//    group 0 loads every A stage, one slice ahead of its use, group 1 every
+//    B stage, two slices ahead;
+//  - edges, descriptors, tile order and the epilogue as in tile_body.
+//
+// Interval t follows barrier t.  Group 0 reads slice j in interval 2j and
+// multiplies it in 2j + 1; group 1 reads it in 2j + 1 and multiplies it in
+// 2j + 2.  Slice j's stages are therefore free after barrier 2j + 2, which
+// is when group 0 (interval 2j + 2) refills A stage j with slice j + 2 and
+// group 1 (interval 2j + 3) refills B stage j with slice j + 3.  Before the
+// barrier that precedes group 0's reads of slice j + 1 (barrier 2j + 2),
+// group 0 waits for all its loads (A of slice j + 1) and group 1 for all
+// but the last slice's (B of slice j + 1 done, j + 2 in flight).  Each
+// group passes 2 nk + 1 barriers.
+#include "tile_mfma.hpp"
+
+namespace tg {
+namespace tile {
+
+template <int BN_>
+struct PPTile {
+  static constexpr int BM = 256, BN = BN_, BK = 64;
+  static constexpr int WTM = 64, WTN = BN / 2;         // wave tile
+  static constexpr int FM = WTM / 16, FN = WTN / 16;   // 16x16 blocks per wave
+  static constexpr int SUBS = 2;                       // k32 sub-steps per slice
+  static constexpr int ROW_BYTES = 128;
+  static constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
+  static constexpr int A_ST = 2, B_ST = 3;
+  static constexpr int LDS_BYTES = A_ST * A_BYTES + B_ST * B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024 / 4;  // per wave of group 0
+  static constexpr int B_LOADS = B_BYTES / 1024 / 4;  // per wave of group 1
+  static constexpr int GM = 4;
+  static_assert(WTN % 16 == 0, "wave tile columns in whole 16x16 blocks");
+  static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole loads per wave");
+  static_assert(LDS_BYTES <= 160 * 1024, "stages must fit the LDS");
+};
+
+template <typename T, typename Cfg>
+__device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn) {
+  typedef typename Elem<T>::x8 T8;
+  typedef f32x4 Acc;
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, SUBS = Cfg::SUBS;
+  constexpr int A_ST = Cfg::A_ST, B_ST = Cfg::B_ST;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  auto a_off = [](int s) { return s * Cfg::A_BYTES; };
+  auto b_off = [](int s) { return A_ST * Cfg::A_BYTES + s * Cfg::B_BYTES; };
+  const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = w >> 2, q = w & 3;  // group, wave within the group (its SIMD)
+  const int K = (int)a.K;
+  const int nk = (K + BK - 1) / BK;
+  const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
+
+  const int rows_a = (int)min<int64_t>(BM, a.M - m0), rows_b = (int)min<int64_t>(BN, a.N - n0);
+  const T* Ab = static_cast<const T*>(a.A) + m0 * a.sam;
+  const T* Bb = static_cast<const T*>(a.B) + n0 * a.sbn;
+  const i32x4 ra = make_desc(Ab, (uint32_t)(((rows_a - 1) * lda + K) * 2));
+  const i32x4 rb = make_desc(Bb, (uint32_t)(((rows_b - 1) * ldb + K) * 2));
+
+  // Loads: wave q's i-th load of a stage fills its rows 8 (4i + q) .. + 7;
+  // lane l writes row 8 (4i + q) + (l >> 3) at chunk position l & 7, i.e.
+  // logical chunk (l & 7) ^ (4 (q & 1) + (l >> 4)).
+  const int lrow = 8 * q + (lane >> 3);
+  const int lchunk = (lane & 7) ^ (4 * (q & 1) + (lane >> 4));
+  const uint32_t ld = g == 0 ? lda : ldb;
+  const uint32_t l_lane = (uint32_t)lrow * ld * 2 + 16 * lchunk;
+  const uint32_t l_step = 32 * ld * 2;
+  auto load_a = [&](int slot, int k0) {
+    const bool kin = k0 + 8 * lchunk < K;
+    const uint32_t base = lds32 + a_off(slot) + q * 1024;
+#pragma unroll
+    for (int i = 0; i < Cfg::A_LOADS; ++i)
+      load_lds16(ra, base + i * 4096, kin ? l_lane + i * l_step + 2 * k0 : kOutOfRange);
+  };
+  auto load_b = [&](int slot, int k0) {
+    const bool kin = k0 + 8 * lchunk < K;
+    const uint32_t base = lds32 + b_off(slot) + q * 1024;
+#pragma unroll
+    for (int i = 0; i < Cfg::B_LOADS; ++i)
+      load_lds16(rb, base + i * 4096, kin ? l_lane + i * l_step + 2 * k0 : kOutOfRange);
+  };
+
+  // Fragment reads (16x16x32): row (16-aligned base) + (l % 16), chunk
+  // 4 s + l / 16 of the slice for sub-step s, at position chunk ^ ((l >> 1) & 7).
+  const int sw = (lane >> 1) & 7;
+  const int a_rd = (q * Cfg::WTM + (lane & 15)) * Cfg::ROW_BYTES;
+  const int b_rd = (g * Cfg::WTN + (lane & 15)) * Cfg::ROW_BYTES;
+  int ch[SUBS];
+#pragma unroll
+  for (int s = 0; s < SUBS; ++s) ch[s] = ((4 * s + (lane >> 4)) ^ sw) * 16;
+
+  Acc acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0.0f, 0.0f, 0.0f, 0.0f};
+  T8 fa[SUBS][FM], fb[SUBS][FN];
+  auto read_slice = [&](int sa, int sb) {
+    const char* ab = lds + a_off(sa) + a_rd;
+    const char* bb = lds + b_off(sb) + b_rd;
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[s][i] = *reinterpret_cast<const T8*>(ab + i * 16 * Cfg::ROW_BYTES + ch[s]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[s][j] = *reinterpret_cast<const T8*>(bb + j * 16 * Cfg::ROW_BYTES + ch[s]);
+    }
+  };
+  auto multiply = [&]() {
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(fa[s][i], fb[s][j], acc[i][j]);
+  };
+  // Workgroup barrier; the scheduling fences keep the compiler from moving
+  // MFMAs or reads across it (the phases must stay whole).
+  auto barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto wait_lds = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
+  if (g == 0) {
+    load_a(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier();                                   // 0
+    int sa = 0, sb = 0;
+    for (int j = 0; j < nk; ++j) {
+      const int na = sa + 1 == A_ST ? 0 : sa + 1;
+      load_a(na, (j + 1) * BK);                  // slice j + 1 into slice j - 1's stage
+      read_slice(sa, sb);
+      wait_lds();
+      barrier();                                 // 2j + 1
+      multiply();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      barrier();                                 // 2j + 2
+      sa = na;
+      sb = sb + 1 == B_ST ? 0 : sb + 1;
+    }
+  } else {
+    load_b(0, 0);
+    load_b(1, BK);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Cfg::B_LOADS) : "memory");
+    barrier();                                   // 0
+    barrier();                                   // 1
+    int sa = 0, sb = 0;
+    for (int j = 0; j < nk; ++j) {
+      const int nb2 = sb == 0 ? 2 : sb - 1;      // (j + 2) mod 3: slice j - 1's stage
+      load_b(nb2, (j + 2) * BK);
+      read_slice(sa, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(Cfg::B_LOADS) : "memory");
+      barrier();                                 // 2j + 2
+      multiply();
+      if (j + 1 < nk) barrier();                 // 2j + 3
+      sa = sa + 1 == A_ST ? 0 : sa + 1;
+      sb = sb + 1 == B_ST ? 0 : sb + 1;
+    }
+    // the last B loads (slices past K, zeros) land before the LDS is released
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  // Epilogue: round each accumulator to the output type and store it inside
+  // M x N (lane l holds column l % 16, rows 4 (l / 16) + v of each block).
+  T* C = static_cast<T*>(a.C);
+  const int64_t row0 = m0 + q * Cfg::WTM + 4 * (lane >> 4);
+  const int64_t col0 = n0 + g * Cfg::WTN + (lane & 15);
+  if (m0 + BM <= a.M && n0 + BN <= a.N) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          C[(row0 + i * 16 + v) * a.scm + col0 + j * 16] = to_out<T>(acc[i][j][v]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t row = row0 + i * 16 + v, col = col0 + j * 16;
+          if (row < a.M && col < a.N) C[row * a.scm + col] = to_out<T>(acc[i][j][v]);
+        }
+  }
+}
+
+template <typename T, typename Cfg>
+__global__ __launch_bounds__(512) void gemm16_pp(GemmArgs a, int tiles_m, int tiles_n) {
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
+  pp_body<T, Cfg>(a, tm, tn);
+}
+
+}  // namespace tile
+}  // namespace tg
