@@ -11,18 +11,21 @@
 // group by group (a group of M_g rows has ceil(M_g / BM) * ceil(N / BN)
 // tiles), each workgroup finds its group in a table of first tile ids passed
 // with the kernel arguments, re-bases A, B_g and C on the group and runs the
-// N x K tile kernel's K loop and epilogue on its tile.  Calls the tile
+// N x K tile kernel's K loop and epilogue (its eight-wave form) on its tile.  Calls the tile
 // kernel does not take (strides, alignment, more than kMaxGroups groups) run
 // group by group through tg_gemm_f16 / tg_gemm_bf16.
 #include "../../include/tg_gemm.h"
 
 #include "tile_mfma.hpp"
+#include "tile_pp.hpp"
 
 namespace tg {
 namespace {
 
+// One group tile per workgroup, in the eight-wave ping-pong form of the
+// N x K tile kernel (tile_pp.hpp).
 template <typename T, typename Cfg>
-__global__ __launch_bounds__(256) void gemm16_grouped(GemmArgs a, GroupTable gt) {
+__global__ __launch_bounds__(512) void gemm16_grouped(GemmArgs a, GroupTable gt) {
   int g, tm, tn;
   tile::group_coords(gt, Cfg::BM, Cfg::GM, g, tm, tn);
   const int64_t rows = gt.row0[g + 1] - gt.row0[g];
@@ -31,11 +34,11 @@ __global__ __launch_bounds__(256) void gemm16_grouped(GemmArgs a, GroupTable gt)
   ag.A = static_cast<const T*>(a.A) + gt.row0[g] * a.sam;
   ag.B = static_cast<const T*>(a.B) + g * gt.sbg;
   ag.C = static_cast<T*>(a.C) + gt.row0[g] * a.scm;
-  tile::tile_body<T, Cfg, false>(ag, tm, tn);
+  tile::pp_body<T, Cfg>(ag, tm, tn);
 }
 
-typedef tile::Tile<256, 224, tile::Mfma16, 2, 3> Tile224;  // B one stage deeper than A
-typedef tile::Tile<256, 256, tile::Mfma32> Tile256;
+typedef tile::PPTile<224> Tile224;
+typedef tile::PPTile<256> Tile256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -125,7 +128,7 @@ tg_status launch_grouped(const Call& c, hipStream_t s) {
                    static_cast<const T*>(c.A) + c.off[0] * c.lda, c.lda, 1, c.B, 1, c.ldb,
                    nullptr, 0, 0, nullptr, 0, 0,
                    static_cast<T*>(c.C) + c.off[0] * c.ldc, c.ldc};
-  hipLaunchKernelGGL((gemm16_grouped<T, Cfg>), dim3((unsigned)tiles), dim3(256), 0, s, a, gt);
+  hipLaunchKernelGGL((gemm16_grouped<T, Cfg>), dim3((unsigned)tiles), dim3(512), 0, s, a, gt);
   return hipGetLastError() == hipSuccess ? TG_SUCCESS : TG_ERR_LAUNCH;
 }
 

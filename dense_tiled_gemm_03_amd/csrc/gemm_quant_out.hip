@@ -9,13 +9,16 @@
 // result).  Per slice the arithmetic is that of tg_quant_fp8_1x128
 // (fp8_codec.hpp) applied to the fp32 product.
 //
-// Kernels: the 256 x 256 tile kernel (B stored N x K or K x N) with the
-// quantising epilogue -- each wave's 128 columns are one slice, so a row's
-// maximum is a reduction inside one wave -- and, for every call those do
-// not take, a fully masked kernel with one 32 x 128 tile per workgroup.
+// Kernels: the 256 x 256 tile kernels with the quantising epilogue -- the
+// eight-wave ping-pong form for B stored N x K (64 x 128 per wave), the
+// four-wave form for B stored K x N (128 x 128 per wave); each wave's 128
+// columns are one slice, so a row's maximum is a reduction inside one wave
+// -- and, for every call those do not take, a fully masked kernel with one
+// 32 x 128 tile per workgroup.
 #include "../../include/tg_gemm.h"
 
 #include "tile_mfma.hpp"
+#include "tile_pp.hpp"
 
 namespace tg {
 namespace {
@@ -139,7 +142,9 @@ hipError_t launch_t(const Call& c, Path p, hipStream_t s) {
   }
   const int tm = (int)cdiv(a.M, Tile256::BM), tn = (int)cdiv(a.N, Tile256::BN);
   if (p == Path::TileNT)
-    hipLaunchKernelGGL((tile::gemm16_tile_q8<T, Tile256, false>), dim3(tm * tn), dim3(256), 0, s,
+    // B stored N x K: the eight-wave ping-pong form (each wave's 64 x 128
+    // block holds whole 1 x 128 slices)
+    hipLaunchKernelGGL((tile::gemm16_pp_q8<T, tile::PPTile<256>>), dim3(tm * tn), dim3(512), 0, s,
                        a, tm, tn, c.qo);
   else
     hipLaunchKernelGGL((tile::gemm16_tile_q8<T, Tile256, true>), dim3(tm * tn), dim3(256), 0, s,

@@ -225,14 +225,14 @@ __device__ __forceinline__ void quant_store(const Acc (&acc)[FN], const float* s
         if (FULL || c + j * MMA::DIM < N)
           q[j * MMA::DIM] = (uint8_t)(FAST ? code_of_fast(acc[j][v], sc[v], rc[v], zero[v])
                                            : code_of(acc[j][v], sc[v], zero[v]));
-      if ((lane & 31) == 0) qo.S[r * qo.ssm + slice * qo.ssj] = sc[v];
+      if ((lane % MMA::DIM) == 0) qo.S[r * qo.ssm + slice * qo.ssj] = sc[v];
     }
   }
 }
 
 // One accumulator block row of the quantising epilogue: the row maxima over
-// the wave's columns inside N -- four accumulator blocks in the lane, then
-// the 32 lanes that hold the row's other columns -- the scales, then the
+// the wave's columns inside N -- the lane's FN accumulator blocks, then the
+// DIM lanes that hold the row's other columns -- the scales, then the
 // codes.  FULL: the wave's whole tile lies inside M x N.
 template <bool FULL, typename MMA, int FN, typename Acc>
 __device__ __forceinline__ void quant_block_row(const Acc (&acc)[FN], const QuantOut& qo, int64_t M,
@@ -248,7 +248,7 @@ __device__ __forceinline__ void quant_block_row(const Acc (&acc)[FN], const Quan
     for (int j = 0; j < FN; ++j)
       if (FULL || c + j * MMA::DIM < N) m = fmaxf(m, fabsf(acc[j][v]));
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    for (int o = 1; o < MMA::DIM; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
     sc[v] = block_scale(m, zero[v]);
     rc[v] = 1.0f / sc[v];
     fast = fast && scale_in_fast_range(sc[v]);
@@ -281,9 +281,9 @@ __device__ __forceinline__ void quant_block_rows(Acc (&acc)[FM][FN], const Quant
 template <typename MMA, int FM, int FN, typename Acc>
 __device__ __forceinline__ void quant_epilogue(Acc (&acc)[FM][FN], const QuantOut& qo, int64_t M,
                                                int64_t N, int64_t row0, int64_t col0, int lane) {
-  static_assert(MMA::DIM == 32 && FN * MMA::DIM == 128, "a wave row is one 1 x 128 slice");
+  static_assert(FN * MMA::DIM == 128, "a wave row is one 1 x 128 slice");
   if (col0 >= N) return;  // the wave's slice lies past N (wave-uniform)
-  const int64_t c = col0 + (lane & 31), slice = col0 / 128;
+  const int64_t c = col0 + (lane % MMA::DIM), slice = col0 / 128;
   if (row0 + FM * MMA::DIM <= M && col0 + 128 <= N)
     quant_block_rows<true, MMA>(acc, qo, M, N, row0, c, slice, lane,
                                 std::make_integer_sequence<int, FM>());

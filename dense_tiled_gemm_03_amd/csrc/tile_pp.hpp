@@ -23,7 +23,9 @@
 //    swizzle c ^ ((r >> 1) & 7) (conflict-free 16x16x32 fragment reads);
 //    group 0 loads every A stage, one slice ahead of its use, group 1 every
 //    B stage, two slices ahead;
-//  - edges, descriptors, tile order and the epilogue as in tile_body.
+//  - edges, descriptors, tile order and the epilogues (the cast to C, or
+//    with 256 x 256 tiles the fp8 quantisation per 1 x 128 row slice) as in
+//    tile_body.
 //
 // Interval t follows barrier t.  Group 0 reads slice j in interval 2j and
 // multiplies it in 2j + 1; group 1 reads it in 2j + 1 and multiplies it in
@@ -57,8 +59,9 @@ struct PPTile {
   static_assert(LDS_BYTES <= 160 * 1024, "stages must fit the LDS");
 };
 
-template <typename T, typename Cfg>
-__device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn) {
+template <typename T, typename Cfg, bool QUANT = false>
+__device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
+                                        const QuantOut& qo = QuantOut{}) {
   typedef typename Elem<T>::x8 T8;
   typedef f32x4 Acc;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
@@ -197,6 +200,14 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
+  if constexpr (QUANT) {
+    // fp8 output: with 256 x 256 tiles each wave's 128 columns are one
+    // 1 x 128 slice of C, quantised straight from the accumulators
+    static_assert(Cfg::WTN == 128, "a wave row is one 1 x 128 slice");
+    quant_epilogue<Mfma16>(acc, qo, a.M, a.N, m0 + q * Cfg::WTM, n0 + g * Cfg::WTN, lane);
+    return;
+  }
+
   // Epilogue: round each accumulator to the output type and store it inside
   // M x N (lane l holds column l % 16, rows 4 (l / 16) + v of each block).
   T* C = static_cast<T*>(a.C);
@@ -228,6 +239,16 @@ __global__ __launch_bounds__(512) void gemm16_pp(GemmArgs a, int tiles_m, int ti
   int tm, tn;
   tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
   pp_body<T, Cfg>(a, tm, tn);
+}
+
+// fp8 output (256 x 256 tiles): the product quantised per 1 x 128 row slice
+// in the epilogue.
+template <typename T, typename Cfg>
+__global__ __launch_bounds__(512) void gemm16_pp_q8(GemmArgs a, int tiles_m, int tiles_n,
+                                                    QuantOut qo) {
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
+  pp_body<T, Cfg, true>(a, tm, tn, qo);
 }
 
 }  // namespace tile
