@@ -9,12 +9,11 @@
 // result).  Per slice the arithmetic is that of tg_quant_fp8_1x128
 // (fp8_codec.hpp) applied to the fp32 product.
 //
-// Kernels: the 256 x 256 tile kernels with the quantising epilogue -- the
-// eight-wave ping-pong form for B stored N x K (64 x 128 per wave), the
-// four-wave form for B stored K x N (128 x 128 per wave); each wave's 128
-// columns are one slice, so a row's maximum is a reduction inside one wave
-// -- and, for every call those do not take, a fully masked kernel with one
-// 32 x 128 tile per workgroup.
+// Kernels: the 256 x 256 tile kernel in its eight-wave ping-pong form (B
+// stored N x K or K x N, 64 x 128 per wave) with the quantising epilogue --
+// each wave's 128 columns are one slice, so a row's maximum is a reduction
+// inside one wave -- and, for every call it does not take, a fully masked
+// kernel with one 32 x 128 tile per workgroup.
 #include "../../include/tg_gemm.h"
 
 #include "tile_mfma.hpp"
@@ -24,7 +23,7 @@ namespace tg {
 namespace {
 
 using tile::QuantOut;
-typedef tile::Tile<256, 256, tile::Mfma32> Tile256;
+typedef tile::PPTile<256> Tile256;
 
 constexpr int QTM = 32, QTN = 128;  // general kernel's output tile: one slice per row
 constexpr int QK = 32;              // K per step
@@ -147,8 +146,8 @@ hipError_t launch_t(const Call& c, Path p, hipStream_t s) {
     hipLaunchKernelGGL((tile::gemm16_pp_q8<T, tile::PPTile<256>>), dim3(tm * tn), dim3(512), 0, s,
                        a, tm, tn, c.qo);
   else
-    hipLaunchKernelGGL((tile::gemm16_tile_q8<T, Tile256, true>), dim3(tm * tn), dim3(256), 0, s,
-                       a, tm, tn, c.qo);
+    hipLaunchKernelGGL((tile::gemm16_pp_q8<T, tile::PPTile<256>, true>), dim3(tm * tn), dim3(512),
+                       0, s, a, tm, tn, c.qo);
   return hipGetLastError();
 }
 

@@ -1,14 +1,14 @@
 // Registration of the tuned tile kernel (tile_mfma.hpp) for B stored K x N
 // row-major (sbn = 1), the layout of the first-GEMM listing of "Getting to
 // know TileLang" and of the 4096^3 BF16 workload.  B tiles are staged as
-// [k][n] rows and read with the gfx950 transpose read; 256 x 256 tiles with
-// 32x32x16 MFMAs (a 4096 x 4096 C is exactly one wave of 256 tiles).
+// [k][n] rows and read with the gfx950 transpose read; 256 x 256 tiles in
+// the eight-wave ping-pong form (tile_pp.hpp), 16x16x32 MFMAs (a 4096 x 4096
+// C is exactly one wave of 256 tiles).
 #include "tile_mfma.hpp"
+#include "tile_pp.hpp"
 
 namespace tg {
 namespace {
-
-typedef tile::Tile<256, 256, tile::Mfma32> Tile256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -27,13 +27,16 @@ bool accepts(Op op, const GemmArgs& a) {
   return true;
 }
 
+// 256 x 256 tiles in the eight-wave ping-pong form (measured on 4096^3
+// with five rotated operand copies: see the design notes).
 hipError_t launch(Op op, const GemmArgs& a, const Scratch&, hipStream_t s) {
-  const int tm = (int)cdiv(a.M, Tile256::BM), tn = (int)cdiv(a.N, Tile256::BN);
-  const dim3 grid(tm * tn), block(256);
+  typedef tile::PPTile<256> PP;
+  const int tm = (int)cdiv(a.M, PP::BM), tn = (int)cdiv(a.N, PP::BN);
+  const dim3 grid(tm * tn), block(512);
   if (op == Op::BF16)
-    hipLaunchKernelGGL((tile::gemm16_tile<__bf16, Tile256, true>), grid, block, 0, s, a, tm, tn);
+    hipLaunchKernelGGL((tile::gemm16_pp<__bf16, PP, true>), grid, block, 0, s, a, tm, tn);
   else
-    hipLaunchKernelGGL((tile::gemm16_tile<_Float16, Tile256, true>), grid, block, 0, s, a, tm, tn);
+    hipLaunchKernelGGL((tile::gemm16_pp<_Float16, PP, true>), grid, block, 0, s, a, tm, tn);
   return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 #pragma once
-// Eight-wave "ping-pong" form of the N x K tile kernel (A row-major M x K,
-// B stored N x K, both K-contiguous): the same tile loop as tile_body in
+// Eight-wave "ping-pong" form of the tile kernel (A row-major M x K; B
+// stored N x K, or K x N with 256 x 256 tiles): the same tile loop as tile_body in
 // tile_mfma.hpp ("TileKernels deep dive" section 3.1; the first-GEMM listing
 // of "Getting to know TileLang": one output tile per workgroup, operand
 // tiles staged per K slice in a multi-stage pipeline, an fp32 accumulator
@@ -59,7 +59,10 @@ struct PPTile {
   static_assert(LDS_BYTES <= 160 * 1024, "stages must fit the LDS");
 };
 
-template <typename T, typename Cfg, bool QUANT = false>
+// BKN = false: B stored N x K (sbk = 1); true: B stored K x N (sbn = 1),
+// staged as [k][n] rows and read with the gfx950 transpose read, as in
+// tile_body (256 x 256 tiles only).
+template <typename T, typename Cfg, bool QUANT = false, bool BKN = false>
 __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
                                         const QuantOut& qo = QuantOut{}) {
   typedef typename Elem<T>::x8 T8;
@@ -79,13 +82,18 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   const int g = w >> 2, q = w & 3;  // group, wave within the group (its SIMD)
   const int K = (int)a.K;
   const int nk = (K + BK - 1) / BK;
-  const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
+  static_assert(!BKN || BN == 256, "K x N tiles are 256 columns wide");
+  const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)(BKN ? a.sbk : a.sbn);
 
+  // Operand tiles as buffer descriptors that end at the last valid element:
+  // A rows m0 .. of length K; B rows n0 .. of length K (N x K), or B rows
+  // 0 .. K-1 from column n0 (K x N).
   const int rows_a = (int)min<int64_t>(BM, a.M - m0), rows_b = (int)min<int64_t>(BN, a.N - n0);
   const T* Ab = static_cast<const T*>(a.A) + m0 * a.sam;
-  const T* Bb = static_cast<const T*>(a.B) + n0 * a.sbn;
+  const T* Bb = static_cast<const T*>(a.B) + (BKN ? n0 : n0 * a.sbn);
   const i32x4 ra = make_desc(Ab, (uint32_t)(((rows_a - 1) * lda + K) * 2));
-  const i32x4 rb = make_desc(Bb, (uint32_t)(((rows_b - 1) * ldb + K) * 2));
+  const i32x4 rb =
+      make_desc(Bb, (uint32_t)(BKN ? ((K - 1) * ldb + rows_b) * 2 : ((rows_b - 1) * ldb + K) * 2));
 
   // Loads: wave q's i-th load of a stage fills its rows 8 (4i + q) .. + 7;
   // lane l writes row 8 (4i + q) + (l >> 3) at chunk position l & 7, i.e.
@@ -102,12 +110,27 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
     for (int i = 0; i < Cfg::A_LOADS; ++i)
       load_lds16(ra, base + i * 4096, kin ? l_lane + i * l_step + 2 * k0 : kOutOfRange);
   };
+  // K x N B: the stage holds B as 64 k-rows of 512 bytes (32 chunks);
+  // chunk c of k-row k sits at position c ^ ((4k) & 31).  Wave q's i-th
+  // load fills k-rows 2 (4i + q) and + 1; lane l writes k-row 2 (4i + q) +
+  // (l >> 5) at position l & 31, i.e. logical chunk (l & 31) ^ ((8q + 4 (l
+  // >> 5)) & 31).  k-rows past K are fetched out of range (zeros).
+  const int nrow = lane >> 5;
+  const uint32_t nchunk = (lane & 31) ^ ((8 * q + 4 * nrow) & 31);
+  const uint32_t nb_lane = (uint32_t)(2 * q + nrow) * ldb * 2 + 16 * nchunk;
   auto load_b = [&](int slot, int k0) {
     const bool kin = k0 + 8 * lchunk < K;
     const uint32_t base = lds32 + b_off(slot) + q * 1024;
 #pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i)
-      load_lds16(rb, base + i * 4096, kin ? l_lane + i * l_step + 2 * k0 : kOutOfRange);
+    for (int i = 0; i < Cfg::B_LOADS; ++i) {
+      if constexpr (BKN) {
+        const bool rin = k0 + 8 * i + 2 * q + nrow < K;
+        load_lds16(rb, base + i * 4096, rin ? nb_lane + (uint32_t)(8 * i + k0) * ldb * 2
+                                            : kOutOfRange);
+      } else {
+        load_lds16(rb, base + i * 4096, kin ? l_lane + i * l_step + 2 * k0 : kOutOfRange);
+      }
+    }
   };
 
   // Fragment reads (16x16x32): row (16-aligned base) + (l % 16), chunk
@@ -124,6 +147,38 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0.0f, 0.0f, 0.0f, 0.0f};
+  // K x N B fragments (ds_read_b64_tr_b16, as in tile_body): within each
+  // 16-lane group, lane 4r + q' supplies the address of columns 4q' .. +3 of
+  // k-row r of a 4-row group, and lane i receives column i of those rows;
+  // lane l of group u = l / 16 points at k-row 32 s + 8u + 4h + r of the
+  // slice, columns nbase + 4q', and the two reads (h = 0, 1) give its 8
+  // k-values.  The offsets within a stage do not depend on the slice.
+  constexpr int BROW = BN * 2;
+  int kn_off[BKN ? FN : 1][2];
+  if constexpr (BKN) {
+    const int u = lane >> 4, r = (lane >> 2) & 3, qq = lane & 3;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kr = 8 * u + 4 * h + r;
+        const int nbase = g * Cfg::WTN + j * 16;
+        const int chunk = ((nbase >> 3) ^ ((4 * kr) & 31)) + (qq >> 1);
+        kn_off[j][h] = kr * BROW + chunk * 16 + (qq & 1) * 8;
+      }
+  }
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  auto read_b_kn = [&](const char* stage_base, int sub, int j) {
+    const char* p = stage_base + sub * 32 * BROW;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p + kn_off[j][0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p + kn_off[j][1]));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(T8, v);
+  };
+
   T8 fa[SUBS][FM], fb[SUBS][FN];
   auto read_slice = [&](int sa, int sb) {
     const char* ab = lds + a_off(sa) + a_rd;
@@ -134,8 +189,12 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
       for (int i = 0; i < FM; ++i)
         fa[s][i] = *reinterpret_cast<const T8*>(ab + i * 16 * Cfg::ROW_BYTES + ch[s]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        fb[s][j] = *reinterpret_cast<const T8*>(bb + j * 16 * Cfg::ROW_BYTES + ch[s]);
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (BKN)
+          fb[s][j] = read_b_kn(lds + b_off(sb), s, j);
+        else
+          fb[s][j] = *reinterpret_cast<const T8*>(bb + j * 16 * Cfg::ROW_BYTES + ch[s]);
+      }
     }
   };
   auto multiply = [&]() {
@@ -234,21 +293,21 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   }
 }
 
-template <typename T, typename Cfg>
+template <typename T, typename Cfg, bool BKN = false>
 __global__ __launch_bounds__(512) void gemm16_pp(GemmArgs a, int tiles_m, int tiles_n) {
   int tm, tn;
   tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
-  pp_body<T, Cfg>(a, tm, tn);
+  pp_body<T, Cfg, false, BKN>(a, tm, tn);
 }
 
 // fp8 output (256 x 256 tiles): the product quantised per 1 x 128 row slice
 // in the epilogue.
-template <typename T, typename Cfg>
+template <typename T, typename Cfg, bool BKN = false>
 __global__ __launch_bounds__(512) void gemm16_pp_q8(GemmArgs a, int tiles_m, int tiles_n,
                                                     QuantOut qo) {
   int tm, tn;
   tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
-  pp_body<T, Cfg, true>(a, tm, tn, qo);
+  pp_body<T, Cfg, true, BKN>(a, tm, tn, qo);
 }
 
 }  // namespace tile
