@@ -111,13 +111,20 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
       load_lds16(ra, base + i * 4096, kin ? l_lane + i * l_step + 2 * k0 : kOutOfRange);
   };
   // K x N B: the stage holds B as 64 k-rows of 512 bytes (32 chunks);
-  // chunk c of k-row k sits at position c ^ ((4k) & 31).  Wave q's i-th
-  // load fills k-rows 2 (4i + q) and + 1; lane l writes k-row 2 (4i + q) +
-  // (l >> 5) at position l & 31, i.e. logical chunk (l & 31) ^ ((8q + 4 (l
-  // >> 5)) & 31).  k-rows past K are fetched out of range (zeros).
+  // chunk c of k-row k sits at position c ^ kn_swz(k), kn_swz(k) =
+  // 4 (k & 3) + 2 ((k >> 3) & 1).  The transpose reads of one instruction's
+  // first (last) 32 lanes cover k-rows 8u + r (u = 0, 1, or 2, 3; r < 4) of
+  // a 16-column block; with this swizzle their eight 32-byte pieces fall on
+  // eight different 32-byte bank groups (4 (k & 3) alone, the swizzle of
+  // the four-wave kernel, maps rows r and 8 + r to the same banks).  Wave
+  // q's i-th load fills k-rows 8i + 2q and + 1; lane l writes k-row 8i + 2q
+  // + (l >> 5) at position l & 31, i.e. logical chunk (l & 31) ^ kn_swz of
+  // that row = (l & 31) ^ (4 ((2q + (l >> 5)) & 3) + 2 (i & 1)).  k-rows
+  // past K are fetched out of range (zeros).
   const int nrow = lane >> 5;
-  const uint32_t nchunk = (lane & 31) ^ ((8 * q + 4 * nrow) & 31);
-  const uint32_t nb_lane = (uint32_t)(2 * q + nrow) * ldb * 2 + 16 * nchunk;
+  const uint32_t nswz = 4 * ((2 * q + nrow) & 3);
+  const uint32_t nb_lane0 = (uint32_t)(2 * q + nrow) * ldb * 2 + 16 * ((lane & 31) ^ nswz);
+  const uint32_t nb_lane1 = (uint32_t)(2 * q + nrow) * ldb * 2 + 16 * ((lane & 31) ^ (nswz + 2));
   auto load_b = [&](int slot, int k0) {
     const bool kin = k0 + 8 * lchunk < K;
     const uint32_t base = lds32 + b_off(slot) + q * 1024;
@@ -125,6 +132,7 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
     for (int i = 0; i < Cfg::B_LOADS; ++i) {
       if constexpr (BKN) {
         const bool rin = k0 + 8 * i + 2 * q + nrow < K;
+        const uint32_t nb_lane = (i & 1) ? nb_lane1 : nb_lane0;
         load_lds16(rb, base + i * 4096, rin ? nb_lane + (uint32_t)(8 * i + k0) * ldb * 2
                                             : kOutOfRange);
       } else {
@@ -152,7 +160,8 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   // k-row r of a 4-row group, and lane i receives column i of those rows;
   // lane l of group u = l / 16 points at k-row 32 s + 8u + 4h + r of the
   // slice, columns nbase + 4q', and the two reads (h = 0, 1) give its 8
-  // k-values.  The offsets within a stage do not depend on the slice.
+  // k-values.  kn_swz of that k-row is 4r + 2 (u & 1) whatever s and h, so
+  // the offsets within a stage do not depend on the sub-step or the slice.
   constexpr int BROW = BN * 2;
   int kn_off[BKN ? FN : 1][2];
   if constexpr (BKN) {
@@ -163,7 +172,7 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
       for (int h = 0; h < 2; ++h) {
         const int kr = 8 * u + 4 * h + r;
         const int nbase = g * Cfg::WTN + j * 16;
-        const int chunk = ((nbase >> 3) ^ ((4 * kr) & 31)) + (qq >> 1);
+        const int chunk = ((nbase >> 3) ^ (4 * r + 2 * (u & 1))) + (qq >> 1);
         kn_off[j][h] = kr * BROW + chunk * 16 + (qq & 1) * 8;
       }
   }
