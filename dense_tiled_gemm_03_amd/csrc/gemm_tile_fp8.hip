@@ -99,11 +99,25 @@ __device__ __forceinline__ void load_lds4s(const i32x4& desc, uint32_t lds, uint
 // epilogue.  AS / BS: stages of the A ring (A codes + A scales) and of the B
 // ring (B codes + B scale); with S stages an operand's loads have S - 1
 // slices to arrive.
-template <int AS, int BS>
+// Kinds of wave by the scale load each issues per slice: the A-row scales
+// (waves 0-3), the tile's B scale (wave 4), none (waves 5-7).  Each kind
+// runs its own copy of the K loop, so its loads and wait counts are fixed
+// at compile time and no branch splits the MFMA stream.
+enum { kScaleA = 0, kScaleB = 1, kScaleNone = 2 };
+
+// The LDS array of the stage rings, one per size, shared by the copies of
+// the K loop inlined into one kernel.
+template <int BYTES>
+__device__ __forceinline__ char* fp8_lds() {
+  __shared__ __attribute__((aligned(1024))) char lds[BYTES];
+  return lds;
+}
+
+template <int AS, int BS, int KIND>
 __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn) {
   static_assert(AS >= 2 && BS >= AS, "at least two stages, B at least as deep as A");
   static_assert(AS * F_ASTAGE + BS * F_BSTAGE <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) char lds[AS * F_ASTAGE + BS * F_BSTAGE];
+  char* const lds = fp8_lds<AS * F_ASTAGE + BS * F_BSTAGE>();
   const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
   // byte offsets of A stage s and B stage s
@@ -161,8 +175,10 @@ __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn)
   // zeros.  (q is a compile-time index.)
   auto load_one = [&](int q, int sa, int kb_a, int sb, int kb_b) {
     if (q == 0) {
-      load_lds4s(rsa, lds32 + a_off(sa) + F_A_BYTES + 256 * w, kb_a < nkb ? sa_lane : kOutOfRange,
-                 (uint32_t)(kb_a * a.ssak) * 4);
+      // the A-row scales (waves 0-3)
+      if constexpr (KIND == kScaleA)
+        load_lds4s(rsa, lds32 + a_off(sa) + F_A_BYTES + 256 * w,
+                   kb_a < nkb ? sa_lane : kOutOfRange, (uint32_t)(kb_a * a.ssak) * 4);
     } else if (q < F_APART) {
       const uint32_t k0 = (uint32_t)(kb_a * F_BK);
       const bool kin = (int)k0 + 16 * (int)lchunk < K;
@@ -173,7 +189,8 @@ __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn)
       const uint32_t k0 = (uint32_t)(kb_b * F_BK);
       const bool kin = (int)k0 + 16 * (int)lchunk < K;
       load_lds16s(rb, lds32 + b_off(sb) + (w + 8 * i) * 1024, kin ? bv[i] : kOutOfRange, k0);
-    } else {
+    } else if constexpr (KIND == kScaleB) {
+      // the tile's B scale (wave 4)
       load_lds4s(rsb, lds32 + b_off(sb) + F_B_BYTES + 256 * w, kb_b < nkb ? sb_lane : kOutOfRange,
                  (uint32_t)(kb_b * a.ssbk) * 4);
     }
@@ -268,10 +285,14 @@ __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn)
       if (q < F_APART ? j + AS >= 0 : j + BS >= 0)
         load_one(q, j + AS >= 0 ? j + AS : 0, j + AS, j + BS >= 0 ? j + BS : 0, j + BS);
   }
-  constexpr int B_TAIL = BS > AS ? F_BPART : 0;
-  // loads after A(0)'s part: the B part of its batch (when B is deeper) and
-  // AS - 1 full batches
-  constexpr int INIT_WAIT = B_TAIL + (AS - 1) * F_NLD, LOOP_WAIT = B_TAIL + (AS - 2) * F_NLD;
+  // This wave's loads per slice: the code loads and its kind's scale load;
+  // at a slice's wait, the loads after A(kb + 1)'s part may stay in flight:
+  // the B part of its batch (when B is deeper) and AS - 2 full batches
+  // (before slice 0: one batch more).
+  constexpr int NLD = F_A_LD + F_B_LD + (KIND == kScaleNone ? 0 : 1);
+  constexpr int BPART = F_B_LD + (KIND == kScaleB ? 1 : 0);
+  constexpr int B_TAIL = BS > AS ? BPART : 0;
+  constexpr int INIT_WAIT = B_TAIL + (AS - 1) * NLD, LOOP_WAIT = B_TAIL + (AS - 2) * NLD;
   static_assert(INIT_WAIT <= 63, "loads in flight must fit the vmcnt counter");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INIT_WAIT) : "memory");
   asm volatile("s_barrier" ::: "memory");
@@ -310,11 +331,23 @@ __device__ __forceinline__ void fp8_tile_body(const GemmArgs& a, int tm, int tn)
       }
 }
 
+// The tile with each wave in its kind's copy of the K loop (the branch is
+// wave-uniform; every copy passes the same barriers).
+__device__ __forceinline__ void fp8_tile_waves(const GemmArgs& a, int tm, int tn) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w < 4)
+    fp8_tile_body<F_AS, F_BS, kScaleA>(a, tm, tn);
+  else if (w == 4)
+    fp8_tile_body<F_AS, F_BS, kScaleB>(a, tm, tn);
+  else
+    fp8_tile_body<F_AS, F_BS, kScaleNone>(a, tm, tn);
+}
+
 __global__ __launch_bounds__(64 * F_WAVES) void gemm_fp8_tile(GemmArgs a, int tiles_m,
                                                                 int tiles_n) {
   int tm, tn;
   tile::tile_coords(tiles_m, tiles_n, 4, tm, tn);
-  fp8_tile_body<F_AS, F_BS>(a, tm, tn);
+  fp8_tile_waves(a, tm, tn);
 }
 
 // Grouped products (see gemm_grouped.hip): the tile's group re-bases A and
@@ -329,7 +362,7 @@ __global__ __launch_bounds__(64 * F_WAVES) void gemm_fp8_grouped(GemmArgs a, Gro
   ag.B = static_cast<const uint8_t*>(a.B) + g * gt.sbg;
   ag.SB = a.SB + g * gt.ssbg;
   ag.C = static_cast<__bf16*>(a.C) + gt.row0[g] * a.scm;
-  fp8_tile_body<F_AS, F_BS>(ag, tm, tn);
+  fp8_tile_waves(ag, tm, tn);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
