@@ -50,6 +50,7 @@ namespace {
 
 using tile::kOutOfRange;
 using tile::make_desc;
+using tile::load_lds16;
 using tile::waitcnt_imm;
 
 constexpr int F_BM = 256, F_BN = 128, F_BK = 128;    // tile, k per slice (bytes)
@@ -365,6 +366,281 @@ __global__ __launch_bounds__(64 * F_WAVES) void gemm_fp8_grouped(GemmArgs a, Gro
   fp8_tile_waves(ag, tm, tn);
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong form with 256 x 256 tiles.  A 256 x 128 tile moves 48 KiB per
+// 128-wide slice for 2 x 256 x 128 x 128 FLOP; a 256 x 256 tile 64 KiB for
+// twice the FLOP, i.e. a third fewer bytes per FLOP through each CU's load
+// path.  The fp32 accumulators of a 64 x 128 wave tile take 128 VGPRs, so the
+// work of each SIMD is split between two waves that take turns, as in the
+// ping-pong form of the 16-bit kernel:
+//  - waves 0-3 (group 0) own columns 0-127 of the tile, waves 4-7 (group 1)
+//    columns 128-255, so each group's columns are exactly one 128-wide B
+//    scale block; wave q of a group owns rows 64q .. 64q + 63;
+//  - the MFMA runs transposed, P^T = B_blk * A_blk^T, so that lane l's four
+//    accumulators of a block belong to one row of C (16 i + l % 16) and four
+//    consecutive columns: the fold-in acc += (SA[row] * SB) * P then needs one
+//    scale per lane and row block (4 per slice) instead of 16;
+//  - intervals separated by workgroup barriers: in each interval one group
+//    multiplies a slice (32 MFMAs and the fold-ins, reading the B fragments
+//    of the slice from LDS one column block at a time, two ahead of use)
+//    while the other reads the next slice's A fragments and row scales into
+//    registers and issues its share of the loads of the next slice;
+//  - LDS: two stages of A (256 rows x 128 bytes, then the slice's 256 A-row
+//    scales and the tile's two B scales) and two of B (256 x 128 bytes),
+//    130.5 KiB; group 0 loads every A stage with its scales, group 1 every B
+//    stage, each one slice ahead of use.
+// Interval t follows barrier t.  Group 0 reads A(j) in interval 2j and
+// multiplies slice j in 2j + 1; group 1 reads A(j) in 2j + 1 and multiplies
+// in 2j + 2.  So A stage j % 2 is free after barrier 2j + 2 (group 0 refills
+// it with slice j + 2 in interval 2j + 2 and waits for it before barrier
+// 2j + 4), and B stage j % 2 after barrier 2j + 3 (group 1 refills it with
+// slice j + 2 in interval 2j + 3 and waits for it before barrier 2j + 5,
+// ahead of group 0's multiply of slice j + 2).  Each group passes 2 nk + 2
+// barriers (group 0's last one waits for group 1's last multiply: with no
+// conditional barrier in either loop, each loop body is one basic block, and
+// the compiler cannot sink the MFMAs of a multiply past the barrier that
+// ends it).
+constexpr int Q_BM = 256, Q_BN = 256, Q_BK = 128;
+constexpr int Q_ROW = 128;                            // bytes of k per staged row
+constexpr int Q_A_BYTES = Q_BM * Q_ROW, Q_B_BYTES = Q_BN * Q_ROW;
+constexpr int Q_SA = Q_A_BYTES;                       // A-row scales of the slice
+constexpr int Q_SB = Q_A_BYTES + 1024;                // the tile's two B scales
+constexpr int Q_ASTAGE = Q_A_BYTES + 1024 + 256;
+constexpr int Q_LDS = 2 * Q_ASTAGE + 2 * Q_B_BYTES;
+constexpr int Q_LOADS = Q_A_BYTES / 1024 / 4;         // 1 KiB loads per wave per slice
+constexpr int Q_FM = 4, Q_FN = 8;                     // 16 x 16 blocks of a wave tile
+constexpr int Q_LAG = 3;                              // MFMAs between a block and its fold-in
+constexpr int Q_NB = 3;                               // B fragment buffers
+static_assert(Q_LDS <= 160 * 1024, "stages must fit the LDS");
+static_assert(Q_ASTAGE % 256 == 0, "stage bases on whole bank rows");
+
+__device__ __forceinline__ void load_lds4(const i32x4& desc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(desc) : "memory");
+}
+
+__device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
+  char* const lds = fp8_lds<Q_LDS>();
+  const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+  auto a_off = [](int st) { return st * Q_ASTAGE; };
+  auto b_off = [](int st) { return 2 * Q_ASTAGE + st * Q_B_BYTES; };
+
+  const int64_t m0 = (int64_t)tm * Q_BM, n0 = (int64_t)tn * Q_BN;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = w >> 2, q = w & 3;  // group, wave within the group (its SIMD)
+  const int K = (int)a.K;
+  const int nkb = (K + Q_BK - 1) / Q_BK;
+  const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
+
+  // Code tiles as descriptors ending at the last valid row; the tile's
+  // scales: A rows m0 .. (SA[i, kb] at i * ssam + kb * ssak floats) and B
+  // scale rows n0 / 128 and n0 / 128 + 1 (the second only if N reaches it).
+  const int rows_a = (int)min<int64_t>(Q_BM, a.M - m0), rows_b = (int)min<int64_t>(Q_BN, a.N - n0);
+  const uint8_t* Ab = static_cast<const uint8_t*>(a.A) + m0 * a.sam;
+  const uint8_t* Bb = static_cast<const uint8_t*>(a.B) + n0 * a.sbn;
+  const i32x4 ra = make_desc(Ab, (uint32_t)((rows_a - 1) * lda + K));
+  const i32x4 rb = make_desc(Bb, (uint32_t)((rows_b - 1) * ldb + K));
+  const int nsb = (int)min<int64_t>(2, cdiv(a.N, 128) - n0 / 128);
+  const float* SAb = a.SA + m0 * a.ssam;
+  const float* SBb = a.SB + (n0 / 128) * a.ssbn;
+  const i32x4 rsa = make_desc(SAb, (uint32_t)(((rows_a - 1) * a.ssam + (nkb - 1) * a.ssak + 1) * 4));
+  const i32x4 rsb = make_desc(SBb, (uint32_t)(((nsb - 1) * a.ssbn + (nkb - 1) * a.ssbk + 1) * 4));
+
+  // Code loads: wave q's i-th load of a stage fills rows 32 i + 8 q .. + 7;
+  // lane l writes row 32 i + 8 q + (l >> 3) at chunk position l & 7, i.e.
+  // logical chunk (l & 7) ^ (4 (q & 1) + (l >> 4)) (swizzle c ^ ((r >> 1) & 7)).
+  // Rows past the tile's last valid row fall outside the descriptor (zeros).
+  const uint32_t lrow = 8 * q + (lane >> 3);
+  const uint32_t lchunk = (lane & 7) ^ (4 * (q & 1) + (lane >> 4));
+  const uint32_t ld = g == 0 ? lda : ldb;
+  const uint32_t l_lane = lrow * ld + 16 * lchunk, l_step = 32 * ld;
+  auto load_codes = [&](const i32x4& desc, uint32_t base, int kb) {
+    const int k0 = kb * Q_BK;
+    const bool kin = k0 + 16 * (int)lchunk < K;
+#pragma unroll
+    for (int i = 0; i < Q_LOADS; ++i)
+      load_lds16(desc, base + i * 4096, kin ? l_lane + i * l_step + (uint32_t)k0 : kOutOfRange);
+  };
+  // Scale loads (group 0): wave q the A-row scales of rows 64 q + l, wave 0
+  // lanes 0-1 also the two B scales; everything else reads zeros.
+  const int sa_row = 64 * q + lane;
+  const bool sa_in = sa_row < rows_a, sb_in = lane < nsb;
+  const uint32_t sa_lane = (uint32_t)sa_row * (uint32_t)a.ssam * 4;
+  const uint32_t sb_lane = (uint32_t)lane * (uint32_t)a.ssbn * 4;
+  auto load_scales = [&](int st, int kb) {
+    const bool kin = kb < nkb;
+    load_lds4(rsa, lds32 + a_off(st) + Q_SA + 256 * q,
+              kin && sa_in ? sa_lane + (uint32_t)(kb * a.ssak) * 4 : kOutOfRange);
+    if (q == 0)
+      load_lds4(rsb, lds32 + a_off(st) + Q_SB,
+                kin && sb_in ? sb_lane + (uint32_t)(kb * a.ssbk) * 4 : kOutOfRange);
+  };
+
+  // Fragment reads (16x16x128): block row (16-aligned base) + (l & 15);
+  // lane group u = l >> 4 reads chunks u and u + 4 of the 128-byte row, at
+  // positions chunk ^ ((l >> 1) & 7).  A and B take the same k assignment.
+  const int sw = (lane >> 1) & 7, u = lane >> 4;
+  const int rd0 = (lane & 15) * Q_ROW + ((u ^ sw) * 16);
+  const int rd1 = (lane & 15) * Q_ROW + (((u + 4) ^ sw) * 16);
+  auto rd32 = [&](const char* p) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(p + rd0);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + rd1);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  const int a_rd = 64 * q * Q_ROW, b_rd = 128 * g * Q_ROW;
+  const int s_rd = Q_SA + (64 * q + (lane & 15)) * 4;
+
+  // acc[j][i]: block of tile columns 16 j .. (this group's) and rows 16 i ..
+  // (this wave's); lane l holds row 16 i + (l & 15), columns 16 j + 4 (l >> 4) + v.
+  f32x4 acc[Q_FN][Q_FM];
+#pragma unroll
+  for (int j = 0; j < Q_FN; ++j)
+#pragma unroll
+    for (int i = 0; i < Q_FM; ++i) acc[j][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  i32x8 fa[Q_FM], fb[Q_NB];
+  float s[Q_FM];  // SA[row] * SB of this lane's rows for the slice
+  auto read_a = [&](int st) {
+    const char* base = lds + a_off(st);
+#pragma unroll
+    for (int i = 0; i < Q_FM; ++i) fa[i] = rd32(base + a_rd + i * 16 * Q_ROW);
+    const float sb = *reinterpret_cast<const float*>(base + Q_SB + 4 * g);
+#pragma unroll
+    for (int i = 0; i < Q_FM; ++i)
+      s[i] = *reinterpret_cast<const float*>(base + s_rd + 64 * i) * sb;
+  };
+  auto read_b = [&](int st, int j) { return rd32(lds + b_off(st) + b_rd + j * 16 * Q_ROW); };
+  // Step boundary of the multiply: the empty asm with a memory clobber keeps
+  // the LDS reads where they are written (a scheduling fence alone lets
+  // instruction selection hoist all of them to the top, which needs 40 more
+  // VGPRs), the scheduling fence keeps MFMAs and fold-ins in their steps.
+  auto fence = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // One slice from B stage st: MFMA n covers block (j, i) = (n / 4, n % 4)
+  // and the fold-in of MFMA n - Q_LAG follows it; the fragments of column
+  // block j + 2 are read when block j's first MFMA has been issued.
+  auto multiply = [&](int st) {
+    fb[0] = read_b(st, 0);
+    fb[1] = read_b(st, 1);
+    f32x4 p[Q_LAG + 1];
+#pragma unroll
+    for (int n = 0; n < Q_FN * Q_FM + Q_LAG; ++n) {
+      if (n < Q_FN * Q_FM) {
+        const int j = n / Q_FM, i = n % Q_FM;
+        p[n % (Q_LAG + 1)] = mfma16x16x128_e4m3(fb[j % Q_NB], fa[i], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+        if (i == 0 && j + 2 < Q_FN) fb[(j + 2) % Q_NB] = read_b(st, j + 2);
+      }
+      if (n >= Q_LAG) {
+        const int m = n - Q_LAG, j = m / Q_FM, i = m % Q_FM;
+        const f32x4 pm = p[m % (Q_LAG + 1)];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[j][i][v] += s[i] * pm[v];
+      }
+      fence();
+    }
+  };
+  auto barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto wait_lds = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  auto wait_loads = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  if (g == 0) {
+    load_codes(ra, lds32 + a_off(0) + q * 1024, 0);
+    load_scales(0, 0);
+    wait_loads();
+    barrier();                                   // 0
+    int st = 0;
+    for (int j = 0; j < nkb; ++j) {
+      const int nst = st ^ 1;
+      load_codes(ra, lds32 + a_off(nst) + q * 1024, j + 1);  // into slice j - 1's stage
+      load_scales(nst, j + 1);
+      read_a(st);
+      wait_lds();
+      barrier();                                 // 2j + 1
+      multiply(st);
+      wait_loads();
+      barrier();                                 // 2j + 2
+      st = nst;
+    }
+    barrier();                                   // 2 nk + 1: group 1's last multiply
+  } else {
+    load_codes(rb, lds32 + b_off(0) + q * 1024, 0);
+    wait_loads();
+    barrier();                                   // 0
+    barrier();                                   // 1
+    int st = 0;
+    for (int j = 0; j < nkb; ++j) {
+      const int nst = st ^ 1;
+      load_codes(rb, lds32 + b_off(nst) + q * 1024, j + 1);  // into slice j - 1's stage
+      read_a(st);
+      wait_lds();
+      barrier();                                 // 2j + 2
+      multiply(st);
+      wait_loads();                              // B(j + 1) before group 0 multiplies it
+      barrier();                                 // 2j + 3
+      st = nst;
+    }
+  }
+
+  // Epilogue: round each accumulator to bf16 and store it inside M x N.
+  __bf16* C = static_cast<__bf16*>(a.C);
+  const int64_t row0 = m0 + 64 * q + (lane & 15);
+  const int64_t col0 = n0 + 128 * g + 4 * u;
+  const bool whole = m0 + Q_BM <= a.M && n0 + Q_BN <= a.N && a.scm % 4 == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.C) & 7) == 0;
+  if (whole) {
+#pragma unroll
+    for (int j = 0; j < Q_FN; ++j)
+#pragma unroll
+      for (int i = 0; i < Q_FM; ++i) {
+        const bf16x4 o = {to_out<__bf16>(acc[j][i][0]), to_out<__bf16>(acc[j][i][1]),
+                          to_out<__bf16>(acc[j][i][2]), to_out<__bf16>(acc[j][i][3])};
+        *reinterpret_cast<bf16x4*>(C + (row0 + 16 * i) * a.scm + col0 + 16 * j) = o;
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < Q_FN; ++j)
+#pragma unroll
+      for (int i = 0; i < Q_FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t row = row0 + 16 * i, col = col0 + 16 * j + v;
+          if (row < a.M && col < a.N) C[row * a.scm + col] = to_out<__bf16>(acc[j][i][v]);
+        }
+  }
+}
+
+__global__ __launch_bounds__(512) void gemm_fp8_pp(GemmArgs a, int tiles_m, int tiles_n) {
+  int tm, tn;
+  tile::tile_coords(tiles_m, tiles_n, 4, tm, tn);
+  fp8_pp_body(a, tm, tn);
+}
+
+__global__ __launch_bounds__(512) void gemm_fp8_grouped_pp(GemmArgs a, GroupTable gt) {
+  int g, tm, tn;
+  tile::group_coords(gt, Q_BM, 4, g, tm, tn);
+  GemmArgs ag = a;
+  ag.M = gt.row0[g + 1] - gt.row0[g];
+  ag.A = static_cast<const uint8_t*>(a.A) + gt.row0[g] * a.sam;
+  ag.SA = a.SA + gt.row0[g] * a.ssam;
+  ag.B = static_cast<const uint8_t*>(a.B) + g * gt.sbg;
+  ag.SB = a.SB + g * gt.ssbg;
+  ag.C = static_cast<__bf16*>(a.C) + gt.row0[g] * a.scm;
+  fp8_pp_body(ag, tm, tn);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // Both code operands K-contiguous with 16-byte aligned rows, K a multiple of
@@ -377,16 +653,37 @@ bool accepts(Op op, const GemmArgs& a) {
   if (!aligned16(a.A) || !aligned16(a.B)) return false;
   if ((reinterpret_cast<uintptr_t>(a.SA) & 3) || (reinterpret_cast<uintptr_t>(a.SB) & 3)) return false;
   const int64_t lim = int64_t(1) << 30, nkb = cdiv(a.K, 128);
-  if (F_BM * a.sam + a.K >= lim || F_BN * a.sbn + a.K >= lim) return false;
-  if ((F_BM * a.ssam + nkb * a.ssak) * 4 >= lim || (nkb * a.ssbk) * 4 >= lim) return false;
+  if (F_BM * a.sam + a.K >= lim || Q_BN * a.sbn + a.K >= lim) return false;
+  if ((F_BM * a.ssam + nkb * a.ssak) * 4 >= lim || (a.ssbn + nkb * a.ssbk) * 4 >= lim)
+    return false;
   if (a.M > (int64_t(1) << 24) || a.N > (int64_t(1) << 24)) return false;
   return true;
 }
 
+// Tile shape of a call: 256 x 256 (ping-pong) unless 256 x 128 tiles finish
+// in less time.  Both forms are bound by the bytes each CU moves per slice,
+// 64 KiB against 48 KiB, so a tile round of 256 x 256 costs 4 units and one
+// of 256 x 128 costs 3 (one tile round: one tile per CU).
+constexpr int kCus = 256;
+bool wide_tiles(int64_t tiles_m, int64_t N) {
+  const int64_t rounds_w = cdiv(tiles_m * cdiv(N, Q_BN), kCus);
+  const int64_t rounds_n = cdiv(tiles_m * cdiv(N, F_BN), kCus);
+  return 4 * rounds_w <= 3 * rounds_n;
+}
+
 hipError_t launch(Op, const GemmArgs& a, const Scratch&, hipStream_t s) {
-  const int tm = (int)cdiv(a.M, F_BM), tn = (int)cdiv(a.N, F_BN);
-  hipLaunchKernelGGL(gemm_fp8_tile, dim3(tm * tn), dim3(64 * F_WAVES), 0, s, a, tm, tn);
+  if (wide_tiles(cdiv(a.M, 256), a.N)) {
+    const int tm = (int)cdiv(a.M, Q_BM), tn = (int)cdiv(a.N, Q_BN);
+    hipLaunchKernelGGL(gemm_fp8_pp, dim3(tm * tn), dim3(512), 0, s, a, tm, tn);
+  } else {
+    const int tm = (int)cdiv(a.M, F_BM), tn = (int)cdiv(a.N, F_BN);
+    hipLaunchKernelGGL(gemm_fp8_tile, dim3(tm * tn), dim3(64 * F_WAVES), 0, s, a, tm, tn);
+  }
   return hipGetLastError();
+}
+
+const char* plan_name(const GemmArgs& a, const Scratch&) {
+  return wide_tiles(cdiv(a.M, 256), a.N) ? "tile_fp8_256x256" : "tile_fp8_256x128";
 }
 
 struct Grouped8 {
@@ -454,13 +751,21 @@ bool grouped_tiled(const Grouped8& c) {
   return accepts(Op::FP8, a);
 }
 
+// Tile shape of a grouped launch (as wide_tiles, over all groups' tile rows).
+bool grouped_wide(const Grouped8& c) {
+  int64_t tiles_m = 0;
+  for (int64_t g = 0; g < c.G; ++g) tiles_m += cdiv(c.off[g + 1] - c.off[g], 256);
+  return wide_tiles(tiles_m, c.N);
+}
+
 tg_status run_grouped(const Grouped8& c, tg_stream_t stream) {
   tg_status st = validate_grouped(c);
   if (st != TG_SUCCESS || c.G == 0 || c.off[c.G] == c.off[0] || c.N == 0) return st;
   if (grouped_tiled(c)) {
+    const bool wide = grouped_wide(c);
     GroupTable gt;
     gt.G = (int)c.G;
-    gt.tiles_n = (int)cdiv(c.N, F_BN);
+    gt.tiles_n = (int)cdiv(c.N, wide ? Q_BN : F_BN);
     gt.sbg = c.sbg;
     gt.ssbg = c.ssbg;
     int64_t tiles = 0;
@@ -474,8 +779,12 @@ tg_status run_grouped(const Grouped8& c, tg_stream_t stream) {
                      static_cast<const uint8_t*>(c.A) + c.off[0] * c.lda, c.lda, 1, c.B, 1, c.ldb,
                      c.SA + c.off[0] * c.ssam, c.ssam, c.ssak, c.SB, c.ssbn, c.ssbk,
                      static_cast<__bf16*>(c.C) + c.off[0] * c.ldc, c.ldc};
-    hipLaunchKernelGGL(gemm_fp8_grouped, dim3((unsigned)tiles), dim3(64 * F_WAVES), 0,
-                       static_cast<hipStream_t>(stream), a, gt);
+    if (wide)
+      hipLaunchKernelGGL(gemm_fp8_grouped_pp, dim3((unsigned)tiles), dim3(512), 0,
+                         static_cast<hipStream_t>(stream), a, gt);
+    else
+      hipLaunchKernelGGL(gemm_fp8_grouped, dim3((unsigned)tiles), dim3(64 * F_WAVES), 0,
+                         static_cast<hipStream_t>(stream), a, gt);
     return hipGetLastError() == hipSuccess ? TG_SUCCESS : TG_ERR_LAUNCH;
   }
   for (int64_t g = 0; g < c.G; ++g) {
@@ -494,7 +803,7 @@ tg_status run_grouped(const Grouped8& c, tg_stream_t stream) {
 }  // namespace
 
 const Variant* variant_tile_fp8() {
-  static const Variant v = {"tile_fp8_256x128", accepts, launch, nullptr, nullptr};
+  static const Variant v = {"tile_fp8", accepts, launch, plan_name, nullptr};
   return &v;
 }
 
@@ -523,7 +832,8 @@ const char* tg_gemm_grouped_fp8_plan(int64_t G, const int64_t* offsets, int64_t 
                        ssbg, C, ldc};
   if (tg::validate_grouped(c) != TG_SUCCESS) return nullptr;
   if (G == 0 || offsets[G] == offsets[0] || N == 0) return "none";
-  return tg::grouped_tiled(c) ? "grouped_tile_fp8_256x128" : "per_group";
+  if (!tg::grouped_tiled(c)) return "per_group";
+  return tg::grouped_wide(c) ? "grouped_tile_fp8_256x256" : "grouped_tile_fp8_256x128";
 }
 
 }  // extern "C"

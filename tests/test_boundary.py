@@ -248,6 +248,10 @@ def test_grouped_fp8_noop_and_plans(lib):
         assert _grouped8(lib, **kw) == tg.TG_SUCCESS
         assert _grouped8(lib, plan=True, **kw) == "none"
     assert _grouped8(lib, plan=True) == "grouped_tile_fp8_256x128"
+    # 8 x 1024 rows x 4096 columns: 32 tile rows, 512 tiles of 256 x 256 (2 rounds on 256
+    # CUs) against 1024 of 256 x 128 (4 rounds)
+    wide = dict(G=8, off=[1024 * g for g in range(9)], N=4096, ldc=4096, sbg=4096 * 128)
+    assert _grouped8(lib, plan=True, **wide) == "grouped_tile_fp8_256x256"
     assert _grouped8(lib, plan=True, lda=136) == "per_group"       # rows not 16-byte multiples
     assert _grouped8(lib, plan=True, sbg=64 * 128 + 8) == "per_group"
 
@@ -277,7 +281,7 @@ EXPECTED_PLANS = {
     "bf16_4096": ("tile_nn_256x256", "tile_nn_256x256"),
     "bf16_4096x7168x16384": ("tile_nt_256x224", "tile_nt_256x224"),
     "bf16_skinny_64x7168x7168": ("skinny_64x32", "skinny_64x128_splitk4"),
-    "fp8_4096x7168x16384": ("tile_fp8_256x128", "tile_fp8_256x128"),
+    "fp8_4096x7168x16384": ("tile_fp8_256x256", "tile_fp8_256x256"),
 }
 
 
@@ -342,6 +346,28 @@ def test_workload_plans(lib, name):
     assert tg.tg_gemm_plan(*args) == EXPECTED_PLANS[name][0]
     assert tg.tg_gemm_plan_ws(*args, _ws_bytes(op, w.M, w.N, w.K, sbk, sbn)) == \
         EXPECTED_PLANS[name][1]
+
+
+# The fp8 tile shape by grid size: 256 x 256 tiles unless 256 x 128 tiles take
+# fewer tile rounds on 256 CUs, a round of 256 x 256 counting 4/3 of one of
+# 256 x 128 (64 against 48 KiB moved per slice).
+FP8_TILE_PLANS = [
+    ((256, 128, 128), "tile_fp8_256x128"),      # 1 tile either way
+    ((2048, 2048, 1024), "tile_fp8_256x128"),   # 64 or 128 tiles: one round each
+    ((1024, 8192, 512), "tile_fp8_256x128"),    # 128 or 256 tiles: one round each
+    ((4096, 4096, 256), "tile_fp8_256x256"),    # 256 tiles (1 round) or 512 (2)
+    ((4000, 4000, 400), "tile_fp8_256x256"),
+    ((4097, 4000, 16), "tile_fp8_256x256"),     # 272 (2 rounds) or 544 (3)
+    ((4096, 3968, 1040), "tile_fp8_256x256"),   # 256 or 496
+    ((2500, 7000, 2064), "tile_fp8_256x256"),   # 280 or 550
+    ((4096, 7168, 16384), "tile_fp8_256x256"),  # 448 (2 rounds) or 896 (4)
+]
+
+
+@pytest.mark.parametrize("case", FP8_TILE_PLANS, ids=[f"{m}x{n}x{k}" for (m, n, k), _ in FP8_TILE_PLANS])
+def test_fp8_tile_plans(lib, case):
+    (M, N, K), want = case
+    assert tg.tg_gemm_plan(tg.OP_FP8, M, N, K, PA, K, 1, PB, 1, K, PC, N, 1) == want
 
 
 def test_workspace_sizes(lib):

@@ -216,7 +216,7 @@ def test_grouped_fp8_workload_sampled():
     rows = gen.sample_rows(w["rows"], 256, w["seed"])
     x = _fp8_inputs(w["rows"], w["G"], N, K, w["seed"])
     c, plan = _run_fp8(offsets, N, K, *x)
-    assert plan == "grouped_tile_fp8_256x128", plan
+    assert plan == "grouped_tile_fp8_256x256", plan
     C_ref, S = _ref_fp8(offsets, N, K, *x, rows=rows)
     H.assert_within_bound("bf16", c[rows], C_ref, S, f"grouped fp8 workload [{plan}]")
     x = _fp8_inputs(w["rows"], w["G"], N, K, w["seed"], int_r=16)

@@ -244,6 +244,34 @@ def test_fp8_small(layout, shape):
                exact=True, what="int pow2 scales")
 
 
+# Shapes the 256 x 256 fp8 tiles take (grids large enough): ragged M, N and K,
+# N not a multiple of 256 (the last tile's second half has no B scale row) or
+# of 128, one partial slice.  Rows checked: the first and last 40 (ragged
+# last tile row) and 128 seeded ones, every column of each.
+FP8_WIDE_CASES = [(4000, 4000, 400), (4096, 3968, 1040), (4097, 4000, 16), (2500, 7000, 2064)]
+
+
+def _edge_rows(M, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([np.arange(min(40, M)), np.arange(max(0, M - 40), M),
+                           rng.choice(M, size=min(128, M), replace=False)])
+    return np.unique(rows)
+
+
+@pytest.mark.parametrize("case", FP8_WIDE_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in FP8_WIDE_CASES])
+def test_fp8_wide_tile(case):
+    M, N, K = case
+    rows = _edge_rows(M, M + N + K)
+    plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 1500 + M + K), rows=rows, what="wide bound")
+    assert plan == "tile_fp8_256x256", plan
+    plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 1600 + M + K, int_r=16), rows=rows,
+                      exact=True, what="wide int unit scales")
+    assert plan == "tile_fp8_256x256", plan
+    plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 1700 + M + K, int_r=4, pow2_scales=True),
+                      rows=rows, exact=True, what="wide int pow2 scales")
+    assert plan == "tile_fp8_256x256", plan
+
+
 def test_fp8_workload_bound():
     w = configs.WORKLOADS["fp8_4096x7168x16384"]
     d = configs.make_inputs(w)
