@@ -41,6 +41,7 @@
 #include "../../include/tg_gemm.h"
 
 #include <initializer_list>
+#include <type_traits>
 #include <utility>
 
 #include "tile_mfma.hpp"
@@ -382,49 +383,67 @@ __global__ __launch_bounds__(64 * F_WAVES) void gemm_fp8_grouped(GemmArgs a, Gro
 //    scale per lane and row block (4 per slice) instead of 16;
 //  - intervals separated by workgroup barriers: in each interval one group
 //    multiplies a slice (32 MFMAs and the fold-ins, reading the B fragments
-//    of the slice from LDS one column block at a time, two ahead of use)
-//    while the other reads the next slice's A fragments and row scales into
-//    registers and issues its share of the loads of the next slice;
-//  - LDS: two stages of A (256 rows x 128 bytes, then the slice's 256 A-row
-//    scales and the tile's two B scales) and two of B (256 x 128 bytes),
-//    130.5 KiB; group 0 loads every A stage with its scales, group 1 every B
-//    stage, each one slice ahead of use.
-// Interval t follows barrier t.  Group 0 reads A(j) in interval 2j and
-// multiplies slice j in 2j + 1; group 1 reads A(j) in 2j + 1 and multiplies
-// in 2j + 2.  So A stage j % 2 is free after barrier 2j + 2 (group 0 refills
-// it with slice j + 2 in interval 2j + 2 and waits for it before barrier
-// 2j + 4), and B stage j % 2 after barrier 2j + 3 (group 1 refills it with
-// slice j + 2 in interval 2j + 3 and waits for it before barrier 2j + 5,
-// ahead of group 0's multiply of slice j + 2).  Each group passes 2 nk + 2
-// barriers (group 0's last one waits for group 1's last multiply: with no
-// conditional barrier in either loop, each loop body is one basic block, and
-// the compiler cannot sink the MFMAs of a multiply past the barrier that
-// ends it).
+//    of its columns from LDS one 16-column block at a time, two blocks ahead)
+//    while the other reads the next slice's A fragments, row scales and first
+//    two B blocks into registers and issues its loads;
+//  - LDS: a ring of two A stages (256 rows x 128 bytes, then the slice's 256
+//    A-row scales and the tile's two B scales), loaded by group 0, and one
+//    ring per group of its 128 B rows (16 KiB a stage), B0_ST stages loaded
+//    by group 0 and B1_ST by group 1.  A group's B rows are read by that
+//    group alone, so their stage is free as soon as its own multiply ends,
+//    which gives each B load more time in flight than a ring shared by both
+//    groups.
+// Interval t follows barrier t.  Group 0 reads slice j (A, scales, its first
+// B blocks) in interval 2j and multiplies it in 2j + 1; group 1 reads it in
+// 2j + 1 and multiplies it in 2j + 2.  So:
+//  - A stage j % 2 is free after barrier 2j + 2: group 0 refills it with
+//    slice j + 2 in interval 2j + 2 and waits for it before barrier 2j + 4;
+//  - group 0's B stage of slice j is free after barrier 2j + 2: group 0
+//    refills it with slice j + B0_ST in interval 2j + 2, needed before
+//    barrier 2 (j + B0_ST);
+//  - group 1's B stage of slice j is free after barrier 2j + 3: group 1
+//    refills it with slice j + B1_ST in interval 2j + 3, needed before
+//    barrier 2 (j + B1_ST) + 1.
+// Each group passes 2 nk + 2 barriers (group 0's last one waits for group 1's
+// last multiply: with no conditional barrier in either loop, each loop body
+// is one basic block, and the compiler cannot sink the MFMAs of a multiply
+// past the barrier that ends it).
 constexpr int Q_BM = 256, Q_BN = 256, Q_BK = 128;
 constexpr int Q_ROW = 128;                            // bytes of k per staged row
-constexpr int Q_A_BYTES = Q_BM * Q_ROW, Q_B_BYTES = Q_BN * Q_ROW;
+constexpr int Q_A_BYTES = Q_BM * Q_ROW;               // 32 KiB
+constexpr int Q_H_BYTES = Q_BN / 2 * Q_ROW;           // one group's B rows: 16 KiB
 constexpr int Q_SA = Q_A_BYTES;                       // A-row scales of the slice
 constexpr int Q_SB = Q_A_BYTES + 1024;                // the tile's two B scales
 constexpr int Q_ASTAGE = Q_A_BYTES + 1024 + 256;
-constexpr int Q_LDS = 2 * Q_ASTAGE + 2 * Q_B_BYTES;
-constexpr int Q_LOADS = Q_A_BYTES / 1024 / 4;         // 1 KiB loads per wave per slice
+constexpr int Q_A_LOADS = Q_A_BYTES / 1024 / 4;       // 1 KiB loads per wave per slice
+constexpr int Q_B_LOADS = Q_H_BYTES / 1024 / 4;
 constexpr int Q_FM = 4, Q_FN = 8;                     // 16 x 16 blocks of a wave tile
 constexpr int Q_LAG = 3;                              // MFMAs between a block and its fold-in
 constexpr int Q_NB = 3;                               // B fragment buffers
-static_assert(Q_LDS <= 160 * 1024, "stages must fit the LDS");
+constexpr int Q_B0_ST = 3, Q_B1_ST = 2;
 static_assert(Q_ASTAGE % 256 == 0, "stage bases on whole bank rows");
+
+template <int B0_ST, int B1_ST>
+struct QLds {
+  static constexpr int B0 = 2 * Q_ASTAGE;                   // group 0's B ring
+  static constexpr int B1 = B0 + B0_ST * Q_H_BYTES;         // group 1's B ring
+  static constexpr int BYTES = B1 + B1_ST * Q_H_BYTES;
+  static_assert(BYTES <= 160 * 1024, "stages must fit the LDS");
+};
 
 __device__ __forceinline__ void load_lds4(const i32x4& desc, uint32_t lds, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :: "s"(lds), "v"(voff), "s"(desc) : "memory");
 }
 
+template <int B0_ST = Q_B0_ST, int B1_ST = Q_B1_ST>
 __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
-  char* const lds = fp8_lds<Q_LDS>();
+  static_assert(B0_ST >= 2 && B1_ST >= 2, "at least two stages per B ring");
+  typedef QLds<B0_ST, B1_ST> L;
+  char* const lds = fp8_lds<L::BYTES>();
   const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
   auto a_off = [](int st) { return st * Q_ASTAGE; };
-  auto b_off = [](int st) { return 2 * Q_ASTAGE + st * Q_B_BYTES; };
 
   const int64_t m0 = (int64_t)tm * Q_BM, n0 = (int64_t)tn * Q_BN;
   const int lane = threadIdx.x & 63;
@@ -433,15 +452,20 @@ __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
   const int K = (int)a.K;
   const int nkb = (K + Q_BK - 1) / Q_BK;
   const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
+  // this group's B ring
+  const int b_ring = g == 0 ? L::B0 : L::B1;
+  auto b_off = [&](int st) { return b_ring + st * Q_H_BYTES; };
 
-  // Code tiles as descriptors ending at the last valid row; the tile's
-  // scales: A rows m0 .. (SA[i, kb] at i * ssam + kb * ssak floats) and B
-  // scale rows n0 / 128 and n0 / 128 + 1 (the second only if N reaches it).
-  const int rows_a = (int)min<int64_t>(Q_BM, a.M - m0), rows_b = (int)min<int64_t>(Q_BN, a.N - n0);
+  // Code tiles as descriptors ending at the last valid row (A rows m0 ..,
+  // this group's B rows n0 + 128 g ..); the tile's scales: A rows m0 ..
+  // (SA[i, kb] at i * ssam + kb * ssak floats) and B scale rows n0 / 128 and
+  // n0 / 128 + 1 (the second only if N reaches it).
+  const int rows_a = (int)min<int64_t>(Q_BM, a.M - m0);
+  const int rows_b = (int)max<int64_t>(0, min<int64_t>(Q_BN / 2, a.N - n0 - 128 * g));
   const uint8_t* Ab = static_cast<const uint8_t*>(a.A) + m0 * a.sam;
-  const uint8_t* Bb = static_cast<const uint8_t*>(a.B) + n0 * a.sbn;
+  const uint8_t* Bb = static_cast<const uint8_t*>(a.B) + (n0 + 128 * g) * a.sbn;
   const i32x4 ra = make_desc(Ab, (uint32_t)((rows_a - 1) * lda + K));
-  const i32x4 rb = make_desc(Bb, (uint32_t)((rows_b - 1) * ldb + K));
+  const i32x4 rb = make_desc(Bb, rows_b > 0 ? (uint32_t)((rows_b - 1) * ldb + K) : 0u);
   const int nsb = (int)min<int64_t>(2, cdiv(a.N, 128) - n0 / 128);
   const float* SAb = a.SA + m0 * a.ssam;
   const float* SBb = a.SB + (n0 / 128) * a.ssbn;
@@ -451,18 +475,21 @@ __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
   // Code loads: wave q's i-th load of a stage fills rows 32 i + 8 q .. + 7;
   // lane l writes row 32 i + 8 q + (l >> 3) at chunk position l & 7, i.e.
   // logical chunk (l & 7) ^ (4 (q & 1) + (l >> 4)) (swizzle c ^ ((r >> 1) & 7)).
-  // Rows past the tile's last valid row fall outside the descriptor (zeros).
+  // Rows past the last valid row fall outside the descriptor (zeros).
   const uint32_t lrow = 8 * q + (lane >> 3);
   const uint32_t lchunk = (lane & 7) ^ (4 * (q & 1) + (lane >> 4));
-  const uint32_t ld = g == 0 ? lda : ldb;
-  const uint32_t l_lane = lrow * ld + 16 * lchunk, l_step = 32 * ld;
-  auto load_codes = [&](const i32x4& desc, uint32_t base, int kb) {
+  auto load_rows = [&](const i32x4& desc, uint32_t ld, uint32_t base, int kb, auto n_loads) {
     const int k0 = kb * Q_BK;
     const bool kin = k0 + 16 * (int)lchunk < K;
+    const uint32_t lane_off = lrow * ld + 16 * lchunk + (uint32_t)k0;
 #pragma unroll
-    for (int i = 0; i < Q_LOADS; ++i)
-      load_lds16(desc, base + i * 4096, kin ? l_lane + i * l_step + (uint32_t)k0 : kOutOfRange);
+    for (int i = 0; i < decltype(n_loads)::value; ++i)
+      load_lds16(desc, base + i * 4096, kin ? lane_off + i * 32 * ld : kOutOfRange);
   };
+  typedef std::integral_constant<int, Q_A_LOADS> NA;
+  typedef std::integral_constant<int, Q_B_LOADS> NB;
+  auto load_a = [&](int st, int kb) { load_rows(ra, lda, lds32 + a_off(st) + q * 1024, kb, NA()); };
+  auto load_b = [&](int st, int kb) { load_rows(rb, ldb, lds32 + b_off(st) + q * 1024, kb, NB()); };
   // Scale loads (group 0): wave q the A-row scales of rows 64 q + l, wave 0
   // lanes 0-1 also the two B scales; everything else reads zeros.
   const int sa_row = 64 * q + lane;
@@ -489,7 +516,7 @@ __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
     const i32x4 hi = *reinterpret_cast<const i32x4*>(p + rd1);
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  const int a_rd = 64 * q * Q_ROW, b_rd = 128 * g * Q_ROW;
+  const int a_rd = 64 * q * Q_ROW;
   const int s_rd = Q_SA + (64 * q + (lane & 15)) * 4;
 
   // acc[j][i]: block of tile columns 16 j .. (this group's) and rows 16 i ..
@@ -501,16 +528,19 @@ __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
     for (int i = 0; i < Q_FM; ++i) acc[j][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   i32x8 fa[Q_FM], fb[Q_NB];
   float s[Q_FM];  // SA[row] * SB of this lane's rows for the slice
-  auto read_a = [&](int st) {
-    const char* base = lds + a_off(st);
+  auto read_b = [&](int st, int j) { return rd32(lds + b_off(st) + j * 16 * Q_ROW); };
+  // A fragments, scales and the first two B blocks of a slice
+  auto read_slice = [&](int sta, int stb) {
+    const char* base = lds + a_off(sta);
 #pragma unroll
     for (int i = 0; i < Q_FM; ++i) fa[i] = rd32(base + a_rd + i * 16 * Q_ROW);
     const float sb = *reinterpret_cast<const float*>(base + Q_SB + 4 * g);
 #pragma unroll
     for (int i = 0; i < Q_FM; ++i)
       s[i] = *reinterpret_cast<const float*>(base + s_rd + 64 * i) * sb;
+    fb[0] = read_b(stb, 0);
+    fb[1] = read_b(stb, 1);
   };
-  auto read_b = [&](int st, int j) { return rd32(lds + b_off(st) + b_rd + j * 16 * Q_ROW); };
   // Step boundary of the multiply: the empty asm with a memory clobber keeps
   // the LDS reads where they are written (a scheduling fence alone lets
   // instruction selection hoist all of them to the top, which needs 40 more
@@ -523,8 +553,6 @@ __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
   // and the fold-in of MFMA n - Q_LAG follows it; the fragments of column
   // block j + 2 are read when block j's first MFMA has been issued.
   auto multiply = [&](int st) {
-    fb[0] = read_b(st, 0);
-    fb[1] = read_b(st, 1);
     f32x4 p[Q_LAG + 1];
 #pragma unroll
     for (int n = 0; n < Q_FN * Q_FM + Q_LAG; ++n) {
@@ -551,48 +579,63 @@ __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  auto wait_loads = [] {
+  // wait until at most N of this wave's loads are in flight
+  auto wait_loads = [](auto n) {
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(decltype(n)::value) : "memory");
   };
 
   if (g == 0) {
-    load_codes(ra, lds32 + a_off(0) + q * 1024, 0);
+    // Per iteration j: A(j + 1) with its scales, then B0(j + B0_ST - 1).
+    // Before barrier 2j + 2, A(j + 1) and B0(j + 1) must have landed: B0(j +
+    // 1) was issued B0_ST - 2 iterations back, so the B0 loads of the last
+    // B0_ST - 2 iterations may stay in flight (scale loads precede them).
+    load_a(0, 0);
     load_scales(0, 0);
-    wait_loads();
+#pragma unroll
+    for (int x = 0; x < B0_ST - 1; ++x) load_b(x, x);
+    wait_loads(std::integral_constant<int, (B0_ST - 2) * Q_B_LOADS>());
     barrier();                                   // 0
-    int st = 0;
+    int sta = 0, stb = 0;
     for (int j = 0; j < nkb; ++j) {
-      const int nst = st ^ 1;
-      load_codes(ra, lds32 + a_off(nst) + q * 1024, j + 1);  // into slice j - 1's stage
-      load_scales(nst, j + 1);
-      read_a(st);
+      const int nsta = sta ^ 1, lstb = stb == 0 ? B0_ST - 1 : stb - 1;
+      load_a(nsta, j + 1);                       // into slice j - 1's stage
+      load_scales(nsta, j + 1);
+      load_b(lstb, j + B0_ST - 1);               // into slice j - 1's stage
+      read_slice(sta, stb);
       wait_lds();
       barrier();                                 // 2j + 1
-      multiply(st);
-      wait_loads();
+      multiply(stb);
+      wait_loads(std::integral_constant<int, (B0_ST - 2) * Q_B_LOADS>());
       barrier();                                 // 2j + 2
-      st = nst;
+      sta = nsta;
+      stb = stb + 1 == B0_ST ? 0 : stb + 1;
     }
     barrier();                                   // 2 nk + 1: group 1's last multiply
   } else {
-    load_codes(rb, lds32 + b_off(0) + q * 1024, 0);
-    wait_loads();
+    // Per iteration j: B1(j + B1_ST - 1).  Before barrier 2j + 3, B1(j + 1)
+    // must have landed: issued B1_ST - 2 iterations back.
+#pragma unroll
+    for (int x = 0; x < B1_ST - 1; ++x) load_b(x, x);
+    wait_loads(std::integral_constant<int, (B1_ST - 2) * Q_B_LOADS>());
     barrier();                                   // 0
     barrier();                                   // 1
-    int st = 0;
+    int sta = 0, stb = 0;
     for (int j = 0; j < nkb; ++j) {
-      const int nst = st ^ 1;
-      load_codes(rb, lds32 + b_off(nst) + q * 1024, j + 1);  // into slice j - 1's stage
-      read_a(st);
+      const int lstb = stb == 0 ? B1_ST - 1 : stb - 1;
+      load_b(lstb, j + B1_ST - 1);               // into slice j - 1's stage
+      read_slice(sta, stb);
       wait_lds();
       barrier();                                 // 2j + 2
-      multiply(st);
-      wait_loads();                              // B(j + 1) before group 0 multiplies it
+      multiply(stb);
+      wait_loads(std::integral_constant<int, (B1_ST - 2) * Q_B_LOADS>());
       barrier();                                 // 2j + 3
-      st = nst;
+      sta ^= 1;
+      stb = stb + 1 == B1_ST ? 0 : stb + 1;
     }
   }
+  // loads past the last slice (zeros) land before the LDS is released
+  wait_loads(std::integral_constant<int, 0>());
 
   // Epilogue: round each accumulator to bf16 and store it inside M x N.
   __bf16* C = static_cast<__bf16*>(a.C);
