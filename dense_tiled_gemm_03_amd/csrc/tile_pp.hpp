@@ -110,31 +110,35 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
     for (int i = 0; i < Cfg::A_LOADS; ++i)
       load_lds16(ra, base + i * 4096, kin ? l_lane + i * l_step + 2 * k0 : kOutOfRange);
   };
-  // K x N B: the stage holds B as 64 k-rows of 512 bytes (32 chunks);
-  // chunk c of k-row k sits at position c ^ kn_swz(k), kn_swz(k) =
-  // 4 (k & 3) + 2 ((k >> 3) & 1).  The transpose reads of one instruction's
-  // first (last) 32 lanes cover k-rows 8u + r (u = 0, 1, or 2, 3; r < 4) of
-  // a 16-column block; with this swizzle their eight 32-byte pieces fall on
-  // eight different 32-byte bank groups (4 (k & 3) alone, the swizzle of
-  // the four-wave kernel, maps rows r and 8 + r to the same banks).  Wave
-  // q's i-th load fills k-rows 8i + 2q and + 1; lane l writes k-row 8i + 2q
-  // + (l >> 5) at position l & 31, i.e. logical chunk (l & 31) ^ kn_swz of
-  // that row = (l & 31) ^ (4 ((2q + (l >> 5)) & 3) + 2 (i & 1)).  k-rows
-  // past K are fetched out of range (zeros).
-  const int nrow = lane >> 5;
-  const uint32_t nswz = 4 * ((2 * q + nrow) & 3);
-  const uint32_t nb_lane0 = (uint32_t)(2 * q + nrow) * ldb * 2 + 16 * ((lane & 31) ^ nswz);
-  const uint32_t nb_lane1 = (uint32_t)(2 * q + nrow) * ldb * 2 + 16 * ((lane & 31) ^ (nswz + 2));
+  // K x N B: the stage holds the tile's 256 columns as four quarters of 64
+  // columns, quarter Q at Q * 8 KiB, each 64 k-rows of 128 bytes (8 chunks of
+  // 16 bytes); chunk c of k-row k sits at position c ^ 2 t(k), t(k) =
+  // ((k >> 1) & 1) | (((k >> 3) & 1) << 1).  Every load fills 1 KiB: 8
+  // consecutive k-rows of one quarter, 8 rows of 128 bytes from B as in the
+  // N x K layout (a load over 2 k-rows of 512 bytes measured 6 % slower).
+  // Wave q's i-th load fills quarter i & 3, k-rows 8 G .. + 7 with G = 2q +
+  // (i >> 2); lane l writes k-row 8 G + (l >> 3) at position l & 7, i.e.
+  // logical chunk (l & 7) ^ 2 t = (l & 7) ^ (2 ((l >> 4) & 1) + 4 (G & 1)).
+  // k-rows past K are fetched out of range (zeros).
+  uint32_t nb_lane[2] = {0u, 0u};
+  if constexpr (BKN) {
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const uint32_t kr = 16 * q + 8 * hi + (lane >> 3);
+      const uint32_t c = (lane & 7) ^ (2 * ((lane >> 4) & 1) + 4 * hi);
+      nb_lane[hi] = kr * ldb * 2 + 16 * c;
+    }
+  }
   auto load_b = [&](int slot, int k0) {
     const bool kin = k0 + 8 * lchunk < K;
     const uint32_t base = lds32 + b_off(slot) + q * 1024;
 #pragma unroll
     for (int i = 0; i < Cfg::B_LOADS; ++i) {
       if constexpr (BKN) {
-        const bool rin = k0 + 8 * i + 2 * q + nrow < K;
-        const uint32_t nb_lane = (i & 1) ? nb_lane1 : nb_lane0;
-        load_lds16(rb, base + i * 4096, rin ? nb_lane + (uint32_t)(8 * i + k0) * ldb * 2
-                                            : kOutOfRange);
+        const int hi = i >> 2, quarter = i & 3;
+        const bool rin = k0 + 16 * q + 8 * hi + (lane >> 3) < K;
+        load_lds16(rb, lds32 + b_off(slot) + quarter * 8192 + (2 * q + hi) * 1024,
+                   rin ? nb_lane[hi] + (uint32_t)k0 * ldb * 2 + quarter * 128 : kOutOfRange);
       } else {
         load_lds16(rb, base + i * 4096, kin ? l_lane + i * l_step + 2 * k0 : kOutOfRange);
       }
@@ -158,32 +162,38 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   // K x N B fragments (ds_read_b64_tr_b16, as in tile_body): within each
   // 16-lane group, lane 4r + q' supplies the address of columns 4q' .. +3 of
   // k-row r of a 4-row group, and lane i receives column i of those rows;
-  // lane l of group u = l / 16 points at k-row 32 s + 8u + 4h + r of the
-  // slice, columns nbase + 4q', and the two reads (h = 0, 1) give its 8
-  // k-values.  kn_swz of that k-row is 4r + 2 (u & 1) whatever s and h, so
-  // the offsets within a stage do not depend on the sub-step or the slice.
-  constexpr int BROW = BN * 2;
-  int kn_off[BKN ? FN : 1][2];
+  // lane l of group u = l / 16 points at k-row k = 32 s + 8u + 4h + r of the
+  // slice, columns 128 g + 16 j + 4q', and the two reads (h = 0, 1) give its
+  // 8 k-values.  In the layout above that is quarter 2g + (j >> 2), chunk
+  // 2 (j & 3) + (q' >> 1) and t(k) = ((r >> 1) & 1) | ((u & 1) << 1), so the
+  // address within a stage is
+  //   8 KiB (2g + (j >> 2)) + 128 k + 32 ((j & 3) ^ t) + 16 (q' >> 1) + 8 (q' & 1)
+  // and bits 5-6 hold (j & 3) ^ t alone: the lane keeps kn_d = the address for
+  // s = h = j = 0 and XORs 32 (j & 3) into the address after adding the
+  // stage base, the sub-step, h and the quarter (all multiples of 512 bytes;
+  // the XOR after the loop-varying stage base also keeps the compiler from
+  // hoisting 16 offsets per lane into registers for the whole loop).  Each
+  // half-wave's 32 lanes then read 32 distinct 8-byte pairs of banks (eight
+  // k-rows: r & 1 picks the 128-byte half of the 256-byte bank row, t the
+  // 32-byte group within it).
+  constexpr int BROW = 128;
+  uint32_t kn_d = 0u;
   if constexpr (BKN) {
+    static_assert(Cfg::WTN == 128, "K x N tiles are 256 columns wide");
     const int u = lane >> 4, r = (lane >> 2) & 3, qq = lane & 3;
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kr = 8 * u + 4 * h + r;
-        const int nbase = g * Cfg::WTN + j * 16;
-        const int chunk = ((nbase >> 3) ^ (4 * r + 2 * (u & 1))) + (qq >> 1);
-        kn_off[j][h] = kr * BROW + chunk * 16 + (qq & 1) * 8;
-      }
+    const int t = ((r >> 1) & 1) | ((u & 1) << 1);
+    kn_d = 16384 * g + (8 * u + r) * BROW + 32 * t + 16 * (qq >> 1) + 8 * (qq & 1);
   }
   typedef short i16x4 __attribute__((ext_vector_type(4)));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
-  auto read_b_kn = [&](const char* stage_base, int sub, int j) {
-    const char* p = stage_base + sub * 32 * BROW;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  auto read_b_kn = [&](int stage, int sub, int j) {
+    // multiples of 512 bytes: the stage base, the sub-step's 32 k-rows, the quarter
+    const uint32_t base = lds32 + b_off(stage) + sub * 32 * BROW + 8192 * (j >> 2) + kn_d;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(p + kn_off[j][0]));
+        (lds_i16x4*)(uintptr_t)(base ^ (32u * (j & 3))));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(p + kn_off[j][1]));
+        (lds_i16x4*)(uintptr_t)((base + 4 * BROW) ^ (32u * (j & 3))));
     const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(T8, v);
   };
@@ -200,7 +210,7 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         if constexpr (BKN)
-          fb[s][j] = read_b_kn(lds + b_off(sb), s, j);
+          fb[s][j] = read_b_kn(sb, s, j);
         else
           fb[s][j] = *reinterpret_cast<const T8*>(bb + j * 16 * Cfg::ROW_BYTES + ch[s]);
       }
