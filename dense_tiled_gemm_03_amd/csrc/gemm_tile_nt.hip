@@ -42,6 +42,9 @@ bool accepts(Op op, const GemmArgs& a) {
 }
 
 constexpr int64_t kCus = 256;
+// Split K on the eight-wave 256 x 224 kernels: at most 7 splits (with 8, the
+// combine of the partials spills about 660 VGPRs beside the accumulators).
+constexpr int kMaxSplitsPP = 7;
 constexpr int64_t kShortK = 128;  // K slices (of 64) up to which small grids take 128 x 128
 
 // A grid of 256 x 224 tiles is small when it fills at most half the CUs.
@@ -65,6 +68,7 @@ int splits_for(const GemmArgs& a) {
   const int64_t nk = cdiv(a.K, 64);
   int64_t s = kCus / tiles;
   if (s > tile::kMaxSplits) s = tile::kMaxSplits;
+  if (!std::is_same<Cfg, Tile128>::value && s > kMaxSplitsPP) s = kMaxSplitsPP;
   if (std::is_same<Cfg, Tile128>::value) {
     if (s > nk / 16) s = nk / 16;
   } else {
@@ -93,7 +97,7 @@ int splits_for(const GemmArgs& a) {
 // 1.75 waves rounded up to 2).
 double cost(const GemmArgs& a, int64_t bm, int64_t bn, bool split_ok) {
   const int64_t tiles = cdiv(a.M, bm) * cdiv(a.N, bn), nk = cdiv(a.K, 64);
-  const int s = bn == 224 && split_ok ? tile::tail_splits(tiles, nk, kCus) : 1;
+  const int s = bn == 224 && split_ok ? tile::tail_splits(tiles, nk, kCus, kMaxSplitsPP) : 1;
   return tile::tail_waves(tiles, nk, kCus, s) * double(bm * bn);
 }
 enum class Shape { T128, T128x2, T224, T256 };
@@ -122,7 +126,8 @@ Plan plan_of(const GemmArgs& a, bool split_ok) {
   } else if (cost(a, 256, 224, split_ok) < cost(a, 256, 256, split_ok)) {
     p.shape = Shape::T224;
     if (split_ok) {
-      p.splits = tile::tail_splits(cdiv(a.M, 256) * cdiv(a.N, 224), cdiv(a.K, 64), kCus);
+      p.splits = tile::tail_splits(cdiv(a.M, 256) * cdiv(a.N, 224), cdiv(a.K, 64), kCus,
+                                   kMaxSplitsPP);
       p.tail = p.splits > 1;
     }
   }
@@ -151,29 +156,60 @@ Plan choose(const GemmArgs& a, const Scratch& ws) {
 
 size_t scratch_bytes(const GemmArgs& a) { return plan_of(a, true).bytes; }
 
+// A split plan of 256 x 224 tiles on the eight-wave kernels, S splits per
+// split tile (S is a template parameter of the kernels: one combine per
+// kernel).  Tail plans split only the tiles past the first whole wave.
+template <int S>
+hipError_t launch_pp_split(Op op, const GemmArgs& a, const Plan& p, const Scratch& ws, int tm,
+                           int tn, hipStream_t s) {
+  int* counters = reinterpret_cast<int*>(ws.ptr);
+  float* part = reinterpret_cast<float*>(ws.ptr + kWorkspaceCounterBytes);
+  const dim3 block(512);
+  if (p.tail) {
+    // whole tiles of the first wave, then the split tiles' units
+    const int tiles = tm * tn, tail = tiles % (int)kCus, full = tiles - tail;
+    const dim3 grid((unsigned)(full + tail * S));
+    if (op == Op::BF16)
+      hipLaunchKernelGGL((tile::gemm16_pp_tail<__bf16, PP224, S>), grid, block, 0, s, a, tm, tn,
+                         full, part, counters);
+    else
+      hipLaunchKernelGGL((tile::gemm16_pp_tail<_Float16, PP224, S>), grid, block, 0, s, a, tm, tn,
+                         full, part, counters);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)(tm * tn * S));
+  if (op == Op::BF16)
+    hipLaunchKernelGGL((tile::gemm16_pp_splitk<__bf16, PP224, S>), grid, block, 0, s, a, tm, tn,
+                       part, counters);
+  else
+    hipLaunchKernelGGL((tile::gemm16_pp_splitk<_Float16, PP224, S>), grid, block, 0, s, a, tm, tn,
+                       part, counters);
+  return hipGetLastError();
+}
+
 template <typename Cfg>
 hipError_t launch_cfg(Op op, const GemmArgs& a, const Plan& p, const Scratch& ws, hipStream_t s) {
   const int tm = (int)cdiv(a.M, Cfg::BM), tn = (int)cdiv(a.N, Cfg::BN);
-  if constexpr (std::is_same<Cfg, Tile224>::value || std::is_same<Cfg, Tile128>::value) {
+  if constexpr (std::is_same<Cfg, Tile224>::value) {
+    if (p.splits > 1) {
+      // split-K and partial-wave tiles run the eight-wave form as well; its
+      // fp32 partial tile takes the same 256 x 224 x 4 bytes per split
+      switch (p.splits) {
+        case 2: return launch_pp_split<2>(op, a, p, ws, tm, tn, s);
+        case 3: return launch_pp_split<3>(op, a, p, ws, tm, tn, s);
+        case 4: return launch_pp_split<4>(op, a, p, ws, tm, tn, s);
+        case 5: return launch_pp_split<5>(op, a, p, ws, tm, tn, s);
+        case 6: return launch_pp_split<6>(op, a, p, ws, tm, tn, s);
+        case 7: return launch_pp_split<7>(op, a, p, ws, tm, tn, s);
+        default: return launch_pp_split<kMaxSplitsPP>(op, a, p, ws, tm, tn, s);
+      }
+    }
+  }
+  if constexpr (std::is_same<Cfg, Tile128>::value) {
     if (p.splits > 1) {
       int* counters = reinterpret_cast<int*>(ws.ptr);
       float* part = reinterpret_cast<float*>(ws.ptr + kWorkspaceCounterBytes);
-      const dim3 block(256);
-      if (p.tail) {
-        if constexpr (std::is_same<Cfg, Tile224>::value) {
-          // whole tiles of the first wave, then the split tiles' units
-          const int tiles = tm * tn, tail = tiles % (int)kCus, full = tiles - tail;
-          const dim3 grid((unsigned)(full + tail * p.splits));
-          if (op == Op::BF16)
-            hipLaunchKernelGGL((tile::gemm16_tile_tail<__bf16, Cfg>), grid, block, 0, s, a, tm,
-                               tn, full, p.splits, part, counters);
-          else
-            hipLaunchKernelGGL((tile::gemm16_tile_tail<_Float16, Cfg>), grid, block, 0, s, a, tm,
-                               tn, full, p.splits, part, counters);
-          return hipGetLastError();
-        }
-      }
-      const dim3 grid((unsigned)(tm * tn * p.splits));
+      const dim3 grid((unsigned)(tm * tn * p.splits)), block(256);
       if (op == Op::BF16)
         hipLaunchKernelGGL((tile::gemm16_tile_splitk<__bf16, Cfg>), grid, block, 0, s, a, tm, tn,
                            p.splits, part, counters);

@@ -338,11 +338,11 @@ inline double tail_waves(int64_t tiles, int64_t nk, int64_t cus, int s) {
 // 256 x 256 tiles, 6144 x 6144 x 4096), while one wave and a tail gained
 // about 10% (4352 x 4096 x 4096: 158 us unsplit, 142 us with the 67 tiles
 // past the first wave split 2 ways).
-inline int tail_splits(int64_t tiles, int64_t nk, int64_t cus) {
+inline int tail_splits(int64_t tiles, int64_t nk, int64_t cus, int max_splits = kMaxSplits) {
   if (tiles <= cus || tiles >= 2 * cus) return 1;
   int best = 1;
   double best_w = tail_waves(tiles, nk, cus, 1);
-  for (int s = 2; s <= kMaxSplits && nk / s >= 8; ++s) {
+  for (int s = 2; s <= max_splits && nk / s >= 8; ++s) {
     const double w = tail_waves(tiles, nk, cus, s);
     if (w < best_w) {
       best = s;
@@ -365,18 +365,18 @@ constexpr int split_part_q(int nq, int s, int budget) {
 // The tile's sum over its S split partials, in split order 0 .. S-1,
 // starting from zero, into acc, which holds split `me`'s own partial on
 // entry (so only the other S - 1 partials are read).  Partial float4 q of
-// thread t of split sp sits at float4 (sp * NQ + q) * 256 + t of rp, written
+// thread t (of THREADS) of split sp sits at float4 (sp * NQ + q) * THREADS + t of rp, written
 // with device-coherent stores by the other splits.  The thread's NQ float4s
 // go in parts of QP; each part's loads of every other split are issued
 // unconditionally one part ahead of the additions, so the wait before a
 // part's additions counts exactly the next part's loads.
-template <int S, int FM, int FN, typename Acc>
+template <int S, int THREADS, int BUDGET, int FM, int FN, typename Acc>
 __device__ __forceinline__ void sum_splits(Acc (&acc)[FM][FN], __amdgpu_buffer_rsrc_t rp, int me,
                                            int t) {
   constexpr int NV = sizeof(Acc) / 16, NQ = FM * FN * NV;
-  // two parts in flight next to the accumulators: 16 float4s per part with
-  // 224 accumulator registers, 8 with 256
-  constexpr int QP = split_part_q(NQ, S, NQ > 56 ? 8 : 16), NP = NQ / QP;
+  // two parts in flight next to the accumulators, at most BUDGET float4s
+  // each (the registers the accumulators leave)
+  constexpr int QP = split_part_q(NQ, S, BUDGET), NP = NQ / QP;
   f32x4 x[2][S - 1][QP];
   auto load_part = [&](f32x4(&dst)[S - 1][QP], int p) {
 #pragma unroll
@@ -386,7 +386,7 @@ __device__ __forceinline__ void sum_splits(Acc (&acc)[FM][FN], __amdgpu_buffer_r
       for (int u = 0; u < QP; ++u)
         dst[o][u] = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       rp, ((sp * NQ + p * QP + u) * 256 + t) * 16, 0, 0x10));
+                       rp, ((sp * NQ + p * QP + u) * THREADS + t) * 16, 0, 0x10));
     }
   };
   load_part(x[0], 0);
@@ -419,7 +419,66 @@ __device__ __forceinline__ void sum_splits(Acc (&acc)[FM][FN], __amdgpu_buffer_r
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][j][4 * c + e] = s[u][e];
     }
+    // keep each part's loads in their part: the scheduler would otherwise
+    // hoist later parts' loads and spill the registers they take
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// The split-K combine at the end of a tile's K range: publish this split's
+// fp32 partial tile -- accumulator float4 q of thread t at float4 index
+// (split * NQ + q) * THREADS + t of the tile's slots, 16-byte runs
+// contiguous across threads -- with device-coherent (sc1) stores; every wave
+// waits for its stores before the barrier that precedes the tile's counter
+// increment, so the split that finishes last reads every slot whole.  It
+// adds the partials in split order (the result does not depend on which
+// split finishes last) into acc, clears the counter and returns true; the
+// other splits return false.  Every thread of the workgroup calls it.
+// BUDGET: float4s of one part of the combine's loads (sum_splits).  S > 0:
+// the split count is S (sk.splits == S), one instance of the sum; S == 0:
+// a switch over sk.splits.  (Two or more instances of the sum in one
+// kernel beside 112 accumulator registers spill thousands of VGPRs, though
+// each alone fits; the eight-wave kernels take S from the host.)
+template <int THREADS, int BUDGET, int S = 0, int FM, int FN, typename Acc>
+__device__ __forceinline__ bool combine_splits(Acc (&acc)[FM][FN], const SplitK& sk, int t) {
+  constexpr int NV = sizeof(Acc) / 16, NQ = FM * FN * NV;
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      sk.part + (int64_t)sk.tile * sk.splits * NQ * THREADS * 4, (short)0,
+      sk.splits * NQ * THREADS * 16, 0x00020000);
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        const f32x4 x = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
+                         acc[i][j][4 * c + 3]};
+        const int q = (i * FN + j) * NV + c;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rp,
+                                               ((sk.split * NQ + q) * THREADS + t) * 16, 0, 0x10);
+      }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  __shared__ int last;
+  if (t == 0) last = atomicAdd(sk.counters + sk.tile, 1) == sk.splits - 1;
+  __syncthreads();
+  if (!last) return false;
+  if constexpr (S > 0) {
+    sum_splits<S, THREADS, BUDGET>(acc, rp, sk.split, t);
+  } else {
+  switch (sk.splits) {
+    case 2: sum_splits<2, THREADS, BUDGET>(acc, rp, sk.split, t); break;
+    case 3: sum_splits<3, THREADS, BUDGET>(acc, rp, sk.split, t); break;
+    case 4: sum_splits<4, THREADS, BUDGET>(acc, rp, sk.split, t); break;
+    case 5: sum_splits<5, THREADS, BUDGET>(acc, rp, sk.split, t); break;
+    case 6: sum_splits<6, THREADS, BUDGET>(acc, rp, sk.split, t); break;
+    case 7: sum_splits<7, THREADS, BUDGET>(acc, rp, sk.split, t); break;
+    default: sum_splits<kMaxSplits, THREADS, BUDGET>(acc, rp, sk.split, t); break;
+  }
+  }
+  if (t == 0) __hip_atomic_store(sk.counters + sk.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
 // The LDS array of the tile stages: one per size, so that the bodies of one
@@ -700,48 +759,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int tm, int tn,
   }
 
   if constexpr (SPLIT) {
-    // Publish this split's fp32 partial tile -- accumulator float4 q of
-    // thread t at float4 index (split * NQ + q) * 256 + t of the tile's
-    // slots, 16-byte runs contiguous across threads -- with device-coherent
-    // (sc1) stores; every wave waits for its stores before the barrier that
-    // precedes the tile's counter increment, so the split that finishes last
-    // reads every slot whole.  It adds the partials in split order (the
-    // result does not depend on which split finishes last), clears the
-    // counter and goes on to the epilogue with the sums.
-    constexpr int NV = MMA::NACC / 4, NQ = FM * FN * NV;
-    const int t = threadIdx.x;
-    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-        sk.part + (int64_t)sk.tile * sk.splits * NQ * 256 * 4, (short)0,
-        sk.splits * NQ * 256 * 16, 0x00020000);
-    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int c = 0; c < NV; ++c) {
-          const f32x4 x = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
-                           acc[i][j][4 * c + 3]};
-          const int q = (i * FN + j) * NV + c;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rp,
-                                                 ((sk.split * NQ + q) * 256 + t) * 16, 0, 0x10);
-        }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    __shared__ int last;
-    if (t == 0) last = atomicAdd(sk.counters + sk.tile, 1) == sk.splits - 1;
-    __syncthreads();
-    if (!last) return;
-    switch (sk.splits) {
-      case 2: sum_splits<2>(acc, rp, sk.split, t); break;
-      case 3: sum_splits<3>(acc, rp, sk.split, t); break;
-      case 4: sum_splits<4>(acc, rp, sk.split, t); break;
-      case 5: sum_splits<5>(acc, rp, sk.split, t); break;
-      case 6: sum_splits<6>(acc, rp, sk.split, t); break;
-      case 7: sum_splits<7>(acc, rp, sk.split, t); break;
-      default: sum_splits<kMaxSplits>(acc, rp, sk.split, t); break;
-    }
-    if (t == 0) __hip_atomic_store(sk.counters + sk.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // 16 float4s per part with 224 accumulator registers, 8 with 256
+    constexpr int budget = Cfg::FM * Cfg::FN * (MMA::NACC / 4) > 56 ? 8 : 16;
+    if (!combine_splits<256, budget>(acc, sk, (int)threadIdx.x)) return;
   }
 
   static_assert(!(SPLIT && QUANT), "the quantising epilogue takes whole-K tiles");

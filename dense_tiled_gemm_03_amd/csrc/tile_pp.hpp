@@ -62,15 +62,21 @@ struct PPTile {
 // BKN = false: B stored N x K (sbk = 1); true: B stored K x N (sbn = 1),
 // staged as [k][n] rows and read with the gfx950 transpose read, as in
 // tile_body (256 x 256 tiles only).
-template <typename T, typename Cfg, bool QUANT = false, bool BKN = false>
+// SPLITS > 1: this workgroup runs split sk.split of SPLITS (== sk.splits)
+// equal ranges of the K slices and the tile's partials are combined as in
+// the four-wave kernel (combine_splits); N x K tiles only.
+template <typename T, typename Cfg, bool QUANT = false, bool BKN = false, int SPLITS = 1>
 __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
-                                        const QuantOut& qo = QuantOut{}) {
+                                        const QuantOut& qo = QuantOut{},
+                                        const SplitK& sk = SplitK{1, 0, 0, nullptr, nullptr}) {
   typedef typename Elem<T>::x8 T8;
   typedef f32x4 Acc;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, SUBS = Cfg::SUBS;
   constexpr int A_ST = Cfg::A_ST, B_ST = Cfg::B_ST;
-  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  constexpr bool SPLIT = SPLITS > 1;
+  static_assert(!(SPLIT && (QUANT || BKN)), "split K runs N x K tiles with the plain epilogue");
+  char* const lds = tile_lds<Cfg::LDS_BYTES>();
   auto a_off = [](int s) { return s * Cfg::A_BYTES; };
   auto b_off = [](int s) { return A_ST * Cfg::A_BYTES + s * Cfg::B_BYTES; };
   const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
@@ -81,7 +87,12 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = w >> 2, q = w & 3;  // group, wave within the group (its SIMD)
   const int K = (int)a.K;
-  const int nk = (K + BK - 1) / BK;
+  // this workgroup's K slices [s_begin, s_end) and the end of its K range
+  const int nk_all = (K + BK - 1) / BK;
+  const int s_begin = SPLIT ? (int)((int64_t)sk.split * nk_all / SPLITS) : 0;
+  const int s_end = SPLIT ? (int)((int64_t)(sk.split + 1) * nk_all / SPLITS) : nk_all;
+  const int nk = s_end - s_begin;
+  const int k_lo = s_begin * BK, k_end = min(K, s_end * BK);
   static_assert(!BKN || BN == 256, "K x N tiles are 256 columns wide");
   const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)(BKN ? a.sbk : a.sbn);
 
@@ -104,7 +115,7 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   const uint32_t l_lane = (uint32_t)lrow * ld * 2 + 16 * lchunk;
   const uint32_t l_step = 32 * ld * 2;
   auto load_a = [&](int slot, int k0) {
-    const bool kin = k0 + 8 * lchunk < K;
+    const bool kin = k0 + 8 * lchunk < k_end;
     const uint32_t base = lds32 + a_off(slot) + q * 1024;
 #pragma unroll
     for (int i = 0; i < Cfg::A_LOADS; ++i)
@@ -130,13 +141,13 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
     }
   }
   auto load_b = [&](int slot, int k0) {
-    const bool kin = k0 + 8 * lchunk < K;
+    const bool kin = k0 + 8 * lchunk < k_end;
     const uint32_t base = lds32 + b_off(slot) + q * 1024;
 #pragma unroll
     for (int i = 0; i < Cfg::B_LOADS; ++i) {
       if constexpr (BKN) {
         const int hi = i >> 2, quarter = i & 3;
-        const bool rin = k0 + 16 * q + 8 * hi + (lane >> 3) < K;
+        const bool rin = k0 + 16 * q + 8 * hi + (lane >> 3) < k_end;
         load_lds16(rb, lds32 + b_off(slot) + quarter * 8192 + (2 * q + hi) * 1024,
                    rin ? nb_lane[hi] + (uint32_t)k0 * ldb * 2 + quarter * 128 : kOutOfRange);
       } else {
@@ -237,13 +248,13 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   };
 
   if (g == 0) {
-    load_a(0, 0);
+    load_a(0, k_lo);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     barrier();                                   // 0
     int sa = 0, sb = 0;
     for (int j = 0; j < nk; ++j) {
       const int na = sa + 1 == A_ST ? 0 : sa + 1;
-      load_a(na, (j + 1) * BK);                  // slice j + 1 into slice j - 1's stage
+      load_a(na, k_lo + (j + 1) * BK);           // slice j + 1 into slice j - 1's stage
       read_slice(sa, sb);
       wait_lds();
       barrier();                                 // 2j + 1
@@ -255,15 +266,15 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
       sb = sb + 1 == B_ST ? 0 : sb + 1;
     }
   } else {
-    load_b(0, 0);
-    load_b(1, BK);
+    load_b(0, k_lo);
+    load_b(1, k_lo + BK);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Cfg::B_LOADS) : "memory");
     barrier();                                   // 0
     barrier();                                   // 1
     int sa = 0, sb = 0;
     for (int j = 0; j < nk; ++j) {
       const int nb2 = sb == 0 ? 2 : sb - 1;      // (j + 2) mod 3: slice j - 1's stage
-      load_b(nb2, (j + 2) * BK);
+      load_b(nb2, k_lo + (j + 2) * BK);
       read_slice(sa, sb);
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(Cfg::B_LOADS) : "memory");
@@ -273,9 +284,14 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
       sa = sa + 1 == A_ST ? 0 : sa + 1;
       sb = sb + 1 == B_ST ? 0 : sb + 1;
     }
-    // the last B loads (slices past K, zeros) land before the LDS is released
+    // the last B loads (slices past the range, zeros) land before the LDS is released
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  if constexpr (SPLIT) {
+    // 12 float4s per part beside the 112 accumulator registers
+    if (!combine_splits<512, 12, SPLITS>(acc, sk, (int)threadIdx.x)) return;
   }
 
   if constexpr (QUANT) {
@@ -317,6 +333,37 @@ __global__ __launch_bounds__(512) void gemm16_pp(GemmArgs a, int tiles_m, int ti
   int tm, tn;
   tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
   pp_body<T, Cfg, false, BKN>(a, tm, tn);
+}
+
+// Split K: `splits` consecutive workgroups per tile, each over its share of
+// the K slices, combined through scratch (SplitK): for products with too few
+// tiles to fill the CUs.
+template <typename T, typename Cfg, int S>
+__global__ __launch_bounds__(512) void gemm16_pp_splitk(GemmArgs a, int tiles_m, int tiles_n,
+                                                        float* part, int* counters) {
+  const int id = xcd_id();
+  const int tile = id / S;
+  int tm, tn;
+  tile_of(tile, tiles_m, tiles_n, Cfg::GM, tm, tn);
+  pp_body<T, Cfg, false, false, S>(a, tm, tn, QuantOut{}, SplitK{S, id % S, tile, part, counters});
+}
+
+// Grids of one whole wave and a partial one: `full` whole tiles, then the
+// remaining tiles split `splits` ways over K (workgroup order as in
+// tail_unit); the partials and counters are indexed by the tile's place
+// among the split ones.  Both bodies share one LDS array (tile_lds).
+template <typename T, typename Cfg, int S>
+__global__ __launch_bounds__(512) void gemm16_pp_tail(GemmArgs a, int tiles_m, int tiles_n,
+                                                      int full, float* part, int* counters) {
+  int id;
+  const bool whole = tail_unit(blockIdx.x, gridDim.x, full, id);
+  int tm, tn;
+  tile_of(whole ? id : full + id / S, tiles_m, tiles_n, Cfg::GM, tm, tn);
+  if (whole)
+    pp_body<T, Cfg>(a, tm, tn);
+  else
+    pp_body<T, Cfg, false, false, S>(a, tm, tn, QuantOut{},
+                                     SplitK{S, id % S, id / S, part, counters});
 }
 
 // fp8 output (256 x 256 tiles): the product quantised per 1 x 128 row slice

@@ -301,7 +301,7 @@ SWEEP_PLANS = [
     (8192, 8192, 8192, "tile_nt_256x256", "tile_nt_256x256"),
     (2048, 7168, 16384, "tile_nt_256x224", "tile_nt_256x224"),
     (1024, 1024, 8192, "tile_nt_128x128", "tile_nt_128x128_splitk4"),
-    (1024, 1024, 8200, "tile_nt_128x128", "tile_nt_256x224_splitk8"),
+    (1024, 1024, 8200, "tile_nt_128x128", "tile_nt_256x224_splitk7"),
     (2048, 2048, 8192, "tile_nt_128x128", "tile_nt_128x128"),
     (4096, 4096, 1024, "tile_nt_256x256", "tile_nt_256x256"),
     (4096, 1792, 4096, "tile_nt_128x128_2stage", "tile_nt_128x128_2stage"),

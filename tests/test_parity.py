@@ -333,7 +333,7 @@ SPLITK_CASES = [
     (1000, 2600, 8200, "tile_nt_256x224_splitk5"),
     (700, 3000, 8200, "tile_nt_256x224_splitk6"),
     (700, 2600, 8456, "tile_nt_256x224_splitk7"),
-    (200, 300, 8200, "tile_nt_256x224_splitk8"),
+    (200, 300, 8200, "tile_nt_256x224_splitk7"),
 ]
 
 
