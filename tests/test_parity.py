@@ -651,6 +651,16 @@ def test_split_k_graph_capture():
     _graph_case(1024, 1024, 4096, 78, "tile_nt_128x128_splitk4", "tile_nt_128x128")
 
 
+def test_pp_split_k_graph_capture():
+    H.log("eight-wave split-K graph capture")
+    _graph_case(1000, 2600, 8200, 80, "tile_nt_256x224_splitk5", "tile_nt_128x128")
+
+
+def test_pp_tail_graph_capture():
+    H.log("eight-wave partial-wave graph capture")
+    _graph_case(4352, 4096, 1024, 81, "tile_nt_256x224_tail2", "tile_nt_256x224")
+
+
 def test_workspace_short_runs_allocation_free_plan():
     """A workspace one byte short of the split plan's need: the call runs the
     allocation-free plan and leaves the workspace untouched."""
