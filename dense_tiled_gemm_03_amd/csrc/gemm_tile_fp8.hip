@@ -451,6 +451,12 @@ __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
   const int g = w >> 2, q = w & 3;  // group, wave within the group (its SIMD)
   const int K = (int)a.K;
   const int nkb = (K + Q_BK - 1) / Q_BK;
+  // Slice order as in the bf16 eight-wave kernel: workgroups of odd dispatch
+  // rounds take the K blocks from the top down, starting with the rows the
+  // round before read last (still in the last-level cache).  slice_kb(j) is
+  // the K block of the j-th slice taken; past the end it is -1 (zeros).
+  const bool down = (blockIdx.x / tile::kRoundWgs) & 1;
+  auto slice_kb = [&](int j) { return j >= nkb ? -1 : (down ? nkb - 1 - j : j); };
   const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
   // this group's B ring
   const int b_ring = g == 0 ? L::B0 : L::B1;
@@ -480,7 +486,7 @@ __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
   const uint32_t lchunk = (lane & 7) ^ (4 * (q & 1) + (lane >> 4));
   auto load_rows = [&](const i32x4& desc, uint32_t ld, uint32_t base, int kb, auto n_loads) {
     const int k0 = kb * Q_BK;
-    const bool kin = k0 + 16 * (int)lchunk < K;
+    const bool kin = kb >= 0 && k0 + 16 * (int)lchunk < K;
     const uint32_t lane_off = lrow * ld + 16 * lchunk + (uint32_t)k0;
 #pragma unroll
     for (int i = 0; i < decltype(n_loads)::value; ++i)
@@ -497,7 +503,7 @@ __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
   const uint32_t sa_lane = (uint32_t)sa_row * (uint32_t)a.ssam * 4;
   const uint32_t sb_lane = (uint32_t)lane * (uint32_t)a.ssbn * 4;
   auto load_scales = [&](int st, int kb) {
-    const bool kin = kb < nkb;
+    const bool kin = kb >= 0 && kb < nkb;
     load_lds4(rsa, lds32 + a_off(st) + Q_SA + 256 * q,
               kin && sa_in ? sa_lane + (uint32_t)(kb * a.ssak) * 4 : kOutOfRange);
     if (q == 0)
@@ -590,18 +596,18 @@ __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
     // Before barrier 2j + 2, A(j + 1) and B0(j + 1) must have landed: B0(j +
     // 1) was issued B0_ST - 2 iterations back, so the B0 loads of the last
     // B0_ST - 2 iterations may stay in flight (scale loads precede them).
-    load_a(0, 0);
-    load_scales(0, 0);
+    load_a(0, slice_kb(0));
+    load_scales(0, slice_kb(0));
 #pragma unroll
-    for (int x = 0; x < B0_ST - 1; ++x) load_b(x, x);
+    for (int x = 0; x < B0_ST - 1; ++x) load_b(x, slice_kb(x));
     wait_loads(std::integral_constant<int, (B0_ST - 2) * Q_B_LOADS>());
     barrier();                                   // 0
     int sta = 0, stb = 0;
     for (int j = 0; j < nkb; ++j) {
       const int nsta = sta ^ 1, lstb = stb == 0 ? B0_ST - 1 : stb - 1;
-      load_a(nsta, j + 1);                       // into slice j - 1's stage
-      load_scales(nsta, j + 1);
-      load_b(lstb, j + B0_ST - 1);               // into slice j - 1's stage
+      load_a(nsta, slice_kb(j + 1));             // into slice j - 1's stage
+      load_scales(nsta, slice_kb(j + 1));
+      load_b(lstb, slice_kb(j + B0_ST - 1));     // into slice j - 1's stage
       read_slice(sta, stb);
       wait_lds();
       barrier();                                 // 2j + 1
@@ -616,14 +622,14 @@ __device__ __forceinline__ void fp8_pp_body(const GemmArgs& a, int tm, int tn) {
     // Per iteration j: B1(j + B1_ST - 1).  Before barrier 2j + 3, B1(j + 1)
     // must have landed: issued B1_ST - 2 iterations back.
 #pragma unroll
-    for (int x = 0; x < B1_ST - 1; ++x) load_b(x, x);
+    for (int x = 0; x < B1_ST - 1; ++x) load_b(x, slice_kb(x));
     wait_loads(std::integral_constant<int, (B1_ST - 2) * Q_B_LOADS>());
     barrier();                                   // 0
     barrier();                                   // 1
     int sta = 0, stb = 0;
     for (int j = 0; j < nkb; ++j) {
       const int lstb = stb == 0 ? B1_ST - 1 : stb - 1;
-      load_b(lstb, j + B1_ST - 1);               // into slice j - 1's stage
+      load_b(lstb, slice_kb(j + B1_ST - 1));     // into slice j - 1's stage
       read_slice(sta, stb);
       wait_lds();
       barrier();                                 // 2j + 2

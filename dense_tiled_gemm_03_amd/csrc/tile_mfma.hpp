@@ -53,6 +53,9 @@ template <int V> using Int = std::integral_constant<int, V>;
 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // past every descriptor's range
 constexpr int kXcds = 8;
+// Workgroups of the eight-wave kernels that run at once: one per CU (their
+// LDS rings take most of a CU's 160 KiB), 256 CUs.
+constexpr int kRoundWgs = 256;
 
 // MFMA shapes.  A fragment is DIM rows x KSTEP k of one operand; lane l
 // supplies row (l % DIM) and the 16-byte chunk (l / DIM) of the sub-step's

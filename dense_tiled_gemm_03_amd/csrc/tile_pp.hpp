@@ -93,6 +93,14 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   const int s_end = SPLIT ? (int)((int64_t)(sk.split + 1) * nk_all / SPLITS) : nk_all;
   const int nk = s_end - s_begin;
   const int k_lo = s_begin * BK, k_end = min(K, s_end * BK);
+  // Slice order: workgroups of odd dispatch rounds (kRoundWgs run at once)
+  // take their slices from the top of the range down.  A round re-reads the
+  // operand rows the round before streamed, and so starts with the ones that
+  // round read last, which are still in the last-level cache.  slice_k(j) is
+  // the first k of the j-th slice taken; past the range it is negative (the
+  // loads read zeros).
+  const bool down = (blockIdx.x / kRoundWgs) & 1;
+  auto slice_k = [&](int j) { return j >= nk ? -BK : k_lo + (down ? nk - 1 - j : j) * BK; };
   static_assert(!BKN || BN == 256, "K x N tiles are 256 columns wide");
   const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)(BKN ? a.sbk : a.sbn);
 
@@ -115,7 +123,7 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   const uint32_t l_lane = (uint32_t)lrow * ld * 2 + 16 * lchunk;
   const uint32_t l_step = 32 * ld * 2;
   auto load_a = [&](int slot, int k0) {
-    const bool kin = k0 + 8 * lchunk < k_end;
+    const bool kin = k0 >= 0 && k0 + 8 * lchunk < k_end;
     const uint32_t base = lds32 + a_off(slot) + q * 1024;
 #pragma unroll
     for (int i = 0; i < Cfg::A_LOADS; ++i)
@@ -141,13 +149,13 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
     }
   }
   auto load_b = [&](int slot, int k0) {
-    const bool kin = k0 + 8 * lchunk < k_end;
+    const bool kin = k0 >= 0 && k0 + 8 * lchunk < k_end;
     const uint32_t base = lds32 + b_off(slot) + q * 1024;
 #pragma unroll
     for (int i = 0; i < Cfg::B_LOADS; ++i) {
       if constexpr (BKN) {
         const int hi = i >> 2, quarter = i & 3;
-        const bool rin = k0 + 16 * q + 8 * hi + (lane >> 3) < k_end;
+        const bool rin = k0 >= 0 && k0 + 16 * q + 8 * hi + (lane >> 3) < k_end;
         load_lds16(rb, lds32 + b_off(slot) + quarter * 8192 + (2 * q + hi) * 1024,
                    rin ? nb_lane[hi] + (uint32_t)k0 * ldb * 2 + quarter * 128 : kOutOfRange);
       } else {
@@ -248,13 +256,13 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   };
 
   if (g == 0) {
-    load_a(0, k_lo);
+    load_a(0, slice_k(0));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     barrier();                                   // 0
     int sa = 0, sb = 0;
     for (int j = 0; j < nk; ++j) {
       const int na = sa + 1 == A_ST ? 0 : sa + 1;
-      load_a(na, k_lo + (j + 1) * BK);           // slice j + 1 into slice j - 1's stage
+      load_a(na, slice_k(j + 1));                // slice j + 1 into slice j - 1's stage
       read_slice(sa, sb);
       wait_lds();
       barrier();                                 // 2j + 1
@@ -266,15 +274,15 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
       sb = sb + 1 == B_ST ? 0 : sb + 1;
     }
   } else {
-    load_b(0, k_lo);
-    load_b(1, k_lo + BK);
+    load_b(0, slice_k(0));
+    load_b(1, slice_k(1));
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Cfg::B_LOADS) : "memory");
     barrier();                                   // 0
     barrier();                                   // 1
     int sa = 0, sb = 0;
     for (int j = 0; j < nk; ++j) {
       const int nb2 = sb == 0 ? 2 : sb - 1;      // (j + 2) mod 3: slice j - 1's stage
-      load_b(nb2, k_lo + (j + 2) * BK);
+      load_b(nb2, slice_k(j + 2));
       read_slice(sa, sb);
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(Cfg::B_LOADS) : "memory");
