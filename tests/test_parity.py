@@ -313,6 +313,27 @@ def test_tile_nt_ragged(fmt, case):
     assert plan == want
 
 
+# Grids of more than one round of eight-wave tiles (256 run at once): the
+# workgroups of the second round take their K slices from the top down, the
+# first of them a partial slice here (K not a multiple of 64).
+ROUND_CASES = [
+    (4000, 4600, 1000, "nk", "tile_nt_256x224"),
+    (4100, 4400, 520, "nk", "tile_nt_256x224"),
+    (4400, 4200, 1000, "kn", "tile_nn_256x256"),
+]
+
+
+@pytest.mark.parametrize("case", ROUND_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}{c[3]}" for c in ROUND_CASES])
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_two_round_grids(fmt, case):
+    M, N, K, layout, want = case
+    plan = _check16(fmt, M, N, K, layout, seed=800 + M + N + K)
+    assert plan == want
+    r = max(1, min(64 if fmt == "bf16" else 16, int(math.sqrt(2 ** 24 / K))))
+    plan = _check16(fmt, M, N, K, layout, seed=900 + M + N + K, int_r=r)
+    assert plan == want
+
+
 def test_tile_nt_padded_leading_dims():
     """Leading dimensions padded to multiples of 8 (not of the tile)."""
     M, N, K = 520, 460, 200
