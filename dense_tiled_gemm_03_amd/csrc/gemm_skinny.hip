@@ -268,21 +268,31 @@ __global__ __launch_bounds__(256) void gemm16_skinny(GemmArgs a, int splits, flo
 // workgroups; its 4 waves split each 64-wide K slice instead, wave w taking
 // the slice's k16 step w, and their four fp32 partial tiles are added in
 // wave order through LDS at the end.  Same loads, swizzle, descriptors and
-// edges as gemm16_skinny, with a 12-stage ring of 12 KiB slices (8 KiB of
-// A, 4 KiB of B): each workgroup reads all of A (from L2, shared by every
-// strip) and its 32 rows of B.
-constexpr int WN = 32;                     // columns of C per workgroup
-constexpr int WSTAGES = 12;                // LDS ring depth
-constexpr int WSTAGE = (SM + WN) * ROWB;   // 12 KiB
-constexpr int WLD = (SM + WN) / 8 / 4;     // 1 KiB loads per wave per slice: 3
-constexpr int WRED_PITCH = WN + 4;         // fp32 row pitch of the partial tiles in LDS
-static_assert((WSTAGES - 1) * WLD <= 63, "loads in flight must fit the vmcnt counter");
-static_assert(4 * SM * WRED_PITCH * 4 <= WSTAGES * WSTAGE, "partial tiles must fit the ring");
+// edges as gemm16_skinny.  Every workgroup reads all of A (from L2, shared
+// by every strip) and its 32 rows of B (from HBM), so the two streams have
+// different latencies: A and B have LDS rings of their own (WA_ST stages of
+// 8 KiB, WB_ST of 4 KiB), waves 0-1 load only A and waves 2-3 only B, so
+// that each wave's wait counts one stream.  Slices go in groups of WP per
+// barrier (a slice is only 2 MFMAs per wave; the barrier, the fragment reads
+// and their LDS latency are paid once per group).
+constexpr int WN = 32;                          // columns of C per workgroup
+constexpr int WA_ST = 12, WB_ST = 16;           // stages of the A and B rings
+constexpr int WP = 4;                           // slices per barrier
+constexpr int WA_BYTES = SM * ROWB;             // 8 KiB: one A slice
+constexpr int WB_BYTES = WN * ROWB;             // 4 KiB: one B slice
+constexpr int W_LDS = WA_ST * WA_BYTES + WB_ST * WB_BYTES;  // 160 KiB
+constexpr int WRED_PITCH = WN + 4;              // fp32 row pitch of the partial tiles in LDS
+static_assert(W_LDS <= 160 * 1024, "rings must fit the LDS");
+static_assert(WA_ST % WP == 0 && WB_ST % WP == 0 && WA_ST >= 2 * WP && WB_ST >= 2 * WP,
+              "rings hold whole groups, two groups at least");
+static_assert((WA_ST - WP) * 4 <= 63 && (WB_ST - WP) * 2 <= 63,
+              "loads in flight must fit the vmcnt counter");
+static_assert(4 * SM * WRED_PITCH * 4 <= W_LDS, "partial tiles must fit the rings");
 
 template <typename T>
 __global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
   typedef typename Elem<T>::x8 T8;
-  __shared__ __attribute__((aligned(1024))) char lds[WSTAGES * WSTAGE];  // 144 KiB
+  __shared__ __attribute__((aligned(1024))) char lds[W_LDS];
   const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
 
@@ -296,29 +306,65 @@ __global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
   const i32x4 ra = make_desc(a.A, (uint32_t)((((int)a.M - 1) * lda + K) * 2));
   const i32x4 rb = make_desc(Bb, (uint32_t)(((rows_b - 1) * ldb + K) * 2));
   const int count = (K + SK - 1) / SK;
+  const bool loads_a = w < 2;  // wave-uniform
 
-  // The stage's 8-row groups 0 .. 7 hold A's rows, 8 .. 11 the strip's B
-  // rows; wave w loads groups 3w .. 3w + 2.  Lane l writes stage row
-  // 8g + (l >> 3) at chunk position l & 7, i.e. logical chunk
-  // (l & 7) ^ (4 (g & 1) + (l >> 4)).
+  // Slot s of the A ring at s * WA_BYTES, of the B ring after the A ring.
+  // A slice's 8-row groups: wave w (0, 1) loads A groups 4w .. 4w + 3, wave
+  // w (2, 3) B groups 2(w - 2) .. + 1.  Lane l writes group row l >> 3 at
+  // chunk position l & 7, i.e. logical chunk (l & 7) ^ (4 (g & 1) + (l >> 4)).
   const uint32_t lrow = lane >> 3;
   const uint32_t lc0 = (lane & 7) ^ (lane >> 4), lc1 = (lane & 7) ^ (4 + (lane >> 4));
-  auto load_slice = [&](int slot, int slice) {
+  auto load_a = [&](int slice) {
     if (slice >= count) return;  // nothing past K
     const int k0 = slice * SK;
-    const uint32_t stage = lds32 + slot * WSTAGE;
+    const uint32_t stage = lds32 + (slice % WA_ST) * WA_BYTES;
 #pragma unroll
-    for (int j = 0; j < WLD; ++j) {
-      const int g = WLD * w + j;  // wave-uniform
+    for (int j = 0; j < 4; ++j) {
+      const int g = 4 * w + j;
       const uint32_t c = (g & 1) ? lc1 : lc0;
       const bool kin = k0 + 8 * (int)c < K;
-      if (g < SM / 8) {
-        const uint32_t off = (8 * g + lrow) * lda * 2 + 2 * k0 + 16 * c;
-        load_lds16(ra, stage + g * 1024, kin ? off : kOutOfRange);
-      } else {
-        const uint32_t off = (8 * (g - SM / 8) + lrow) * ldb * 2 + 2 * k0 + 16 * c;
-        load_lds16_nt(rb, stage + g * 1024, kin ? off : kOutOfRange);
-      }
+      const uint32_t off = (8 * g + lrow) * lda * 2 + 2 * k0 + 16 * c;
+      load_lds16(ra, stage + g * 1024, kin ? off : kOutOfRange);
+    }
+  };
+  auto load_b = [&](int slice) {
+    if (slice >= count) return;
+    const int k0 = slice * SK;
+    const uint32_t stage = lds32 + WA_ST * WA_BYTES + (slice % WB_ST) * WB_BYTES;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int g = 2 * (w - 2) + j;
+      const uint32_t c = (g & 1) ? lc1 : lc0;
+      const bool kin = k0 + 8 * (int)c < K;
+      const uint32_t off = (8 * g + lrow) * ldb * 2 + 2 * k0 + 16 * c;
+      load_lds16_nt(rb, stage + g * 1024, kin ? off : kOutOfRange);
+    }
+  };
+  // Waits for this wave's stream.  Before the first group: slices 0 .. WP - 1
+  // landed, the ring's other ST - WP slices may be in flight.  Before the
+  // group after slices i .. i + WP - 1 is read: slices .. i + 2 WP - 1 landed,
+  // the ST - 2 WP issued after them may be in flight (all of them near the
+  // end of K, where fewer were issued).
+  auto wait_first = [&]() {
+    if (loads_a) {
+      if (WA_ST <= count) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((WA_ST - WP) * 4) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      if (WB_ST <= count) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((WB_ST - WP) * 2) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
+  auto wait_next = [&](int i) {
+    if (loads_a) {
+      if (i + WA_ST <= count)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((WA_ST - 2 * WP) * 4) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    } else {
+      if (i + WB_ST <= count)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((WB_ST - 2 * WP) * 2) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     }
   };
 
@@ -331,41 +377,53 @@ __global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
-  T8 fa0[2], fa1[2], fb[2];
-  auto read_slice = [&](int buf, int slot) {
-    const char* base = lds + slot * WSTAGE;
-    fa0[buf] = *reinterpret_cast<const T8*>(base + rd);
-    fa1[buf] = *reinterpret_cast<const T8*>(base + 32 * ROWB + rd);
-    fb[buf] = *reinterpret_cast<const T8*>(base + SM * ROWB + rd);
-  };
-  // As in gemm16_skinny: wait for slice i + 1 and for every wave's reads of
-  // slice i, refill slice i's slot with slice i + WSTAGES, read slice i + 1,
-  // multiply slice i.
-  auto step = [&](int i, int cur) {
-    if (i + WSTAGES - 1 < count)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((WSTAGES - 2) * WLD) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    asm volatile("s_barrier" ::: "memory");
-    load_slice(i % WSTAGES, i + WSTAGES);
-    if (i + 1 < count) read_slice(cur ^ 1, (i + 1) % WSTAGES);
-    __builtin_amdgcn_sched_barrier(0);
-    acc[0] = mfma32x32x16(fa0[cur], fb[cur], acc[0]);
-    acc[1] = mfma32x32x16(fa1[cur], fb[cur], acc[1]);
-    __builtin_amdgcn_sched_barrier(0);
-  };
+  T8 fa0[2][WP], fa1[2][WP], fb[2][WP];  // [buffer][slice of the group]
+  auto read_group = [&](int buf, int first) {
 #pragma unroll
-  for (int p = 0; p < WSTAGES; ++p) load_slice(p, p);
-  if (WSTAGES <= count)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((WSTAGES - 1) * WLD) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int h = 0; h < WP; ++h) {
+      const char* ab = lds + ((first + h) % WA_ST) * WA_BYTES;
+      const char* bb = lds + WA_ST * WA_BYTES + ((first + h) % WB_ST) * WB_BYTES;
+      fa0[buf][h] = *reinterpret_cast<const T8*>(ab + rd);
+      fa1[buf][h] = *reinterpret_cast<const T8*>(ab + 32 * ROWB + rd);
+      fb[buf][h] = *reinterpret_cast<const T8*>(bb + rd);
+    }
+  };
+  // The group of slices i .. i + WP - 1 (read into buffer cur): wait for the
+  // next group and for every wave's reads of this one, refill this group's
+  // slots with the slices a ring's depth later, read the next group,
+  // multiply this one (slices past K are skipped; their fragments are stale).
+  auto step = [&](int i, int cur) {
+    wait_next(i);
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < WP; ++h) {
+      if (loads_a) load_a(i + h + WA_ST);
+      else load_b(i + h + WB_ST);
+    }
+    if (i + WP < count) read_group(cur ^ 1, i + WP);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < WP; ++h)
+      if (i + h < count) {
+        acc[0] = mfma32x32x16(fa0[cur][h], fb[cur][h], acc[0]);
+        acc[1] = mfma32x32x16(fa1[cur][h], fb[cur][h], acc[1]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (loads_a) {
+#pragma unroll
+    for (int p = 0; p < WA_ST; ++p) load_a(p);
+  } else {
+#pragma unroll
+    for (int p = 0; p < WB_ST; ++p) load_b(p);
+  }
+  wait_first();
   asm volatile("s_barrier" ::: "memory");
-  read_slice(0, 0);
+  read_group(0, 0);
   int i = 0;
-  for (; i + 1 < count; i += 2) {
+  for (; i + WP < count; i += 2 * WP) {
     step(i, 0);
-    step(i + 1, 1);
+    step(i + WP, 1);
   }
   if (i < count) step(i, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
