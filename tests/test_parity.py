@@ -554,9 +554,12 @@ def test_split_k_scratch_reused_by_more_tiles():
 
 # (M, N, K): no split wanted (short K), and K split across workgroups with a
 # workspace / across the waves of 32-column strips without one (K of 16 or
-# more 64-wide slices), ragged N strips, K not a multiple of the slice.
+# more 64-wide slices), ragged N strips, K not a multiple of the slice.  The
+# 32-column strips take their slices four to a barrier: 16, 18, 19, 33, 65
+# and 112 slices leave 0, 2, 3, 1, 1 and 0 over.
 SKINNY_CASES = [(1, 100, 64), (17, 300, 200), (64, 64, 8), (64, 33, 1000), (40, 7168, 1024),
-                (63, 95, 4104), (64, 1000, 2056), (64, 7168, 520), (64, 7168, 7168)]
+                (63, 95, 4104), (64, 1000, 2056), (64, 7168, 520), (64, 7168, 7168),
+                (64, 512, 1152), (48, 600, 1192)]
 
 
 @pytest.mark.parametrize("case", SKINNY_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SKINNY_CASES])
