@@ -12,7 +12,8 @@ torch / numpy dtype conversions (tests/test_codecs.py); the fp8 block
 quantiser against torch's e4m3fn cast, numpy's fp32 division, the block
 invariants of its definition and the input generator's own quantiser; the
 product with fp8 output against an identity product and numpy's integer
-matmul; the acceptance bound against its stated constants, the unit
+matmul; the SwiGLU combination against closed forms of silu, a selection
+product and exact integer products; the acceptance bound against its stated constants, the unit
 roundoffs of torch's format descriptions and an fp32-accumulating model of
 the GPU arithmetic.
 """
@@ -58,6 +59,8 @@ class Oracle:
         lib.tg_oracle_decode.restype = None
         lib.tg_oracle_quant_fp8.argtypes = [i64, i64, vp, i64, i64, vp, i64, vp, i64, i64]
         lib.tg_oracle_quant_fp8.restype = c_int
+        lib.tg_oracle_swiglu.argtypes = [i64, vp, vp, vp]
+        lib.tg_oracle_swiglu.restype = c_int
         lib.tg_oracle_bound.argtypes = [c_int, vp, i64, vp]
         lib.tg_oracle_bound.restype = None
         lib.tg_oracle_threads.argtypes = [c_int]
@@ -126,6 +129,33 @@ class Oracle:
         Q, SC = self.quant_fp8(C.astype(np.float32), 1)
         return Q, SC, C, S
 
+    def swiglu(self, G: np.ndarray, U: np.ndarray) -> np.ndarray:
+        """h = silu(g) * u element by element, silu(g) = g / (1 + e^-g), in
+        fp64 (see oracle.c)."""
+        G = np.ascontiguousarray(G, dtype=np.float64)
+        U = np.ascontiguousarray(U, dtype=np.float64)
+        if G.shape != U.shape:
+            raise ValueError("oracle: gate and up shapes differ")
+        H = np.empty(G.shape, np.float64)
+        if self.lib.tg_oracle_swiglu(G.size, _p(G), _p(U), _p(H)) != 0:
+            raise ValueError("oracle: bad arguments")
+        return H
+
+    def swiglu_quant_fp8(self, fmt: str, M: int, N: int, K: int, A: np.ndarray, sam: int,
+                         sak: int, Bg: np.ndarray, Bu: np.ndarray, sbk: int, sbn: int, rows=None):
+        """The fused SwiGLU with an fp8 output ("TileKernels deep dive" section
+        4.3): the gate product G = A Bg and the up product U = A Bu in fp64,
+        h = silu(g) * u in fp64, rounded once to fp32, then quantised with one
+        scale per 1 x 128 row slice as in gemm_quant_fp8.  Bg and Bu share the
+        strides (B[k,j] at k*sbk + j*sbn).  Returns (codes nrows x N, scales
+        nrows x ceil(N / 128), fp64 H, fp64 G, fp64 U, S_g, S_u) for the
+        requested rows (all if None); S = sum |a||b| of each product."""
+        G, Sg = self.gemm(fmt, M, N, K, A, sam, sak, Bg, sbk, sbn, rows=rows)
+        U, Su = self.gemm(fmt, M, N, K, A, sam, sak, Bu, sbk, sbn, rows=rows)
+        H = self.swiglu(G, U)
+        Q, SC = self.quant_fp8(H.astype(np.float32), 1)
+        return Q, SC, H, G, U, Sg, Su
+
     def round_to(self, fmt: str, x: np.ndarray) -> np.ndarray:
         """Round fp64 values to fp16 / bf16 codes, nearest-even (overflow -> inf)."""
         x = np.ascontiguousarray(x, dtype=np.float64)
@@ -187,6 +217,14 @@ def gemm_fp8_blockscaled(*args, **kw):
 
 def gemm_quant_fp8(*args, **kw):
     return default().gemm_quant_fp8(*args, **kw)
+
+
+def swiglu(*args, **kw):
+    return default().swiglu(*args, **kw)
+
+
+def swiglu_quant_fp8(*args, **kw):
+    return default().swiglu_quant_fp8(*args, **kw)
 
 
 def threads(n):

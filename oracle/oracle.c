@@ -300,6 +300,19 @@ int tg_oracle_quant_fp8(int64_t R, int64_t K, const float* X, int64_t ldx, int64
 
 /* fmt 1: fp16 (p = 11, emin = -14, max 65504); fmt 2: bf16 (p = 8,
  * emin = -126, max (2 - 2^-7) * 2^127). */
+/* ---- SwiGLU of a gate and an up product ----------------------------------
+ * "TileKernels deep dive", section 4.3 (the fused SwiGLU + FP8 quantisation
+ * example): the gate and up projections of one input are combined by the
+ * SwiGLU activation, and the combination, not the two products, is what is
+ * quantised.  Read here as, element by element,
+ *   h = silu(g) * u,   silu(g) = g / (1 + e^(-g)),
+ * in fp64 from the fp64 products g (gate) and u (up); n values. */
+int tg_oracle_swiglu(int64_t n, const double* G, const double* U, double* H) {
+  if (n < 0) return -1;
+  for (int64_t t = 0; t < n; ++t) H[t] = G[t] / (1.0 + exp(-G[t])) * U[t];
+  return 0;
+}
+
 void tg_oracle_round(int fmt, const double* x, int64_t n, uint16_t* out) {
   for (int64_t t = 0; t < n; ++t) {
     if (fmt == FMT_F16)

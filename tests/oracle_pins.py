@@ -471,6 +471,71 @@ def pin_gemm_quant_integers(orc):
             assert np.array_equal(Q[i, j * 128:(j + 1) * 128], want), (i, j)
 
 
+# ---------------------------------------------------------- SwiGLU
+
+def pin_swiglu_closed_forms(orc):
+    """silu(g) = g / (1 + e^-g) at points with closed forms, with u = 1:
+    silu(0) = 0; silu(ln 3) = (3/4) ln 3 and silu(-ln 3) = -(1/4) ln 3 (e^-ln3
+    = 1/3); silu(t) - silu(-t) = t for every t; silu(50) = 50 in fp64.  And
+    h = silu(g) * u scales with u: u = -2.5 gives -2.5 silu(g).  (A sign slip
+    in the exponent, the gate and up roles swapped, a missing division or a
+    missing factor g each break one of these.)"""
+    ln3 = np.log(3.0)
+    G = np.array([0.0, ln3, -ln3, 50.0, 0.7, -0.7, 3.25, -3.25])
+    H = orc.swiglu(G, np.ones_like(G))
+    assert H[0] == 0.0
+    assert abs(H[1] - 0.75 * ln3) <= 1e-15 and abs(H[2] + 0.25 * ln3) <= 1e-15
+    assert H[3] == 50.0
+    for a, b in ((4, 5), (6, 7)):
+        assert abs((H[a] - H[b]) - G[a]) <= 1e-15, (H[a], H[b], G[a])
+    H2 = orc.swiglu(G, np.full_like(G, -2.5))
+    assert np.all(np.abs(H2 - (-2.5) * H) <= 1e-15 * np.abs(H) + 1e-300)
+
+
+def pin_swiglu_selection(orc):
+    """With A = I the gate and up products select the weights' rows, so h at
+    (i, n) is silu(Bg[n, i]) * Bu[n, i] (weights stored N x K): element by
+    element on exactly representable values, in both formats (a transposed
+    weight, a swapped gate and up, or a row offset would all differ)."""
+    rng = np.random.default_rng(31)
+    for fmt in ("bf16", "f16"):
+        M = K = 24
+        N = 150
+        gv = lib_decode(fmt, lib_encode(fmt, rng.uniform(-6, 6, (N, K))))
+        uv = lib_decode(fmt, lib_encode(fmt, rng.uniform(-3, 3, (N, K))))
+        Bg, Bu = lib_encode(fmt, gv), lib_encode(fmt, uv)   # N x K, K-contiguous
+        A = lib_encode(fmt, np.eye(M, K))
+        Q, SC, H, G, U, _, _ = orc.swiglu_quant_fp8(fmt, M, N, K, A, K, 1, Bg, Bu, 1, K)
+        assert np.array_equal(G, gv.T) and np.array_equal(U, uv.T)
+        want = gv.T / (1.0 + np.exp(-gv.T)) * uv.T
+        assert np.all(np.abs(H - want) <= 1e-15 * np.abs(want))
+
+
+def pin_swiglu_quant_large_gate(orc):
+    """Positive integer inputs and gate weights make every gate value at least
+    K = 200, where 1 + e^-g rounds to 1 and silu(g) = g exactly: h is numpy's
+    exact integer product (A Bg) * (A Bu), and each 1 x 128 slice's scale and
+    codes are numpy's fp32 quotient of its maximum by 448 and torch's e4m3fn
+    cast of h / scale (ragged last slice, N = 300)."""
+    rng = np.random.default_rng(32)
+    M, N, K = 20, 300, 200
+    Ai = rng.integers(1, 4, (M, K))
+    Gw = rng.integers(1, 4, (N, K))
+    Uw = rng.integers(-3, 4, (N, K))
+    A, Bg, Bu = lib_encode("bf16", Ai), lib_encode("bf16", Gw), lib_encode("bf16", Uw)
+    Q, SC, H, G, U, _, _ = orc.swiglu_quant_fp8("bf16", M, N, K, A, K, 1, Bg, Bu, 1, K)
+    Hi = (Ai @ Gw.T) * (Ai @ Uw.T)
+    assert np.array_equal(H, Hi)
+    for i in range(M):
+        for j in range((N + 127) // 128):
+            blk = Hi[i, j * 128:(j + 1) * 128].astype(np.float32)
+            s = _fp32_div(np.abs(blk).max(), 448.0)
+            assert SC[i, j] == s, (i, j)
+            y = np.clip(blk / s, -448, 448).astype(np.float32)
+            want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(Q[i, j * 128:(j + 1) * 128], want), (i, j)
+
+
 # ---------------------------------------------------------- acceptance bound
 
 def pin_bound_constants(orc):
@@ -527,4 +592,5 @@ ALL_PINS = [pin_identity, pin_selection, pin_rank1, pin_all_ones, pin_bruteforce
             pin_fp8_layout_and_rows, pin_decoders, pin_rounding, pin_quant_codes_match_torch,
             pin_quant_scales_and_bounds, pin_quant_edge_blocks, pin_quant_block_relation,
             pin_quant_matches_generator, pin_gemm_quant_identity, pin_gemm_quant_integers,
+            pin_swiglu_closed_forms, pin_swiglu_selection, pin_swiglu_quant_large_gate,
             pin_bound_constants, pin_bound_model]

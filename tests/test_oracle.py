@@ -44,6 +44,11 @@ MUTATIONS = [
      "return (uint8_t)lo;"),
     ("quantiser amax of the first column only", "for (int64_t k = k0; k < k1; ++k) {\n          float a",
      "for (int64_t k = k0; k < k0 + 1; ++k) {\n          float a"),
+    ("silu with e^g", "G[t] / (1.0 + exp(-G[t])) * U[t]", "G[t] / (1.0 + exp(G[t])) * U[t]"),
+    ("gate and up swapped", "G[t] / (1.0 + exp(-G[t])) * U[t]", "U[t] / (1.0 + exp(-U[t])) * G[t]"),
+    ("no sigmoid on the gate", "G[t] / (1.0 + exp(-G[t])) * U[t]", "G[t] * U[t]"),
+    ("sigmoid without the gate factor", "G[t] / (1.0 + exp(-G[t])) * U[t]",
+     "1.0 / (1.0 + exp(-G[t])) * U[t]"),
     ("bound constants of bf16 and fp16 swapped", "const int p = fmt == FMT_F16 ? 11 : 8;",
      "const int p = fmt == FMT_F16 ? 8 : 11;"),
     ("bound of eight unit roundoffs", "ldexp(4.0, -p) * S[t]", "ldexp(8.0, -p) * S[t]"),
