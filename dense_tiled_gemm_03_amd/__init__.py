@@ -23,7 +23,8 @@ EXPORTS = ("tg_status_string", "tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8_block
            "tg_gemm_grouped_bf16", "tg_gemm_grouped_plan", "tg_gemm_grouped_fp8_blockscaled",
            "tg_gemm_grouped_fp8_plan", "tg_gemm_f16_quant_fp8", "tg_gemm_bf16_quant_fp8",
            "tg_gemm_quant_fp8_plan", "tg_gemm_f16_ws", "tg_gemm_bf16_ws", "tg_gemm_workspace_size",
-           "tg_gemm_plan_ws", "tg_gemm_bf16_static_scratch")
+           "tg_gemm_plan_ws", "tg_gemm_bf16_static_scratch", "tg_gemm_f16_swiglu_quant_fp8",
+           "tg_gemm_bf16_swiglu_quant_fp8", "tg_gemm_swiglu_quant_fp8_plan")
 
 
 class TgError(RuntimeError):
@@ -88,6 +89,12 @@ def load():
         getattr(lib, name).restype = c_int
     lib.tg_gemm_quant_fp8_plan.argtypes = [c_int] + sigq
     lib.tg_gemm_quant_fp8_plan.restype = ctypes.c_char_p
+    sigs = [i64, i64, i64, vp, i64, i64, vp, vp, i64, i64, vp, i64, vp, i64, i64]
+    for name in ("tg_gemm_f16_swiglu_quant_fp8", "tg_gemm_bf16_swiglu_quant_fp8"):
+        getattr(lib, name).argtypes = sigs + [vp]
+        getattr(lib, name).restype = c_int
+    lib.tg_gemm_swiglu_quant_fp8_plan.argtypes = [c_int] + sigs
+    lib.tg_gemm_swiglu_quant_fp8_plan.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -175,6 +182,25 @@ def tg_gemm_bf16_quant_fp8(M, N, K, A, sam, sak, B, sbk, sbn, Q, sqm, S, ssm, ss
 
 def tg_gemm_quant_fp8_plan(op, M, N, K, A, sam, sak, B, sbk, sbn, Q, sqm, S, ssm, ssj):
     r = load().tg_gemm_quant_fp8_plan(op, M, N, K, A, sam, sak, B, sbk, sbn, Q, sqm, S, ssm, ssj)
+    return None if r is None else r.decode()
+
+
+def tg_gemm_f16_swiglu_quant_fp8(M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm, S, ssm, ssj,
+                                 stream=0):
+    return _check(load().tg_gemm_f16_swiglu_quant_fp8(M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q,
+                                                      sqm, S, ssm, ssj, stream))
+
+
+def tg_gemm_bf16_swiglu_quant_fp8(M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm, S, ssm, ssj,
+                                  stream=0):
+    return _check(load().tg_gemm_bf16_swiglu_quant_fp8(M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q,
+                                                       sqm, S, ssm, ssj, stream))
+
+
+def tg_gemm_swiglu_quant_fp8_plan(op, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm, S, ssm,
+                                  ssj):
+    r = load().tg_gemm_swiglu_quant_fp8_plan(op, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm,
+                                             S, ssm, ssj)
     return None if r is None else r.decode()
 
 

@@ -65,10 +65,18 @@ struct PPTile {
 // SPLITS > 1: this workgroup runs split sk.split of SPLITS (== sk.splits)
 // equal ranges of the K slices and the tile's partials are combined as in
 // the four-wave kernel (combine_splits); N x K tiles only.
-template <typename T, typename Cfg, bool QUANT = false, bool BKN = false, int SPLITS = 1>
+// SWIGLU (with QUANT, N x K, 256 x 256 tiles): the tile covers 128 output
+// columns; B stage rows 0 .. 127 are those columns' rows of the gate weights
+// (a.B) and rows 128 .. 255 the same rows of the up weights (`up`, same
+// strides), so group 0 accumulates the gate product g and group 1 the up
+// product u of the same C block; the epilogue hands u to group 0 through
+// LDS, which quantises h = silu(g) u.
+template <typename T, typename Cfg, bool QUANT = false, bool BKN = false, int SPLITS = 1,
+          bool SWIGLU = false>
 __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
                                         const QuantOut& qo = QuantOut{},
-                                        const SplitK& sk = SplitK{1, 0, 0, nullptr, nullptr}) {
+                                        const SplitK& sk = SplitK{1, 0, 0, nullptr, nullptr},
+                                        const void* up = nullptr) {
   typedef typename Elem<T>::x8 T8;
   typedef f32x4 Acc;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
@@ -76,13 +84,16 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   constexpr int A_ST = Cfg::A_ST, B_ST = Cfg::B_ST;
   constexpr bool SPLIT = SPLITS > 1;
   static_assert(!(SPLIT && (QUANT || BKN)), "split K runs N x K tiles with the plain epilogue");
+  static_assert(!SWIGLU || (QUANT && !BKN && !SPLIT && BN == 256),
+                "SwiGLU: N x K weights, 256 x 256 tiles, quantised output");
   char* const lds = tile_lds<Cfg::LDS_BYTES>();
   auto a_off = [](int s) { return s * Cfg::A_BYTES; };
   auto b_off = [](int s) { return A_ST * Cfg::A_BYTES + s * Cfg::B_BYTES; };
   const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
 
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  // first row and first (output) column of the tile
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * (SWIGLU ? BN / 2 : BN);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = w >> 2, q = w & 3;  // group, wave within the group (its SIMD)
@@ -107,12 +118,17 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
   // Operand tiles as buffer descriptors that end at the last valid element:
   // A rows m0 .. of length K; B rows n0 .. of length K (N x K), or B rows
   // 0 .. K-1 from column n0 (K x N).
-  const int rows_a = (int)min<int64_t>(BM, a.M - m0), rows_b = (int)min<int64_t>(BN, a.N - n0);
+  // (SwiGLU: rb the gate weights' rows n0 .., rbu the up weights' rows n0 ..)
+  const int rows_a = (int)min<int64_t>(BM, a.M - m0);
+  const int rows_b = (int)min<int64_t>(SWIGLU ? BN / 2 : BN, a.N - n0);
   const T* Ab = static_cast<const T*>(a.A) + m0 * a.sam;
   const T* Bb = static_cast<const T*>(a.B) + (BKN ? n0 : n0 * a.sbn);
   const i32x4 ra = make_desc(Ab, (uint32_t)(((rows_a - 1) * lda + K) * 2));
   const i32x4 rb =
       make_desc(Bb, (uint32_t)(BKN ? ((K - 1) * ldb + rows_b) * 2 : ((rows_b - 1) * ldb + K) * 2));
+  i32x4 rbu = rb;
+  if constexpr (SWIGLU)
+    rbu = make_desc(static_cast<const T*>(up) + n0 * a.sbn, (uint32_t)(((rows_b - 1) * ldb + K) * 2));
 
   // Loads: wave q's i-th load of a stage fills its rows 8 (4i + q) .. + 7;
   // lane l writes row 8 (4i + q) + (l >> 3) at chunk position l & 7, i.e.
@@ -158,6 +174,11 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
         const bool rin = k0 >= 0 && k0 + 16 * q + 8 * hi + (lane >> 3) < k_end;
         load_lds16(rb, lds32 + b_off(slot) + quarter * 8192 + (2 * q + hi) * 1024,
                    rin ? nb_lane[hi] + (uint32_t)k0 * ldb * 2 + quarter * 128 : kOutOfRange);
+      } else if constexpr (SWIGLU) {
+        // loads 0 .. B_LOADS/2 - 1 fill the gate half, the others the up half
+        constexpr int H = Cfg::B_LOADS / 2;
+        load_lds16(i < H ? rb : rbu, base + i * 4096,
+                   kin ? l_lane + (i % H) * l_step + 2 * k0 : kOutOfRange);
       } else {
         load_lds16(rb, base + i * 4096, kin ? l_lane + i * l_step + 2 * k0 : kOutOfRange);
       }
@@ -302,6 +323,39 @@ __device__ __forceinline__ void pp_body(const GemmArgs& a, int tm, int tn,
     if (!combine_splits<512, 12, SPLITS>(acc, sk, (int)threadIdx.x)) return;
   }
 
+  if constexpr (SWIGLU) {
+    // Group 1's up accumulators go to the group 0 wave on the same SIMD
+    // (same rows and columns) through the LDS, which both loops have left
+    // idle: every load has landed and every fragment read is done.  Slot of
+    // wave q's accumulator (i, j, v): ((q FM + i) FN + j) 4 + v, 64 lanes of
+    // 4 bytes each (128 KiB in all).
+    static_assert(4 * FM * FN * 4 * 64 * 4 <= Cfg::LDS_BYTES, "the up tile fits the LDS");
+    float* xch = reinterpret_cast<float*>(lds);
+    __syncthreads();
+    if (g == 1) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) xch[(((q * FM + i) * FN + j) * 4 + v) * 64 + lane] = acc[i][j][v];
+    }
+    __syncthreads();
+    if (g == 1) return;
+    // h = silu(g) u = g u / (1 + e^-g): e^-g overflows to inf for very
+    // negative g, which gives h = 0 with the sign of g u
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gv = acc[i][j][v];
+          const float uv = xch[(((q * FM + i) * FN + j) * 4 + v) * 64 + lane];
+          acc[i][j][v] = gv * uv / (1.0f + expf(-gv));
+        }
+  }
+
   if constexpr (QUANT) {
     // fp8 output: with 256 x 256 tiles each wave's 128 columns are one
     // 1 x 128 slice of C, quantised straight from the accumulators
@@ -382,6 +436,17 @@ __global__ __launch_bounds__(512) void gemm16_pp_q8(GemmArgs a, int tiles_m, int
   int tm, tn;
   tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
   pp_body<T, Cfg, true, BKN>(a, tm, tn, qo);
+}
+
+// Fused SwiGLU with an fp8 output (256 x 256 tiles, each over 128 output
+// columns: tiles_n = ceil(N / 128)): gate weights a.B, up weights `up`, both
+// stored N x K with the same strides.
+template <typename T, typename Cfg>
+__global__ __launch_bounds__(512) void gemm16_pp_swiglu(GemmArgs a, int tiles_m, int tiles_n,
+                                                        QuantOut qo, const void* up) {
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, Cfg::GM, tm, tn);
+  pp_body<T, Cfg, true, false, 1, true>(a, tm, tn, qo, SplitK{1, 0, 0, nullptr, nullptr}, up);
 }
 
 }  // namespace tile

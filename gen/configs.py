@@ -1,4 +1,4 @@
-"""The five GEMM workloads and their seeded input recipes.
+"""The GEMM workloads and their seeded input recipes.
 
 Shapes follow the pages' workloads: the 4096 x 7168 x 16384 bf16 product of
 the Ascend "six-piece" release ("Getting to know TileLang"), the 7168 hidden
@@ -135,3 +135,20 @@ def group_sizes(total: int, G: int, seed: int) -> np.ndarray:
 # N = 4096, K = 7168 (the 7168 hidden size), bf16, B_g stored N x K.
 GROUPED = {"name": "grouped_bf16_8x8192x4096x7168", "G": 8, "rows": 8192, "N": 4096, "K": 7168,
            "seed": 6}
+
+
+# The fused SwiGLU measured by the benchmark: the gate and up projections
+# whose h feeds the 4096 x 7168 x 16384 down projection above -- 4096 rows,
+# hidden size K = 7168, intermediate size N = 16384 per projection, bf16,
+# both weights stored N x K.
+SWIGLU = {"name": "swiglu_bf16_4096x16384x7168", "M": 4096, "N": 16384, "K": 7168, "seed": 7}
+
+
+def swiglu_inputs(M: int, N: int, K: int, seed: int, fmt: str = "bf16"):
+    """Input x (M x K, N(0, 1)) and the gate and up weights (each N x K,
+    N(0, 1) / sqrt(K), so each product element is about N(0, 1)), drawn from
+    streams 0, 1 and 4 of `seed`."""
+    div = math.sqrt(max(K, 1))
+    return {"A": fill((M, K), DIST_NORMAL, seed, 0, fmt),
+            "Bg": fill((N, K), DIST_NORMAL, seed, 1, fmt, divisor=div),
+            "Bu": fill((N, K), DIST_NORMAL, seed, 4, fmt, divisor=div)}

@@ -312,6 +312,45 @@ const char* tg_gemm_quant_fp8_plan(int op, int64_t M, int64_t N, int64_t K,
                                    const void* B, int64_t sbk, int64_t sbn,
                                    void* Q, int64_t sqm, float* S, int64_t ssm, int64_t ssj);
 
+/* Fused SwiGLU with an fp8 output: the gate product G = A * Bg and the up
+ * product U = A * Bu of one input, combined as h = silu(g) * u with
+ * silu(g) = g / (1 + e^-g), and each 1 x 128 row slice of h quantised as
+ * tg_gemm_f16_quant_fp8 quantises C -- "TileKernels deep dive", section 4.3
+ * (the SwiGLU result quantised straight to FP8 without a round trip through
+ * a wide type) and section 7.2 (the FP8 quantisation's scale and cast).
+ * Both products accumulate in fp32 as tg_gemm_f16 / tg_gemm_bf16 do; h is
+ * formed in fp32 from the two accumulators (g * u / (1 + e^-g)); neither
+ * product nor h reaches memory.  The output feeds the down projection as
+ * the A operand (codes and SA) of tg_gemm_fp8_blockscaled.
+ * A: as for tg_gemm_f16.  Bg, Bu (device): the gate and up weights,
+ * K x N with the same strides, B[k,n] at B + k*sbk + n*sbn; the tiled kernel
+ * takes them stored N x K (sbk = 1) as tg_gemm_f16 takes B.  Q, S: as for
+ * tg_gemm_f16_quant_fp8 (code of h[m,n] at Q + m*sqm + n, scale of slice j
+ * of row m at S + m*ssm + j*ssj).  Errors: those of tg_gemm_f16_quant_fp8
+ * with Bg for B, and TG_ERR_INVALID_VALUE for Bu == NULL when M, N, K > 0.
+ * K == 0 gives zero codes and scales of 1.  Q and S must not overlap the
+ * inputs or each other.  Asynchronous on `stream`; nothing is allocated. */
+tg_status tg_gemm_f16_swiglu_quant_fp8(int64_t M, int64_t N, int64_t K,
+                                       const void* A, int64_t sam, int64_t sak,
+                                       const void* Bg, const void* Bu, int64_t sbk, int64_t sbn,
+                                       void* Q, int64_t sqm, float* S, int64_t ssm, int64_t ssj,
+                                       tg_stream_t stream);
+tg_status tg_gemm_bf16_swiglu_quant_fp8(int64_t M, int64_t N, int64_t K,
+                                        const void* A, int64_t sam, int64_t sak,
+                                        const void* Bg, const void* Bu, int64_t sbk, int64_t sbn,
+                                        void* Q, int64_t sqm, float* S, int64_t ssm, int64_t ssj,
+                                        tg_stream_t stream);
+
+/* How a fused SwiGLU call would run: "tile_nt_256x256_swiglu_q8" (both
+ * weights stored N x K and accepted by the N x K tile kernel),
+ * "generic16_32x128_swiglu_q8" (any other call), "none" (no-op) or NULL
+ * (invalid arguments).  op: 0 = f16, 1 = bf16.  Host only. */
+const char* tg_gemm_swiglu_quant_fp8_plan(int op, int64_t M, int64_t N, int64_t K,
+                                          const void* A, int64_t sam, int64_t sak,
+                                          const void* Bg, const void* Bu, int64_t sbk,
+                                          int64_t sbn, void* Q, int64_t sqm, float* S,
+                                          int64_t ssm, int64_t ssj);
+
 /* Name of the kernel a call with these arguments would launch ("none" for a
  * no-op, NULL if the arguments are invalid); nothing is launched.  op: 0 =
  * tg_gemm_f16, 1 = tg_gemm_bf16, 2 = tg_gemm_fp8_blockscaled (the scale

@@ -174,6 +174,47 @@ def test_quant_out_noop_and_plans(lib):
         == "tile_nt_256x256_q8"
 
 
+def _callsw(lib, name, **kw):
+    a = dict(M=8, N=300, K=64, A=PA, sam=64, sak=1, Bg=PB, Bu=PB + 0x8000, sbk=1, sbn=64, Q=PC,
+             sqm=300, S=PS, ssm=3, ssj=1)
+    a.update(kw)
+    args = [a[k] for k in ("M", "N", "K", "A", "sam", "sak", "Bg", "Bu", "sbk", "sbn", "Q", "sqm",
+                           "S", "ssm", "ssj")]
+    if name == "plan":
+        r = lib.tg_gemm_swiglu_quant_fp8_plan(a.get("op", 1), *args)
+        return None if r is None else r.decode()
+    return getattr(lib, name)(*args, None)
+
+
+INVALIDSW = INVALIDQO[:9] + [dict(Bg=0), dict(Bu=0)] + INVALIDQO[10:]
+
+
+@pytest.mark.parametrize("kw", INVALIDSW, ids=[str(k) for k in INVALIDSW])
+@pytest.mark.parametrize("name", ["tg_gemm_f16_swiglu_quant_fp8", "tg_gemm_bf16_swiglu_quant_fp8",
+                                  "plan"])
+def test_swiglu_invalid(lib, name, kw):
+    r = _callsw(lib, name, **kw)
+    assert (r is None) if name == "plan" else (r == tg.TG_ERR_INVALID_VALUE)
+
+
+def test_swiglu_noop_and_plans(lib):
+    for name in ("tg_gemm_f16_swiglu_quant_fp8", "tg_gemm_bf16_swiglu_quant_fp8"):
+        assert _callsw(lib, name, M=0, A=0, Bg=0, Bu=0, Q=0, S=0) == tg.TG_SUCCESS
+        assert _callsw(lib, name, N=0, A=0, Bg=0, Bu=0, Q=0, S=0) == tg.TG_SUCCESS
+    plan = lambda **kw: _callsw(lib, "plan", **kw)  # noqa
+    assert plan() == "tile_nt_256x256_swiglu_q8"
+    assert plan(op=0) == "tile_nt_256x256_swiglu_q8"
+    assert plan(op=2) is None                                  # fp8 inputs: not this entry
+    assert plan(Bu=PB + 2) == "generic16_32x128_swiglu_q8"     # misaligned up weights
+    assert plan(Bg=PB + 2) == "generic16_32x128_swiglu_q8"     # misaligned gate weights
+    assert plan(sbk=304, sbn=1, N=304, sqm=304) == "generic16_32x128_swiglu_q8"  # K x N
+    assert plan(K=0, A=0, Bg=0, Bu=0) == "generic16_32x128_swiglu_q8"
+    assert plan(M=0) == "none"
+    # gate and up projections of a 7168-wide layer over 4096 rows
+    assert plan(M=4096, N=7168, K=7168, sam=7168, sbn=7168, sqm=7168, ssm=56) \
+        == "tile_nt_256x256_swiglu_q8"
+
+
 def _grouped(lib, fn, **kw):
     import numpy as np
     a = dict(G=2, off=[0, 100, 300], N=64, K=128, A=PA, lda=128, B=PB, ldb=128, sbg=64 * 128,

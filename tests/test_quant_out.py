@@ -36,10 +36,11 @@ def _lib(gpu_lib):
     return gpu_lib
 
 
-def _run(fmt, M, N, K, A, sam, sak, B, sbk, sbn, sqm=None, ssm=None, ssj=1):
-    """Run the fused product on device operands; returns (codes M x N,
-    scales M x ceil(N/128), plan), after checking that nothing outside the
-    codes and scales was written."""
+def run_guarded(M, N, launch, sqm=None, ssm=None, ssj=1):
+    """Codes and scales of an fp8-output call behind guard bytes: `launch(Q, sqm,
+    S, ssm, ssj)` (device addresses) runs it and returns its plan.  Returns
+    (codes M x N, scales M x ceil(N/128), plan), after checking that nothing
+    outside the codes and scales was written."""
     nb = -(-N // 128)
     sqm = N if sqm is None else sqm
     ssm = nb * ssj if ssm is None else ssm
@@ -47,13 +48,7 @@ def _run(fmt, M, N, K, A, sam, sak, B, sbk, sbn, sqm=None, ssm=None, ssj=1):
     Qd = torch.full((64 + qspan + 64,), QG, dtype=torch.uint8, device="cuda")
     sspan = (M - 1) * ssm + (nb - 1) * ssj + 1
     Sd = torch.full((16 + sspan + 16,), SG, dtype=torch.float32, device="cuda")
-    fn = tg.tg_gemm_bf16_quant_fp8 if fmt == "bf16" else tg.tg_gemm_f16_quant_fp8
-    op = 1 if fmt == "bf16" else 0
-    plan = tg.tg_gemm_quant_fp8_plan(op, M, N, K, A.data_ptr(), sam, sak, B.data_ptr(), sbk, sbn,
-                                     Qd.data_ptr() + 64, sqm, Sd.data_ptr() + 64, ssm, ssj)
-    H.log(f"gemm->fp8 {fmt} M={M} N={N} K={K} sqm={sqm} ssm={ssm} ssj={ssj} [{plan}]")
-    fn(M, N, K, A.data_ptr(), sam, sak, B.data_ptr(), sbk, sbn, Qd.data_ptr() + 64, sqm,
-       Sd.data_ptr() + 64, ssm, ssj, torch.cuda.current_stream().cuda_stream)
+    plan = launch(Qd.data_ptr() + 64, sqm, Sd.data_ptr() + 64, ssm, ssj)
     torch.cuda.synchronize()
     q = Qd.cpu().numpy()
     s = Sd.cpu().numpy()
@@ -70,6 +65,23 @@ def _run(fmt, M, N, K, A, sam, sak, B, sbk, sbn, sqm=None, ssm=None, ssj=1):
     return Q, S, plan
 
 
+def _run(fmt, M, N, K, A, sam, sak, B, sbk, sbn, sqm=None, ssm=None, ssj=1):
+    """Run the fused product on device operands; returns (codes M x N,
+    scales M x ceil(N/128), plan)."""
+    fn = tg.tg_gemm_bf16_quant_fp8 if fmt == "bf16" else tg.tg_gemm_f16_quant_fp8
+    op = 1 if fmt == "bf16" else 0
+
+    def launch(Q, sqm, S, ssm, ssj):
+        plan = tg.tg_gemm_quant_fp8_plan(op, M, N, K, A.data_ptr(), sam, sak, B.data_ptr(), sbk,
+                                         sbn, Q, sqm, S, ssm, ssj)
+        H.log(f"gemm->fp8 {fmt} M={M} N={N} K={K} sqm={sqm} ssm={ssm} ssj={ssj} [{plan}]")
+        fn(M, N, K, A.data_ptr(), sam, sak, B.data_ptr(), sbk, sbn, Q, sqm, S, ssm, ssj,
+           torch.cuda.current_stream().cuda_stream)
+        return plan
+
+    return run_guarded(M, N, launch, sqm, ssm, ssj)
+
+
 def assert_exact(Q, S, Qo, So, what):
     assert np.array_equal(S.view(np.uint32), So.view(np.uint32)), f"scales differ: {what}"
     bad = Q != Qo
@@ -80,13 +92,18 @@ def assert_exact(Q, S, Qo, So, what):
 
 
 def assert_within(Q, S, C_ref, Sb, K, what):
-    """Scales and dequantised values against the exact product C_ref.  The
-    fp32 accumulation error e is at most K * 2^-24 * sum |a||b| per element;
-    a scale is the fp32 quotient of a maximum within e of the exact one; a
-    code is within half an e4m3fn step of C / scale: 2^-4 relative above the
-    subnormal range, 2^-10 * scale below it."""
+    """Scales and dequantised values against the exact product C_ref, whose
+    fp32 accumulation error is at most K * 2^-24 * sum |a||b| per element."""
+    assert_within_err(Q, S, C_ref, K * 2.0 ** -24 * Sb, what)
+
+
+def assert_within_err(Q, S, C_ref, e, what):
+    """Scales and dequantised values against exact values C_ref, given a
+    bound e on the error of the fp32 values the kernel quantised: a scale is
+    the fp32 quotient of a maximum within e of the exact one; a code is within
+    half an e4m3fn step of C / scale: 2^-4 relative above the subnormal range,
+    2^-10 * scale below it."""
     M, N = C_ref.shape
-    e = K * 2.0 ** -24 * Sb
     for j in range(-(-N // 128)):
         sl = slice(j * 128, min(N, j * 128 + 128))
         amax = np.abs(C_ref[:, sl]).max(axis=1)
