@@ -7,11 +7,13 @@
 // back in a wider type; the down projection then reads it as the A operand
 // of the block-scaled product).  Neither product nor h reaches memory.
 //
-// Kernels: the 256 x 256 tile kernel in its eight-wave ping-pong form, each
-// tile over 128 output columns (B stage rows 0 .. 127 from the gate weights,
-// 128 .. 255 from the up weights, so the two wave groups hold g and u of the
-// same block and meet through LDS in the epilogue), and, for every call it
-// does not take, a fully masked kernel with one 32 x 128 tile per workgroup.
+// Kernels: for M <= 64 a skinny kernel, one 128-column slice per workgroup
+// over the whole of K (below); otherwise the 256 x 256 tile kernel in its
+// eight-wave ping-pong form, each tile over 128 output columns (B stage rows
+// 0 .. 127 from the gate weights, 128 .. 255 from the up weights, so the two
+// wave groups hold g and u of the same block and meet through LDS in the
+// epilogue); and, for every call neither takes, a fully masked kernel with
+// one 32 x 128 tile per workgroup.
 #include "../../include/tg_gemm.h"
 
 #include "tile_mfma.hpp"
@@ -21,6 +23,10 @@ namespace tg {
 namespace {
 
 using tile::QuantOut;
+using tile::kOutOfRange;
+using tile::load_lds16;
+using tile::load_lds16_nt;
+using tile::make_desc;
 
 constexpr int WTM = 32, WTN = 128;  // general kernel's output tile: one slice per row
 constexpr int WK = 32;              // K per step
@@ -104,6 +110,190 @@ __global__ __launch_bounds__(256) void gemm16_generic_swiglu_q8(GemmArgs a, cons
   }
 }
 
+// Decode-sized calls (M <= 64, both operands K-contiguous): the products are
+// bound by streaming the two weight matrices from HBM, which the 256-row tile
+// does with most of its rows empty.  One workgroup of 4 waves owns one
+// 128-column output slice (so the slice's row maxima stay in the workgroup)
+// over the whole of K:
+//  - 64-wide K slices go HBM -> LDS by LDS-direct loads into a 4-stage ring;
+//    a stage holds the slice of A (64 rows), then the slice's 128 gate rows
+//    and its 128 up rows (40 KiB; the weights non-temporal, as they are read
+//    once); one barrier per slice; slice i + 1's fragments are read while
+//    slice i's MFMAs run;
+//  - wave w owns columns 32w .. 32w + 31 of both products: per k16 step two
+//    32x32x16 MFMAs (rows 0-31, 32-63) of the gate and two of the up
+//    weights, so g and u of an element sit in the same lane and h = silu(g) u
+//    is formed in registers;
+//  - the epilogue takes each row's maximum |h| over the wave's 32 columns by
+//    shuffles and over the four waves through LDS, then quantises as the
+//    fp8-output epilogue does.
+// Chunk swizzle, descriptors and edges as in the skinny product: chunk c of
+// stage row r at position c ^ ((r >> 1) & 7); rows past M or N read as zero
+// through the descriptor bounds; chunks past K get an out-of-range offset.
+constexpr int DM = 64;                         // rows of C per workgroup (all of M)
+constexpr int DN = 128;                        // output columns per workgroup (one slice)
+constexpr int DK = 64;                         // k per slice
+constexpr int DROW = DK * 2;                   // 128 bytes per stage row
+constexpr int D_STAGE = (DM + 2 * DN) * DROW;  // 40 KiB: A, gate rows, up rows
+constexpr int D_ST = 4;                        // ring depth
+constexpr int D_ALD = DM / 8 / 4;              // 1 KiB loads per wave per slice: A
+constexpr int D_BLD = DN / 8 / 4;              // each of the gate and up weights
+constexpr int D_NLD = D_ALD + 2 * D_BLD;       // 10
+static_assert(D_ST * D_STAGE <= 160 * 1024, "the ring must fit the LDS");
+static_assert(D_ST * D_NLD <= 63, "loads in flight must fit the vmcnt counter");
+static_assert(4 * DM * 4 <= D_STAGE, "the row maxima fit the first stage");
+
+template <typename T>
+__global__ __launch_bounds__(256) void gemm16_swiglu_skinny(GemmArgs a, const void* up,
+                                                            QuantOut qo) {
+  typedef typename Elem<T>::x8 T8;
+  typedef tile::Mfma32 MMA;
+  __shared__ __attribute__((aligned(1024))) char lds[D_ST * D_STAGE];
+  const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t strip = blockIdx.x, n0 = strip * DN;
+  const int K = (int)a.K;
+  const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
+  const int rows_a = (int)a.M;  // <= 64
+  const int rows_b = (int)min<int64_t>(DN, a.N - n0);
+  const i32x4 ra = make_desc(a.A, (uint32_t)(((rows_a - 1) * lda + K) * 2));
+  const uint32_t b_range = (uint32_t)(((rows_b - 1) * ldb + K) * 2);
+  const i32x4 rg = make_desc(static_cast<const T*>(a.B) + n0 * a.sbn, b_range);
+  const i32x4 ru = make_desc(static_cast<const T*>(up) + n0 * a.sbn, b_range);
+  const int nk = (K + DK - 1) / DK;
+
+  // Wave w's j-th load of a stage fills 8-row group G of the stage: A rows
+  // 16w + 8j (G = 2w + j), gate rows 32w + 8j' (G = 8 + 4w + j'), up rows
+  // 32w + 8j' (G = 24 + 4w + j'); lane l writes stage row 8G + (l >> 3) at
+  // chunk position l & 7, i.e. logical chunk (l & 7) ^ (4 (G & 1) + (l >> 4)).
+  const uint32_t lrow = lane >> 3;
+  const uint32_t lc0 = (lane & 7) ^ (lane >> 4), lc1 = (lane & 7) ^ (4 + (lane >> 4));
+  auto load_slice = [&](int slot, int slice) {
+    if (slice >= nk) return;  // nothing past K (an empty load still costs an issue)
+    const int k0 = slice * DK;
+    const uint32_t stage = lds32 + slot * D_STAGE;
+#pragma unroll
+    for (int j = 0; j < D_ALD; ++j) {
+      const uint32_t c = (j & 1) ? lc1 : lc0;
+      const uint32_t off = (16 * w + 8 * j + lrow) * lda * 2 + 2 * k0 + 16 * c;
+      load_lds16(ra, stage + (2 * w + j) * 1024, k0 + 8 * (int)c < K ? off : kOutOfRange);
+    }
+#pragma unroll
+    for (int j = 0; j < D_BLD; ++j) {
+      const uint32_t c = (j & 1) ? lc1 : lc0;
+      const uint32_t off = (32 * w + 8 * j + lrow) * ldb * 2 + 2 * k0 + 16 * c;
+      const bool kin = k0 + 8 * (int)c < K;
+      load_lds16_nt(rg, stage + (8 + 4 * w + j) * 1024, kin ? off : kOutOfRange);
+      load_lds16_nt(ru, stage + (24 + 4 * w + j) * 1024, kin ? off : kOutOfRange);
+    }
+  };
+
+  // Fragment reads (32x32x16): row (32-aligned base) + (l & 31), chunk
+  // 2s + (l >> 5) for k16 step s, at position chunk ^ ((l >> 1) & 7).
+  const int sw = (lane >> 1) & 7;
+  int rd[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) rd[s] = (lane & 31) * DROW + (((2 * s + (lane >> 5)) ^ sw) * 16);
+  const int g_rows = (DM + 32 * w) * DROW, u_rows = (DM + DN + 32 * w) * DROW;
+
+  f32x16 acc_g[2], acc_u[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc_g[i][v] = acc_u[i][v] = 0.0f;
+
+  T8 fa0[2][4], fa1[2][4], fg[2][4], fu[2][4];
+  auto read_slice = [&](int buf, int slot) {
+    const char* base = lds + slot * D_STAGE;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      fa0[buf][s] = *reinterpret_cast<const T8*>(base + rd[s]);
+      fa1[buf][s] = *reinterpret_cast<const T8*>(base + 32 * DROW + rd[s]);
+      fg[buf][s] = *reinterpret_cast<const T8*>(base + g_rows + rd[s]);
+      fu[buf][s] = *reinterpret_cast<const T8*>(base + u_rows + rd[s]);
+    }
+  };
+  // One slice: wait until slice i + 1 has landed (at most the loads of the
+  // D_ST - 2 slices issued after it outstanding; near the end, where fewer
+  // follow, every load) and every wave's reads of slice i are done; refill
+  // slice i's slot with slice i + D_ST; read slice i + 1; multiply slice i.
+  auto step = [&](int i, int cur) {
+    if (i + D_ST - 1 < nk)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((D_ST - 2) * D_NLD) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+    load_slice(i % D_ST, i + D_ST);
+    read_slice(cur ^ 1, (i + 1) % D_ST);
+    __builtin_amdgcn_sched_barrier(0);  // reads ahead of the MFMAs
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      acc_g[0] = mfma32x32x16(fa0[cur][s], fg[cur][s], acc_g[0]);
+      acc_g[1] = mfma32x32x16(fa1[cur][s], fg[cur][s], acc_g[1]);
+      acc_u[0] = mfma32x32x16(fa0[cur][s], fu[cur][s], acc_u[0]);
+      acc_u[1] = mfma32x32x16(fa1[cur][s], fu[cur][s], acc_u[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int p = 0; p < D_ST; ++p) load_slice(p, p);
+  if (D_ST <= nk)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((D_ST - 1) * D_NLD) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_barrier" ::: "memory");
+  read_slice(0, 0);
+  int i = 0;
+  for (; i + 1 < nk; i += 2) {
+    step(i, 0);
+    step(i + 1, 1);
+  }
+  if (i < nk) step(i, 0);
+  // every load has landed; once every wave is past its last reads the LDS
+  // holds the row maxima
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // h = silu(g) u; lane l holds column 32w + (l & 31), rows 32i + out_row(l, v)
+  f32x16 h[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      h[b][v] = acc_g[b][v] * acc_u[b][v] / (1.0f + expf(-acc_g[b][v]));
+  // Columns past N are left out of the maxima explicitly: with weight rows
+  // closer than K apart, the rows past N are not all outside the descriptor.
+  float* rmax = reinterpret_cast<float*>(lds);  // [wave][row]
+  const int64_t c = n0 + 32 * w + (lane & 31);
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float m = c < a.N ? fabsf(h[b][v]) : 0.0f;
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+      if ((lane & 31) == 0) rmax[w * DM + 32 * b + MMA::out_row(lane, v)] = m;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = 32 * b + MMA::out_row(lane, v);
+      const float amax = fmaxf(fmaxf(rmax[row], rmax[DM + row]),
+                               fmaxf(rmax[2 * DM + row], rmax[3 * DM + row]));
+      bool zero;
+      const float sc = block_scale(amax, zero);
+      if (row < a.M) {
+        if (c < a.N) qo.Q[row * qo.sqm + c] = (uint8_t)code_of(h[b][v], sc, zero);
+        if (w == 0 && (lane & 31) == 0) qo.S[row * qo.ssm + strip * qo.ssj] = sc;
+      }
+    }
+}
+
 struct Call {
   Op op;
   GemmArgs a;       // B is the gate weights; C and scm stand for Q and sqm
@@ -131,27 +321,45 @@ tg_status validate(const Call& c) {
   return TG_SUCCESS;
 }
 
-// The tiled kernel takes the calls the N x K tile kernel takes for both
-// weight matrices (K-contiguous, 16-byte aligned rows, descriptor ranges).
-bool tiled(const Call& c) {
+enum class Path { Skinny, Tile, Generic };
+
+// Decode-sized calls take the skinny kernel and the rest of the N x K calls
+// the tile kernel, when the skinny / N x K tile product takes the call with
+// each weight matrix as B (K-contiguous, 16-byte aligned rows, descriptor
+// ranges); everything else the masked kernel.
+Path path_of(const Call& c) {
   GemmArgs u = c.a;
   u.B = c.up;
-  return variant_tile_nt16()->accepts(c.op, c.a) && variant_tile_nt16()->accepts(c.op, u);
+  if (variant_skinny16()->accepts(c.op, c.a) && variant_skinny16()->accepts(c.op, u))
+    return Path::Skinny;
+  if (variant_tile_nt16()->accepts(c.op, c.a) && variant_tile_nt16()->accepts(c.op, u))
+    return Path::Tile;
+  return Path::Generic;
+}
+
+int64_t grid_of(const Call& c, Path p) {
+  switch (p) {
+    case Path::Skinny: return cdiv(c.a.N, DN);
+    case Path::Tile: return cdiv(c.a.M, 256) * cdiv(c.a.N, 128);
+    default: return cdiv(c.a.M, WTM) * cdiv(c.a.N, WTN);
+  }
 }
 
 template <typename T>
-hipError_t launch_t(const Call& c, bool tile, hipStream_t s) {
+hipError_t launch_t(const Call& c, Path p, hipStream_t s) {
   const GemmArgs& a = c.a;
-  if (!tile) {
-    const int64_t tn = cdiv(a.N, WTN), tiles = cdiv(a.M, WTM) * tn;
-    hipLaunchKernelGGL(gemm16_generic_swiglu_q8<T>, dim3((unsigned)tiles), dim3(256), 0, s, a,
-                       c.up, c.qo, tn);
-    return hipGetLastError();
+  const unsigned grid = (unsigned)grid_of(c, p);
+  if (p == Path::Skinny) {
+    hipLaunchKernelGGL(gemm16_swiglu_skinny<T>, dim3(grid), dim3(256), 0, s, a, c.up, c.qo);
+  } else if (p == Path::Generic) {
+    hipLaunchKernelGGL(gemm16_generic_swiglu_q8<T>, dim3(grid), dim3(256), 0, s, a, c.up, c.qo,
+                       cdiv(a.N, WTN));
+  } else {
+    typedef tile::PPTile<256> Cfg;
+    const int tm = (int)cdiv(a.M, Cfg::BM), tn = (int)cdiv(a.N, Cfg::BN / 2);
+    hipLaunchKernelGGL((tile::gemm16_pp_swiglu<T, Cfg>), dim3(grid), dim3(512), 0, s, a, tm, tn,
+                       c.qo, c.up);
   }
-  typedef tile::PPTile<256> Cfg;
-  const int tm = (int)cdiv(a.M, Cfg::BM), tn = (int)cdiv(a.N, Cfg::BN / 2);
-  hipLaunchKernelGGL((tile::gemm16_pp_swiglu<T, Cfg>), dim3(tm * tn), dim3(512), 0, s, a, tm, tn,
-                     c.qo, c.up);
   return hipGetLastError();
 }
 
@@ -159,13 +367,10 @@ tg_status run(const Call& c, tg_stream_t stream) {
   tg_status st = validate(c);
   if (st != TG_SUCCESS) return st;
   if (c.a.M == 0 || c.a.N == 0) return TG_SUCCESS;
-  const bool tile = tiled(c);
-  const int64_t tiles = tile ? cdiv(c.a.M, 256) * cdiv(c.a.N, 128)
-                             : cdiv(c.a.M, WTM) * cdiv(c.a.N, WTN);
-  if (tiles >= (int64_t(1) << 31)) return TG_ERR_UNSUPPORTED;
+  const Path p = path_of(c);
+  if (grid_of(c, p) >= (int64_t(1) << 31)) return TG_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e =
-      c.op == Op::BF16 ? launch_t<__bf16>(c, tile, s) : launch_t<_Float16>(c, tile, s);
+  const hipError_t e = c.op == Op::BF16 ? launch_t<__bf16>(c, p, s) : launch_t<_Float16>(c, p, s);
   return e == hipSuccess ? TG_SUCCESS : TG_ERR_LAUNCH;
 }
 
@@ -212,7 +417,11 @@ const char* tg_gemm_swiglu_quant_fp8_plan(int op, int64_t M, int64_t N, int64_t 
                               sqm, S, ssm, ssj);
   if (tg::validate(c) != TG_SUCCESS) return nullptr;
   if (M == 0 || N == 0) return "none";
-  return tg::tiled(c) ? "tile_nt_256x256_swiglu_q8" : "generic16_32x128_swiglu_q8";
+  switch (tg::path_of(c)) {
+    case tg::Path::Skinny: return "skinny_64x128_swiglu_q8";
+    case tg::Path::Tile: return "tile_nt_256x256_swiglu_q8";
+    default: return "generic16_32x128_swiglu_q8";
+  }
 }
 
 }  // extern "C"

@@ -341,10 +341,12 @@ tg_status tg_gemm_bf16_swiglu_quant_fp8(int64_t M, int64_t N, int64_t K,
                                         void* Q, int64_t sqm, float* S, int64_t ssm, int64_t ssj,
                                         tg_stream_t stream);
 
-/* How a fused SwiGLU call would run: "tile_nt_256x256_swiglu_q8" (both
- * weights stored N x K and accepted by the N x K tile kernel),
- * "generic16_32x128_swiglu_q8" (any other call), "none" (no-op) or NULL
- * (invalid arguments).  op: 0 = f16, 1 = bf16.  Host only. */
+/* How a fused SwiGLU call would run: "skinny_64x128_swiglu_q8" (M <= 64,
+ * both weights stored N x K: one workgroup per 128-column slice over the
+ * whole of K), "tile_nt_256x256_swiglu_q8" (larger M, both weights stored
+ * N x K and accepted by the N x K tile kernel), "generic16_32x128_swiglu_q8"
+ * (any other call), "none" (no-op) or NULL (invalid arguments).  op: 0 =
+ * f16, 1 = bf16.  Host only. */
 const char* tg_gemm_swiglu_quant_fp8_plan(int op, int64_t M, int64_t N, int64_t K,
                                           const void* A, int64_t sam, int64_t sak,
                                           const void* Bg, const void* Bu, int64_t sbk,

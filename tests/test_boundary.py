@@ -202,12 +202,16 @@ def test_swiglu_noop_and_plans(lib):
         assert _callsw(lib, name, M=0, A=0, Bg=0, Bu=0, Q=0, S=0) == tg.TG_SUCCESS
         assert _callsw(lib, name, N=0, A=0, Bg=0, Bu=0, Q=0, S=0) == tg.TG_SUCCESS
     plan = lambda **kw: _callsw(lib, "plan", **kw)  # noqa
-    assert plan() == "tile_nt_256x256_swiglu_q8"
-    assert plan(op=0) == "tile_nt_256x256_swiglu_q8"
+    assert plan() == "skinny_64x128_swiglu_q8"                 # M <= 64
+    assert plan(op=0) == "skinny_64x128_swiglu_q8"
+    assert plan(M=64) == "skinny_64x128_swiglu_q8"
+    assert plan(M=65, ssm=3) == "tile_nt_256x256_swiglu_q8"
+    assert plan(M=1, K=7168, sam=7168, sbn=7168) == "skinny_64x128_swiglu_q8"
     assert plan(op=2) is None                                  # fp8 inputs: not this entry
-    assert plan(Bu=PB + 2) == "generic16_32x128_swiglu_q8"     # misaligned up weights
-    assert plan(Bg=PB + 2) == "generic16_32x128_swiglu_q8"     # misaligned gate weights
-    assert plan(sbk=304, sbn=1, N=304, sqm=304) == "generic16_32x128_swiglu_q8"  # K x N
+    for M in (8, 300):
+        assert plan(M=M, Bu=PB + 2) == "generic16_32x128_swiglu_q8"  # misaligned up weights
+        assert plan(M=M, Bg=PB + 2) == "generic16_32x128_swiglu_q8"  # misaligned gate weights
+        assert plan(M=M, sbk=304, sbn=1, N=304, sqm=304) == "generic16_32x128_swiglu_q8"  # K x N
     assert plan(K=0, A=0, Bg=0, Bu=0) == "generic16_32x128_swiglu_q8"
     assert plan(M=0) == "none"
     # gate and up projections of a 7168-wide layer over 4096 rows

@@ -10,10 +10,11 @@ preconditions are asserted on the oracle's values).  Normal mode: seeded
 N(0, 1) input and N(0, 1)/sqrt(K) weights (gate values about N(0, 1), the
 curved part of silu); each scale and dequantised value must lie within the
 bound that the products' fp32 accumulation error, carried through h, and half
-an e4m3fn step allow.  The cases reach both kernels, ragged edges, a grid of
+an e4m3fn step allow.  The cases reach all three kernels, ragged edges, a grid of
 more than one round of workgroups, padded code and scale strides behind guard
-bytes, K = 0, the 4096 x 16384 x 7168 shape on sampled rows, and the output
-fed to tg_gemm_fp8_blockscaled as the down projection's A operand.
+bytes, K = 0, weight rows closer than K apart, the 4096 x 16384 x 7168 shape on
+sampled rows, the 64 x 16384 x 7168 decode shape in full, and the output fed
+to tg_gemm_fp8_blockscaled as the down projection's A operand.
 """
 from __future__ import annotations
 
@@ -130,9 +131,13 @@ def _check(fmt, M, N, K, layout, seed, want=None):
 CASES = [
     (300, 500, 256, "nk", "tile_nt_256x256_swiglu_q8"),
     (256, 256, 64, "nk", "tile_nt_256x256_swiglu_q8"),
-    (33, 129, 8, "nk", "tile_nt_256x256_swiglu_q8"),
+    (33, 129, 8, "nk", "skinny_64x128_swiglu_q8"),
     (513, 392, 200, "nk", "tile_nt_256x256_swiglu_q8"),
-    (1, 1000, 520, "nk", "tile_nt_256x256_swiglu_q8"),
+    (65, 300, 136, "nk", "tile_nt_256x256_swiglu_q8"),
+    (1, 1000, 520, "nk", "skinny_64x128_swiglu_q8"),
+    (64, 600, 1000, "nk", "skinny_64x128_swiglu_q8"),
+    (17, 300, 200, "nk", "skinny_64x128_swiglu_q8"),
+    (64, 256, 64, "padded", "skinny_64x128_swiglu_q8"),
     (300, 256, 256, "padded", "tile_nt_256x256_swiglu_q8"),
     (100, 300, 100, "padded", "generic16_32x128_swiglu_q8"),
     (70, 200, 96, "kn", "generic16_32x128_swiglu_q8"),
@@ -146,6 +151,41 @@ CASES = [
 def test_swiglu(fmt, case):
     M, N, K, layout, want = case
     _check(fmt, M, N, K, layout, 3100 + M + N + K, want)
+
+
+def test_swiglu_decode_shape():
+    """The gate and up projections of 64 decode rows, 64 x 16384 x 7168 (the
+    skinny kernel: one workgroup per 128-column slice over all of K), every
+    row, in the workload's normal recipe, within the bound."""
+    M, N, K = 64, 16384, 7168
+    d = configs.swiglu_inputs(M, N, K, 3700)
+    Q, S, plan = _run("bf16", M, N, K, H.dev(d["A"]), K, 1, H.dev(d["Bg"]), H.dev(d["Bu"]), 1, K)
+    assert plan == "skinny_64x128_swiglu_q8", plan
+    _, _, Ho, G, U, Sg, Su = oracle.swiglu_quant_fp8("bf16", M, N, K, d["A"], K, 1, d["Bg"],
+                                                     d["Bu"], 1, K)
+    assert_within_err(Q, S, Ho, _h_error(K, G, U, Sg, Su), "decode shape, normal")
+
+
+@pytest.mark.parametrize("M", [20, 200])
+def test_swiglu_overlapping_weight_rows(M):
+    """Weight rows 8 elements apart with K = 64 (legal: the weights are only
+    read): the rows past N of the last 128-column slice then lie inside the
+    buffer, and their products must still stay out of that slice's row
+    maxima.  Integer inputs, bit for bit, on both the skinny and the tile
+    kernel."""
+    N, K, sbn = 200, 64, 8
+    fmt = "bf16"
+    g_lo = -(-GATE_MIN // K)
+    A = _ints((M, K), 3800, 0, 1, 2, fmt)
+    span = (N - 1) * sbn + K
+    Bg = _ints((span,), 3800, 1, g_lo, g_lo + 1, fmt)
+    Bu = _ints((span,), 3800, 4, -2, 2, fmt)
+    A, Bg, Bu = _encode(fmt, A), _encode(fmt, Bg), _encode(fmt, Bu)
+    Q, S, plan = _run(fmt, M, N, K, H.dev(A), K, 1, H.dev(Bg), H.dev(Bu), 1, sbn)
+    assert plan == ("skinny_64x128_swiglu_q8" if M <= 64 else "tile_nt_256x256_swiglu_q8"), plan
+    Qo, So, Ho, G, U, _, _ = oracle.swiglu_quant_fp8(fmt, M, N, K, A, K, 1, Bg, Bu, 1, sbn)
+    assert G.min() >= GATE_MIN and np.abs(Ho).max() < 2.0 ** 24 and np.array_equal(Ho, G * U)
+    assert_exact(Q, S, Qo, So, f"overlapping weight rows [{plan}]")
 
 
 def test_swiglu_two_rounds():
