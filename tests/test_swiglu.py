@@ -265,11 +265,12 @@ def test_swiglu_feeds_down_projection():
     H.assert_within_bound("bf16", c, C_ref, Sb, f"down projection [{plan} -> {plan2}]")
 
 
-def test_swiglu_graph_capture():
+@pytest.mark.parametrize("M", [300, 48])
+def test_swiglu_graph_capture(M):
     """The fused SwiGLU allocates nothing, so it can be captured: a graph
     replayed several times with eager work in between gives the eager codes
-    and scales bit for bit."""
-    M, N, K = 300, 512, 256
+    and scales bit for bit (the tile kernel, and the decode-sized one)."""
+    N, K = 512, 256
     A, sam, sak, Bg, Bu, sbk, sbn = _operands("bf16", M, N, K, "nk", 3600, False)
     Ad, Bgd, Bud = H.dev(A), H.dev(Bg), H.dev(Bu)
     nb = -(-N // 128)
@@ -278,7 +279,9 @@ def test_swiglu_graph_capture():
     args = lambda q, s: (M, N, K, Ad.data_ptr(), sam, sak, Bgd.data_ptr(), Bud.data_ptr(),  # noqa
                          sbk, sbn, q.data_ptr(), N, s.data_ptr(), nb, 1)
     stream = torch.cuda.Stream()
-    H.log(f"swiglu graph capture M={M} N={N} K={K}")
+    plan = tg.tg_gemm_swiglu_quant_fp8_plan(1, *args(Q, S))
+    assert plan == ("skinny_64x128_swiglu_q8" if M <= 64 else "tile_nt_256x256_swiglu_q8"), plan
+    H.log(f"swiglu graph capture M={M} N={N} K={K} [{plan}]")
     with torch.cuda.stream(stream):
         tg.tg_gemm_bf16_swiglu_quant_fp8(*args(Q, S), stream.cuda_stream)
     stream.synchronize()
@@ -291,7 +294,7 @@ def test_swiglu_graph_capture():
     for rep in range(3):
         Qg.fill_(0x5A)
         Sg.fill_(-7.0)
-        _run("bf16", 70, 200, 96, Ad, K, 1, Bgd, Bud, 1, K)     # eager work in between
+        _run("bf16", min(M, 40), 200, 96, Ad, K, 1, Bgd, Bud, 1, K)  # eager work in between
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
