@@ -7,6 +7,10 @@
 #include "common.hpp"
 
 namespace tg {
+
+// M <= 64 block-scaled fp8 products (gemm_skinny_fp8.hip)
+const Variant* variant_skinny_fp8();
+
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
@@ -71,7 +75,8 @@ tg_status validate(const Call& c) { return validate_args(c.op, c.a, c.scn); }
 // Kernel tables, most specialised first; the last entry takes every call.
 const Variant* (*const kTable16[])() = {variant_skinny16, variant_tile_nt16, variant_tile_nn16,
                                           variant_generic16};
-const Variant* (*const kTableFp8[])() = {variant_tile_fp8, variant_generic_fp8};
+const Variant* (*const kTableFp8[])() = {variant_skinny_fp8, variant_tile_fp8,
+                                           variant_generic_fp8};
 
 const Variant* select(const Call& c) {
   if (c.op == Op::FP8) {

@@ -397,6 +397,10 @@ def test_workload_plans(lib, name):
 # fewer tile rounds on 256 CUs, a round of 256 x 256 counting 4/3 of one of
 # 256 x 128 (64 against 48 KiB moved per slice).
 FP8_TILE_PLANS = [
+    ((64, 7168, 7168), "skinny_fp8_64x32"),     # M <= 64: 32-column strips over all of K
+    ((1, 100, 16), "skinny_fp8_64x32"),
+    ((65, 7168, 7168), "tile_fp8_256x128"),     # 28 tiles
+    ((64, 100, 24), "generic_fp8_64x64"),       # K not a multiple of 16
     ((256, 128, 128), "tile_fp8_256x128"),      # 1 tile either way
     ((2048, 2048, 1024), "tile_fp8_256x128"),   # 64 or 128 tiles: one round each
     ((1024, 8192, 512), "tile_fp8_256x128"),    # 128 or 256 tiles: one round each

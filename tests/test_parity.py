@@ -730,7 +730,7 @@ def test_tile_nn_padded():
 # ------------------------------------------------------- fp8 tile kernel
 
 FP8_TILE_CASES = [(256, 128, 128), (384, 256, 208), (300, 200, 400), (513, 384, 1040),
-                  (64, 1000, 2048), (1000, 136, 16), (257, 129, 3072)]
+                  (65, 1000, 2048), (1000, 136, 16), (257, 129, 3072)]
 
 
 @pytest.mark.parametrize("case", FP8_TILE_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in FP8_TILE_CASES])
@@ -744,3 +744,27 @@ def test_fp8_tile(case):
     plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 1400 + M + K, int_r=4, pow2_scales=True),
                       exact=True, what="tile int pow2 scales")
     assert plan == "tile_fp8_256x128", plan
+
+
+# ------------------------------------------------------- fp8 skinny kernel
+
+# M <= 64: 32-column strips over the whole of K, each wave one 128-wide block
+# of every four.  Fewer blocks than waves (K = 256), a partial last block
+# (K = 1936, 400), strips past N (N = 300, 130: the last strip partly empty,
+# and strips in the second 128-column B scale block), one row, and the
+# 64 x 7168 x 7168 decode shape in full.
+FP8_SKINNY_CASES = [(1, 1000, 2048), (20, 200, 256), (17, 300, 400), (64, 96, 128),
+                    (33, 40, 1936), (8, 130, 256), (64, 7168, 7168)]
+
+
+@pytest.mark.parametrize("case", FP8_SKINNY_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in FP8_SKINNY_CASES])
+def test_fp8_skinny(case):
+    M, N, K = case
+    plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 1800 + M + K), what="skinny bound")
+    assert plan == "skinny_fp8_64x32", plan
+    plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 1900 + M + K, int_r=16), exact=True,
+                      what="skinny int unit scales")
+    assert plan == "skinny_fp8_64x32", plan
+    plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 2000 + M + K, int_r=4, pow2_scales=True),
+                      exact=True, what="skinny int pow2 scales")
+    assert plan == "skinny_fp8_64x32", plan
