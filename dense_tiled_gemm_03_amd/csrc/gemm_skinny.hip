@@ -271,28 +271,41 @@ __global__ __launch_bounds__(256) void gemm16_skinny(GemmArgs a, int splits, flo
 // edges as gemm16_skinny.  Every workgroup reads all of A (from L2, shared
 // by every strip) and its 32 rows of B (from HBM), so the two streams have
 // different latencies: A and B have LDS rings of their own (WA_ST stages of
-// 8 KiB, WB_ST of 4 KiB), waves 0-1 load only A and waves 2-3 only B, so
-// that each wave's wait counts one stream.  Slices go in groups of WP per
-// barrier (a slice is only 2 MFMAs per wave; the barrier, the fragment reads
-// and their LDS latency are paid once per group).
+// MT rows of A, WB_ST of 4 KiB of B), waves 0-1 load only A and waves 2-3
+// only B, so that each wave's wait counts one stream.  Slices go in groups
+// of WP per barrier (a slice is only 2 MFMAs per wave; the barrier, the
+// fragment reads and their LDS latency are paid once per group).  The kernel
+// takes MT = 32 rows of A per stage for M <= 32 and 64 otherwise: the B ring
+// gets the LDS the smaller A stages free (28 stages against 16), so a decode
+// step with few rows keeps more of B, the stream from HBM, in flight.
 constexpr int WN = 32;                          // columns of C per workgroup
-constexpr int WA_ST = 12, WB_ST = 16;           // stages of the A and B rings
+constexpr int WA_ST = 12;                       // stages of the A ring
 constexpr int WP = 4;                           // slices per barrier
-constexpr int WA_BYTES = SM * ROWB;             // 8 KiB: one A slice
 constexpr int WB_BYTES = WN * ROWB;             // 4 KiB: one B slice
-constexpr int W_LDS = WA_ST * WA_BYTES + WB_ST * WB_BYTES;  // 160 KiB
 constexpr int WRED_PITCH = WN + 4;              // fp32 row pitch of the partial tiles in LDS
-static_assert(W_LDS <= 160 * 1024, "rings must fit the LDS");
-static_assert(WA_ST % WP == 0 && WB_ST % WP == 0 && WA_ST >= 2 * WP && WB_ST >= 2 * WP,
-              "rings hold whole groups, two groups at least");
-static_assert((WA_ST - WP) * 4 <= 63 && (WB_ST - WP) * 2 <= 63,
-              "loads in flight must fit the vmcnt counter");
-static_assert(4 * SM * WRED_PITCH * 4 <= W_LDS, "partial tiles must fit the rings");
 
-template <typename T>
+template <int MT>
+struct WCfg {
+  static constexpr int A_BYTES = MT * ROWB;    // one A slice
+  static constexpr int A_LD = MT / 16;         // loads per slice of an A wave
+  static constexpr int B_ST = (160 * 1024 - WA_ST * A_BYTES) / WB_BYTES / WP * WP;
+  static constexpr int LDS = WA_ST * A_BYTES + B_ST * WB_BYTES;
+  static_assert(MT == 32 || MT == 64, "32 or 64 rows");
+  static_assert(LDS <= 160 * 1024, "rings must fit the LDS");
+  static_assert(WA_ST % WP == 0 && B_ST % WP == 0 && WA_ST >= 2 * WP && B_ST >= 2 * WP,
+                "rings hold whole groups, two groups at least");
+  static_assert((WA_ST - WP) * A_LD <= 63 && (B_ST - WP) * 2 <= 63,
+                "loads in flight must fit the vmcnt counter");
+  static_assert(4 * MT * WRED_PITCH * 4 <= LDS, "partial tiles must fit the rings");
+};
+
+template <typename T, int MT>
 __global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
   typedef typename Elem<T>::x8 T8;
-  __shared__ __attribute__((aligned(1024))) char lds[W_LDS];
+  typedef WCfg<MT> Cfg;
+  constexpr int WA_BYTES = Cfg::A_BYTES, WB_ST = Cfg::B_ST, A_LD = Cfg::A_LD;
+  constexpr int NI = MT / 32;                  // 32-row blocks
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS];
   const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
 
@@ -309,9 +322,10 @@ __global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
   const bool loads_a = w < 2;  // wave-uniform
 
   // Slot s of the A ring at s * WA_BYTES, of the B ring after the A ring.
-  // A slice's 8-row groups: wave w (0, 1) loads A groups 4w .. 4w + 3, wave
-  // w (2, 3) B groups 2(w - 2) .. + 1.  Lane l writes group row l >> 3 at
-  // chunk position l & 7, i.e. logical chunk (l & 7) ^ (4 (g & 1) + (l >> 4)).
+  // A slice's 8-row groups: wave w (0, 1) loads A groups A_LD w .. A_LD w +
+  // A_LD - 1, wave w (2, 3) B groups 2(w - 2) .. + 1.  Lane l writes group
+  // row l >> 3 at chunk position l & 7, i.e. logical chunk (l & 7) ^ (4 (g &
+  // 1) + (l >> 4)).
   const uint32_t lrow = lane >> 3;
   const uint32_t lc0 = (lane & 7) ^ (lane >> 4), lc1 = (lane & 7) ^ (4 + (lane >> 4));
   auto load_a = [&](int slice) {
@@ -319,8 +333,8 @@ __global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
     const int k0 = slice * SK;
     const uint32_t stage = lds32 + (slice % WA_ST) * WA_BYTES;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int g = 4 * w + j;
+    for (int j = 0; j < A_LD; ++j) {
+      const int g = A_LD * w + j;
       const uint32_t c = (g & 1) ? lc1 : lc0;
       const bool kin = k0 + 8 * (int)c < K;
       const uint32_t off = (8 * g + lrow) * lda * 2 + 2 * k0 + 16 * c;
@@ -347,7 +361,7 @@ __global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
   // end of K, where fewer were issued).
   auto wait_first = [&]() {
     if (loads_a) {
-      if (WA_ST <= count) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((WA_ST - WP) * 4) : "memory");
+      if (WA_ST <= count) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((WA_ST - WP) * A_LD) : "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
       if (WB_ST <= count) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((WB_ST - WP) * 2) : "memory");
@@ -357,7 +371,7 @@ __global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
   auto wait_next = [&](int i) {
     if (loads_a) {
       if (i + WA_ST <= count)
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((WA_ST - 2 * WP) * 4) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((WA_ST - 2 * WP) * A_LD) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     } else {
@@ -372,19 +386,19 @@ __global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
   // (l & 31) and 32 + (l & 31), B rows (l & 31), chunk 2w + (l >> 5) at
   // position chunk ^ ((l >> 1) & 7).
   const int rd = (lane & 31) * ROWB + (((2 * w + (lane >> 5)) ^ ((lane >> 1) & 7)) * 16);
-  f32x16 acc[2];
+  f32x16 acc[NI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
-  T8 fa0[2][WP], fa1[2][WP], fb[2][WP];  // [buffer][slice of the group]
+  T8 fa[2][WP][NI], fb[2][WP];  // [buffer][slice of the group][32-row block]
   auto read_group = [&](int buf, int first) {
 #pragma unroll
     for (int h = 0; h < WP; ++h) {
       const char* ab = lds + ((first + h) % WA_ST) * WA_BYTES;
       const char* bb = lds + WA_ST * WA_BYTES + ((first + h) % WB_ST) * WB_BYTES;
-      fa0[buf][h] = *reinterpret_cast<const T8*>(ab + rd);
-      fa1[buf][h] = *reinterpret_cast<const T8*>(ab + 32 * ROWB + rd);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) fa[buf][h][i] = *reinterpret_cast<const T8*>(ab + 32 * i * ROWB + rd);
       fb[buf][h] = *reinterpret_cast<const T8*>(bb + rd);
     }
   };
@@ -405,8 +419,8 @@ __global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
 #pragma unroll
     for (int h = 0; h < WP; ++h)
       if (i + h < count) {
-        acc[0] = mfma32x32x16(fa0[cur][h], fb[cur][h], acc[0]);
-        acc[1] = mfma32x32x16(fa1[cur][h], fb[cur][h], acc[1]);
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) acc[ii] = mfma32x32x16(fa[cur][h][ii], fb[cur][h], acc[ii]);
       }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -433,25 +447,25 @@ __global__ __launch_bounds__(256) void gemm16_skinny_wsplit(GemmArgs a) {
   // l & 31, rows 32i + 8(v/4) + 4(l >> 5) + (v % 4).
   float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int i2 = 0; i2 < 2; ++i2)
+  for (int i2 = 0; i2 < NI; ++i2)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int row = 32 * i2 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      red[(w * SM + row) * WRED_PITCH + (lane & 31)] = acc[i2][v];
+      red[(w * MT + row) * WRED_PITCH + (lane & 31)] = acc[i2][v];
     }
   __syncthreads();
-  // Thread t, step e: float4 q = 256 e + t of the 64 x 32 tile (row q >> 3,
+  // Thread t, step e: float4 q = 256 e + t of the MT x 32 tile (row q >> 3,
   // columns 4 (q & 7) .. + 3), the sum of the four partials in wave order.
   typedef typename Elem<T>::x4 T4;
   T* Cb = static_cast<T*>(a.C);
   const int t = threadIdx.x;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
+  for (int e = 0; e < MT / 32; ++e) {
     const int q = 256 * e + t, row = q >> 3, col = 4 * (q & 7);
     f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww)
-      x += *reinterpret_cast<const f32x4*>(red + (ww * SM + row) * WRED_PITCH + col);
+      x += *reinterpret_cast<const f32x4*>(red + (ww * MT + row) * WRED_PITCH + col);
     if (row >= a.M) continue;
     T* C = Cb + (int64_t)row * a.scm + n0 + col;
     T4 o;
@@ -520,10 +534,17 @@ hipError_t launch(Op op, const GemmArgs& a, const Scratch& ws, hipStream_t strea
   const dim3 block(256);
   if (plan == Skinny::Strip32) {
     const dim3 grid((unsigned)cdiv(a.N, WN));
-    if (op == Op::BF16)
-      hipLaunchKernelGGL(gemm16_skinny_wsplit<__bf16>, grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL(gemm16_skinny_wsplit<_Float16>, grid, block, 0, stream, a);
+    if (a.M <= 32) {
+      if (op == Op::BF16)
+        hipLaunchKernelGGL((gemm16_skinny_wsplit<__bf16, 32>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((gemm16_skinny_wsplit<_Float16, 32>), grid, block, 0, stream, a);
+    } else {
+      if (op == Op::BF16)
+        hipLaunchKernelGGL((gemm16_skinny_wsplit<__bf16, 64>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((gemm16_skinny_wsplit<_Float16, 64>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
   }
   int* counters = nullptr;

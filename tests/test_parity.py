@@ -559,7 +559,10 @@ def test_split_k_scratch_reused_by_more_tiles():
 # and 112 slices leave 0, 2, 3, 1, 1 and 0 over.
 SKINNY_CASES = [(1, 100, 64), (17, 300, 200), (64, 64, 8), (64, 33, 1000), (40, 7168, 1024),
                 (63, 95, 4104), (64, 1000, 2056), (64, 7168, 520), (64, 7168, 7168),
-                (64, 512, 1152), (48, 600, 1192)]
+                (64, 512, 1152), (48, 600, 1192),
+                # M <= 32 (the allocation-free plan's 32-row form, 28 B stages):
+                # more slices than the deeper ring holds, a ragged last group
+                (32, 7168, 7168), (1, 300, 7176), (9, 130, 1800)]
 
 
 @pytest.mark.parametrize("case", SKINNY_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SKINNY_CASES])
