@@ -757,7 +757,7 @@ def test_fp8_tile(case):
 # and strips in the second 128-column B scale block), one row, and the
 # 64 x 7168 x 7168 decode shape in full.
 FP8_SKINNY_CASES = [(1, 1000, 2048), (20, 200, 256), (17, 300, 400), (64, 96, 128),
-                    (33, 40, 1936), (8, 130, 256), (64, 7168, 7168)]
+                    (33, 40, 1936), (8, 130, 256), (5, 16, 256), (64, 7168, 7168)]
 
 
 @pytest.mark.parametrize("case", FP8_SKINNY_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in FP8_SKINNY_CASES])
@@ -771,3 +771,17 @@ def test_fp8_skinny(case):
     plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 2000 + M + K, int_r=4, pow2_scales=True),
                       exact=True, what="skinny int pow2 scales")
     assert plan == "skinny_fp8_64x32", plan
+
+
+def test_fp8_skinny_padded_c():
+    """The skinny fp8 product storing into C rows padded by 40 elements, behind
+    guard bands (nothing outside the M x N block is written)."""
+    M, N, K = 20, 100, 512
+    d = _fp8_inputs(M, N, K, 2100, int_r=16)
+    nkb = d["SA"].shape[1]
+    c, plan = H.run_fp8(M, N, K, H.dev(d["A"]), K, 1, H.dev(d["SA"]), nkb, 1, H.dev(d["B"]),
+                        d["sbk"], d["sbn"], H.dev(d["SB"]), nkb, 1, scm=N + 40)
+    assert plan == "skinny_fp8_64x32", plan
+    C_ref, _ = oracle.gemm_fp8_blockscaled(M, N, K, d["A"], K, 1, d["SA"], nkb, 1, d["B"],
+                                           d["sbk"], d["sbn"], d["SB"], nkb, 1)
+    H.assert_bit_exact("bf16", c, C_ref, f"fp8 skinny, padded C [{plan}]")
