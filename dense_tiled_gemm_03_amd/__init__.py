@@ -24,7 +24,8 @@ EXPORTS = ("tg_status_string", "tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8_block
            "tg_gemm_grouped_fp8_plan", "tg_gemm_f16_quant_fp8", "tg_gemm_bf16_quant_fp8",
            "tg_gemm_quant_fp8_plan", "tg_gemm_f16_ws", "tg_gemm_bf16_ws", "tg_gemm_workspace_size",
            "tg_gemm_plan_ws", "tg_gemm_bf16_static_scratch", "tg_gemm_f16_swiglu_quant_fp8",
-           "tg_gemm_bf16_swiglu_quant_fp8", "tg_gemm_swiglu_quant_fp8_plan")
+           "tg_gemm_bf16_swiglu_quant_fp8", "tg_gemm_swiglu_quant_fp8_plan",
+           "tg_gemm_fp8_blockscaled_ws")
 
 
 class TgError(RuntimeError):
@@ -55,6 +56,9 @@ def load():
     lib.tg_gemm_fp8_blockscaled.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64,
                                             vp, i64, i64, vp, i64, i64, vp, i64, i64, vp]
     lib.tg_gemm_fp8_blockscaled.restype = c_int
+    lib.tg_gemm_fp8_blockscaled_ws.argtypes = (lib.tg_gemm_fp8_blockscaled.argtypes[:-1]
+                                               + [vp, ctypes.c_size_t, vp])
+    lib.tg_gemm_fp8_blockscaled_ws.restype = c_int
     lib.tg_gemm_plan.argtypes = [c_int, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64]
     lib.tg_gemm_plan.restype = ctypes.c_char_p
     sz = ctypes.c_size_t
@@ -160,6 +164,13 @@ def tg_gemm_fp8_blockscaled(M, N, K, A, sam, sak, SA, ssam, ssak, B, sbk, sbn, S
                             C, scm, scn, stream=0):
     return _check(load().tg_gemm_fp8_blockscaled(M, N, K, A, sam, sak, SA, ssam, ssak, B, sbk,
                                                  sbn, SB, ssbn, ssbk, C, scm, scn, stream))
+
+
+def tg_gemm_fp8_blockscaled_ws(M, N, K, A, sam, sak, SA, ssam, ssak, B, sbk, sbn, SB, ssbn,
+                               ssbk, C, scm, scn, workspace, workspace_bytes, stream=0):
+    return _check(load().tg_gemm_fp8_blockscaled_ws(M, N, K, A, sam, sak, SA, ssam, ssak, B, sbk,
+                                                    sbn, SB, ssbn, ssbk, C, scm, scn, workspace,
+                                                    workspace_bytes, stream))
 
 
 def tg_quant_fp8_1x128(R, K, X, ldx, Q, ldq, S, ssr, ssk, stream=0):

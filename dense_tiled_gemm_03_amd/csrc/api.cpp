@@ -198,6 +198,22 @@ tg_status tg_gemm_bf16_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_
   return tg::run(c, tg::Scratch{static_cast<char*>(workspace), workspace_bytes}, stream);
 }
 
+tg_status tg_gemm_fp8_blockscaled_ws(int64_t M, int64_t N, int64_t K, const void* A,
+                                     int64_t sam, int64_t sak, const float* SA, int64_t ssam,
+                                     int64_t ssak, const void* B, int64_t sbk, int64_t sbn,
+                                     const float* SB, int64_t ssbn, int64_t ssbk, void* C,
+                                     int64_t scm, int64_t scn, void* workspace,
+                                     size_t workspace_bytes, tg_stream_t stream) {
+  tg::Call c;
+  c.op = tg::Op::FP8;
+  c.a = tg::GemmArgs{M, N, K, A, sam, sak, B, sbk, sbn, SA, ssam, ssak, SB, ssbn, ssbk, C, scm};
+  c.scn = scn;
+  tg_status st = tg::validate(c);
+  if (st == TG_SUCCESS) st = tg::check_workspace(workspace, workspace_bytes);
+  if (st != TG_SUCCESS) return st;
+  return tg::run(c, tg::Scratch{static_cast<char*>(workspace), workspace_bytes}, stream);
+}
+
 tg_status tg_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K, const void* A,
                                  int64_t sam, int64_t sak, const void* B, int64_t sbk,
                                  int64_t sbn, void* C, int64_t scm, int64_t scn, size_t* bytes) {

@@ -279,6 +279,281 @@ __global__ __launch_bounds__(256) void gemm_fp8_skinny(GemmArgs a) {
   }
 }
 
+// The split plan, for a caller that gives a workspace: the strip kernel above
+// reads all of A once per 32 columns, which at 64 rows is twice the bytes of
+// B it reads, from L2.  Here, as in the 16-bit split plan (gemm_skinny.hip), a
+// workgroup owns 128 columns of C over one of `splits` ranges of the K
+// blocks, so A is read once per 128 columns and each workgroup moves about
+// half the bytes:
+//  - one ring of XST stages shared by the 4 waves, one barrier per block;
+//    a stage holds the block's 64 A rows, their scales and the strip's B
+//    scale, then the strip's 128 B rows; wave w loads A rows 16w .. 16w + 15
+//    and B rows 32w .. 32w + 31, wave 0 the A-row scales, wave 1 the B scale;
+//  - wave w owns columns 32w .. 32w + 31 of the strip, all 64 rows: per block
+//    8 16x16x128 MFMAs, transposed as above, each folded in with SA * SB;
+//  - the fp32 64 x 128 partial tile goes to the workspace; the last of a
+//    strip's workgroups to finish (a device-scope counter) adds the strip's
+//    partial tiles in split order, rounds once to bf16 and clears the counter.
+constexpr int XM = 64, XN = 128;               // rows, columns of C per workgroup
+constexpr int X_SA = 64 * FROW;                // 8 KiB of A codes, then the A-row scales
+constexpr int X_SB = X_SA + 256;               // the strip's B scale
+constexpr int X_B = X_SA + 512;                // B codes
+constexpr int X_STAGE = X_B + XN * FROW;       // 24.5 KiB
+constexpr int XST = 6;                         // ring depth
+constexpr int X_NLD = 6;                       // 16-byte loads per wave per block
+constexpr int X_PITCH = XN + 4;                // fp32 row pitch of the tile in LDS
+constexpr int kMinBlocks = 4;                  // fewest K blocks per split
+constexpr int kCus = 256;
+constexpr int kCoherent = 0x10;                // sc1: device-coherent buffer access
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+static_assert(XST * X_STAGE <= F_LDS_MAX, "the ring fits the LDS");
+static_assert(XM * X_PITCH * 4 <= XST * X_STAGE, "the tile fits the ring");
+static_assert(XST * (X_NLD + 1) <= 63, "loads in flight fit the vmcnt counter");
+static_assert(X_B % 256 == 0 && X_STAGE % 256 == 0, "stage parts on whole bank rows");
+
+__global__ __launch_bounds__(256) void gemm_fp8_skinny_split(GemmArgs a, int splits, float* part,
+                                                             int* counters) {
+  __shared__ __attribute__((aligned(1024))) char lds[XST * X_STAGE];
+  __shared__ int last;  // this workgroup is the strip's last to finish
+  const uint32_t lds32 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int strip = blockIdx.x / splits, split = blockIdx.x % splits;
+  const int64_t n0 = (int64_t)strip * XN;
+  const int K = (int)a.K;
+  const int nkb = (K + FK - 1) / FK;
+  const int b_begin = (int)((int64_t)split * nkb / splits);
+  const int b_end = (int)((int64_t)(split + 1) * nkb / splits);
+  const int count = b_end - b_begin;
+  const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
+  const int rows_a = (int)a.M;
+  const int rows_b = (int)min<int64_t>(XN, a.N - n0);
+  const uint8_t* Bb = static_cast<const uint8_t*>(a.B) + n0 * a.sbn;
+  const i32x4 ra = make_desc(a.A, (uint32_t)((rows_a - 1) * lda + K));
+  const i32x4 rb = make_desc(Bb, (uint32_t)((rows_b - 1) * ldb + K));
+  const i32x4 rsa = make_desc(
+      a.SA, (uint32_t)(((rows_a - 1) * a.ssam + (nkb - 1) * a.ssak + 1) * 4));
+  const i32x4 rsb = make_desc(a.SB + strip * a.ssbn, (uint32_t)(((nkb - 1) * a.ssbk + 1) * 4));
+  const bool scales = w < 2;  // waves 0 and 1 load a scale too (wave-uniform)
+
+  // Block blk (blk - b_begin = i) in slot i % XST.  8-row groups: A group g
+  // at g KiB, B group g at X_B + g KiB; lane l writes group row l >> 3 at
+  // chunk position l & 7, i.e. logical chunk (l & 7) ^ (4 (g & 1) + (l >> 4)).
+  const uint32_t lrow = lane >> 3;
+  const uint32_t lc0 = (lane & 7) ^ (lane >> 4), lc1 = (lane & 7) ^ (4 + (lane >> 4));
+  auto load_block = [&](int slot, int blk) {
+    if (blk >= b_end) return;  // nothing past the range
+    const int k0 = blk * FK;
+    const uint32_t stage = lds32 + slot * X_STAGE;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int g = 2 * w + j;
+      const uint32_t c = (g & 1) ? lc1 : lc0;
+      const bool kin = k0 + 16 * (int)c < K;
+      load_lds16(ra, stage + g * 1024, kin ? (8 * g + lrow) * lda + k0 + 16 * c : kOutOfRange);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int g = 4 * w + j;
+      const uint32_t c = (g & 1) ? lc1 : lc0;
+      const bool kin = k0 + 16 * (int)c < K;
+      load_lds16_nt(rb, stage + X_B + g * 1024,
+                    kin ? (8 * g + lrow) * ldb + k0 + 16 * c : kOutOfRange);
+    }
+    if (w == 0)  // SA[lane, blk]
+      load_lds4(rsa, stage + X_SA,
+                lane < rows_a ? (uint32_t)((lane * a.ssam + blk * a.ssak) * 4) : kOutOfRange);
+    else if (w == 1)  // SB[strip, blk] in lane 0
+      load_lds4(rsb, stage + X_SB, lane == 0 ? (uint32_t)(blk * a.ssbk * 4) : kOutOfRange);
+  };
+
+  // Fragments as in the strip kernel: A row blocks i (rows 16 i + (l & 15)),
+  // this wave's B column blocks j (strip rows 32 w + 16 j + (l & 15)).
+  const int sw = (lane >> 1) & 7, u = lane >> 4;
+  const int rd0 = (lane & 15) * FROW + ((u ^ sw) * 16);
+  const int rd1 = (lane & 15) * FROW + (((u + 4) ^ sw) * 16);
+  auto rd32 = [&](const char* p) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(p + rd0);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + rd1);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  i32x8 fa[2][4], fb[2][2];
+  float s[2][4];
+  auto read_block = [&](int buf, int slot) {
+    const char* st = lds + slot * X_STAGE;
+    const float sb = *reinterpret_cast<const float*>(st + X_SB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[buf][i] = rd32(st + i * 16 * FROW);
+      s[buf][i] = *reinterpret_cast<const float*>(st + X_SA + (16 * i + (lane & 15)) * 4) * sb;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[buf][j] = rd32(st + X_B + (32 * w + 16 * j) * FROW);
+  };
+  // Block i: wait until block i + 1 has landed (at most the loads of the
+  // XST - 2 blocks issued after it outstanding; all, near the end of the
+  // range) and every wave's reads of block i are done; refill block i's slot
+  // with block i + XST; read block i + 1; multiply block i.
+  auto step = [&](int i, int cur) {
+    if (i + XST - 1 < count) {
+      if (scales)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((XST - 2) * (X_NLD + 1)) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((XST - 2) * X_NLD) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_barrier" ::: "memory");
+    load_block(i % XST, b_begin + i + XST);
+    if (i + 1 < count) read_block(cur ^ 1, (i + 1) % XST);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const f32x4 p = mfma16x16x128_e4m3(fb[cur][j], fa[cur][ii], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[j][ii][v] += s[cur][ii] * p[v];
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int p = 0; p < XST; ++p) load_block(p, b_begin + p);
+  if (XST <= count) {
+    if (scales)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((XST - 1) * (X_NLD + 1)) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((XST - 1) * X_NLD) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  asm volatile("s_barrier" ::: "memory");
+  read_block(0, 0);
+  int i = 0;
+  for (; i + 1 < count; i += 2) {
+    step(i, 0);
+    step(i + 1, 1);
+  }
+  if (i < count) step(i, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // The 64 x 128 tile through LDS (wave w's lane l: row 16 i + (l & 15),
+  // columns 32 w + 16 j + 4 u .. + 3), then thread t, step e: float4
+  // q = 256 e + t (row q >> 5, columns 4 (q & 31) .. + 3).
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+      *reinterpret_cast<f32x4*>(red + (16 * ii + (lane & 15)) * X_PITCH + 32 * w + 16 * j +
+                                4 * u) = acc[j][ii];
+  __syncthreads();
+  const int t = threadIdx.x;
+  f32x4 x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int q = 256 * e + t;
+    x[e] = *reinterpret_cast<const f32x4*>(red + (q >> 5) * X_PITCH + 4 * (q & 31));
+  }
+  if (splits > 1) {
+    // Publish this split's tile (device-coherent stores, complete before the
+    // barrier ahead of the counter increment); the strip's last workgroup
+    // adds every split's tile in split order, so the sum does not depend on
+    // which finishes last, and clears the counter for the next call.
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        part + (int64_t)strip * splits * XM * XN, (short)0, splits * XM * XN * 4, 0x00020000);
+    // only the rows of C are stored and read (row (256 e + t) >> 5 < M)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (8 * e + (t >> 5) < a.M)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x[e]), rp,
+                                               (split * XM * XN + 4 * (256 * e + t)) * 4, 0,
+                                               kCoherent);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t == 0) last = atomicAdd(counters + strip, 1) == splits - 1;
+    __syncthreads();
+    if (!last) return;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sp0 = 0; sp0 < splits; sp0 += 4) {
+      u32x4 y[4][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          y[j][e] = 8 * e + (t >> 5) < a.M && sp0 + j < splits
+                        ? __builtin_amdgcn_raw_buffer_load_b128(
+                              rp, ((sp0 + j) * XM * XN + 4 * (256 * e + t)) * 4, 0, kCoherent)
+                        : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (sp0 + j < splits)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] += __builtin_bit_cast(f32x4, y[j][e]);
+    }
+    if (t == 0) __hip_atomic_store(counters + strip, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __bf16* Cb = static_cast<__bf16*>(a.C);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int q = 256 * e + t, row = q >> 5, col = 4 * (q & 31);
+    if (row >= a.M) continue;
+    __bf16* C = Cb + (int64_t)row * a.scm + n0 + col;
+    bf16x4 o;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) o[jj] = to_out<__bf16>(x[e][jj]);
+    if (n0 + col + 4 <= a.N && (reinterpret_cast<uintptr_t>(C) & 7) == 0) {
+      *reinterpret_cast<bf16x4*>(C) = o;
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        if (n0 + col + jj < a.N) C[jj] = o[jj];
+    }
+  }
+}
+
+// Splits of the K blocks: about one workgroup per CU, each with at least
+// kMinBlocks blocks; 1 (no split plan) where the strip kernel is as fast.
+// Both kernels stream the same B bytes per CU; the split saves A bytes and
+// fills the CUs when the strip grid does not, but pays the combine of the
+// partial tiles.  It is taken for more than 32 rows (with fewer, A is
+// small and the strip kernel keeps more of B in flight) when the strip grid
+// is not one nearly full round (kStripRoundMin .. 256 workgroups) or each
+// split has at least kAmortBlocks blocks to amortise the combine.
+constexpr int kStripRoundMin = 192;
+constexpr int kAmortBlocks = 24;
+int choose_splits(const GemmArgs& a) {
+  if (a.M <= 32) return 1;
+  const int64_t strips = cdiv(a.N, XN), nkb = cdiv(a.K, FK);
+  int64_t sp = kCus / strips;
+  if (sp > nkb / kMinBlocks) sp = nkb / kMinBlocks;
+  if (sp < 2) return 1;
+  const int64_t strip_wgs = cdiv(a.N, FN_);
+  const bool full_round = strip_wgs >= kStripRoundMin && strip_wgs <= kCus;
+  if (full_round && nkb / sp < kAmortBlocks) return 1;
+  return (int)sp;
+}
+
+// The split plan's scratch: a counter per strip in the fixed counter area,
+// then each split's 64 x 128 fp32 tile (0: no split plan for this call, or
+// a B strip whose offsets leave the descriptor range).
+size_t scratch_bytes(const GemmArgs& a) {
+  const int64_t strips = cdiv(a.N, XN);
+  const int splits = choose_splits(a);
+  if (splits == 1 || strips > kWorkspaceCounters) return 0;
+  if (XN * a.sbn + a.K >= (int64_t(1) << 30)) return 0;
+  return kWorkspaceCounterBytes + (size_t)strips * splits * XM * XN * 4;
+}
+
 bool aligned16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // At most 64 rows, both code matrices K-contiguous with 16-byte aligned rows
@@ -298,7 +573,15 @@ bool accepts(Op op, const GemmArgs& a) {
   return true;
 }
 
-hipError_t launch(Op, const GemmArgs& a, const Scratch&, hipStream_t s) {
+hipError_t launch(Op, const GemmArgs& a, const Scratch& ws, hipStream_t s) {
+  if (scratch_fits(ws, scratch_bytes(a))) {
+    const int splits = choose_splits(a);
+    const dim3 grid((unsigned)(cdiv(a.N, XN) * splits));
+    hipLaunchKernelGGL(gemm_fp8_skinny_split, grid, dim3(256), 0, s, a, splits,
+                       reinterpret_cast<float*>(ws.ptr + kWorkspaceCounterBytes),
+                       reinterpret_cast<int*>(ws.ptr));
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)cdiv(a.N, FN_));
   if (a.M <= 16)
     hipLaunchKernelGGL(gemm_fp8_skinny<16>, grid, dim3(256), 0, s, a);
@@ -309,10 +592,20 @@ hipError_t launch(Op, const GemmArgs& a, const Scratch&, hipStream_t s) {
   return hipGetLastError();
 }
 
+const char* const kSplitNames[] = {
+    "skinny_fp8_64x32",          "skinny_fp8_64x32",          "skinny_fp8_64x128_splitk2",
+    "skinny_fp8_64x128_splitk3", "skinny_fp8_64x128_splitk4", "skinny_fp8_64x128_splitk5",
+    "skinny_fp8_64x128_splitk6", "skinny_fp8_64x128_splitk7", "skinny_fp8_64x128_splitk8"};
+const char* name_of(const GemmArgs& a, const Scratch& ws) {
+  if (!scratch_fits(ws, scratch_bytes(a))) return "skinny_fp8_64x32";
+  const int splits = choose_splits(a);
+  return splits <= 8 ? kSplitNames[splits] : "skinny_fp8_64x128_splitk";
+}
+
 }  // namespace
 
 const Variant* variant_skinny_fp8() {
-  static const Variant v = {"skinny_fp8_64x32", accepts, launch, nullptr, nullptr};
+  static const Variant v = {"skinny_fp8_64x32", accepts, launch, name_of, scratch_bytes};
   return &v;
 }
 

@@ -150,9 +150,30 @@ tg_status tg_gemm_bf16_ws(int64_t M, int64_t N, int64_t K,
                           void* C, int64_t scm, int64_t scn,
                           void* workspace, size_t workspace_bytes, tg_stream_t stream);
 
+/* tg_gemm_fp8_blockscaled with a caller-owned workspace (same contract as
+ * the 16-bit *_ws calls above).  Its split plan is for M <= 64 (a decode
+ * step over fp8 weights): 64 x 128 strips of C, the K blocks split so that
+ * there is about one workgroup per CU, each split's block sums folded in
+ * with SA * SB as in tg_gemm_fp8_blockscaled and the fp32 partial tiles
+ * added in split order.  Without workspace (or too little) it runs exactly
+ * as tg_gemm_fp8_blockscaled.  Results: within the same bound, bit for bit
+ * equal when every fp32 partial sum is exact.  Errors: those of
+ * tg_gemm_fp8_blockscaled, plus TG_ERR_INVALID_VALUE for workspace_bytes > 0
+ * with a NULL or not 256-byte aligned workspace.  Nothing is allocated;
+ * asynchronous on `stream`. */
+tg_status tg_gemm_fp8_blockscaled_ws(int64_t M, int64_t N, int64_t K,
+                                     const void* A, int64_t sam, int64_t sak,
+                                     const float* SA, int64_t ssam, int64_t ssak,
+                                     const void* B, int64_t sbk, int64_t sbn,
+                                     const float* SB, int64_t ssbn, int64_t ssbk,
+                                     void* C, int64_t scm, int64_t scn,
+                                     void* workspace, size_t workspace_bytes,
+                                     tg_stream_t stream);
+
 /* Workspace bytes the split plan of a call with these arguments uses (0: the
  * call has no split plan, so a workspace changes nothing).  op: 0 = f16,
- * 1 = bf16, 2 = fp8 block-scaled (always 0).  Host only: no HIP call.
+ * 1 = bf16, 2 = fp8 block-scaled (scale pointers and strides do not change
+ * the plan and are not taken).  Host only: no HIP call.
  * Errors: TG_ERR_INVALID_VALUE for a NULL `bytes`, an unknown op, or
  * arguments the product would reject (the same validation). */
 tg_status tg_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K,
@@ -358,8 +379,8 @@ const char* tg_gemm_swiglu_quant_fp8_plan(int op, int64_t M, int64_t N, int64_t 
  * tg_gemm_f16, 1 = tg_gemm_bf16, 2 = tg_gemm_fp8_blockscaled (the scale
  * arguments do not affect the choice).  tg_gemm_plan names the plan of the
  * allocation-free entry points; tg_gemm_plan_ws the plan of
- * tg_gemm_f16_ws / tg_gemm_bf16_ws with a workspace of workspace_bytes.
- * Host only.  For tests and benchmarks. */
+ * tg_gemm_f16_ws / tg_gemm_bf16_ws / tg_gemm_fp8_blockscaled_ws with a
+ * workspace of workspace_bytes.  Host only.  For tests and benchmarks. */
 const char* tg_gemm_plan(int op, int64_t M, int64_t N, int64_t K,
                          const void* A, int64_t sam, int64_t sak,
                          const void* B, int64_t sbk, int64_t sbn,

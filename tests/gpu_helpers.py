@@ -102,17 +102,28 @@ def run16(fmt: str, M, N, K, A, sam, sak, B, sbk, sbn, scm=None, a_off=0, b_off=
     return c_view(buf, off, M, N, scm), plan
 
 
-def run_fp8(M, N, K, A, sam, sak, SA, ssam, ssak, B, sbk, sbn, SB, ssbn, ssbk, scm=None):
+def run_fp8(M, N, K, A, sam, sak, SA, ssam, ssak, B, sbk, sbn, SB, ssbn, ssbk, scm=None,
+            ws=None):
+    """tg_gemm_fp8_blockscaled on device tensors; returns (C codes, plan).
+    ws=True / <Workspace>: tg_gemm_fp8_blockscaled_ws, as run16 does."""
     buf, off, scm = alloc_c(M, N, scm)
     args = (M, N, K, A.data_ptr(), sam, sak, B.data_ptr(), sbk, sbn, buf.data_ptr() + off * 2,
             scm, 1)
-    plan = tg.tg_gemm_plan(tg.OP_FP8, *args)
-    tg.tg_gemm_fp8_blockscaled(M, N, K, A.data_ptr(), sam, sak, SA.data_ptr(), ssam, ssak,
-                               B.data_ptr(), sbk, sbn, SB.data_ptr(), ssbn, ssbk,
-                               buf.data_ptr() + off * 2, scm, 1,
-                               torch.cuda.current_stream().cuda_stream)
+    full = (M, N, K, A.data_ptr(), sam, sak, SA.data_ptr(), ssam, ssak, B.data_ptr(), sbk, sbn,
+            SB.data_ptr(), ssbn, ssbk, buf.data_ptr() + off * 2, scm, 1)
+    st = torch.cuda.current_stream().cuda_stream
+    if ws is None or ws is False:
+        plan = tg.tg_gemm_plan(tg.OP_FP8, *args)
+        tg.tg_gemm_fp8_blockscaled(*full, st)
+    else:
+        if ws is True:
+            ws = Workspace(tg.tg_gemm_workspace_size(tg.OP_FP8, *args))
+        plan = tg.tg_gemm_plan_ws(tg.OP_FP8, *args, ws.nbytes)
+        tg.tg_gemm_fp8_blockscaled_ws(*full, ws.ptr, ws.nbytes, st)
     torch.cuda.synchronize()
     check_guards(buf, off, M, N, scm)
+    if ws is not None and ws is not False:
+        assert ws.counters_zero(), "workspace counters left nonzero"
     return c_view(buf, off, M, N, scm), plan
 
 

@@ -419,6 +419,46 @@ def test_fp8_tile_plans(lib, case):
     assert tg.tg_gemm_plan(tg.OP_FP8, M, N, K, PA, K, 1, PB, 1, K, PC, N, 1) == want
 
 
+# The fp8 decode product with a workspace: 64 x 128 strips, the K blocks
+# split so that strips x splits stays within 256 workgroups, with at least 4
+# blocks per split -- for more than 32 rows, where the strip grid is not one
+# nearly full round (192 .. 256 workgroups of 32 columns) or each split gets
+# at least 24 blocks.  Otherwise (and for M > 64, or K not a multiple of 16)
+# the plan without workspace.
+FP8_WS_PLANS = [
+    ((64, 7168, 16384), "skinny_fp8_64x128_splitk4"),    # 224 strip workgroups, 32 blocks per split
+    ((33, 7168, 18432), "skinny_fp8_64x128_splitk4"),    # 36 blocks per split
+    ((64, 16384, 7168), "skinny_fp8_64x128_splitk2"),    # 512 strip workgroups: 2 rounds
+    ((40, 1000, 4096), "skinny_fp8_64x128_splitk8"),     # 32 strip workgroups; 8 strips, 32 blocks
+    ((64, 2048, 2048), "skinny_fp8_64x128_splitk4"),     # 16 strips, 16 blocks
+    ((48, 300, 1024), "skinny_fp8_64x128_splitk2"),      # 3 strips, 8 blocks
+    ((64, 7168, 7168), "skinny_fp8_64x32"),              # one full round, 14 blocks per split
+    ((32, 16384, 7168), "skinny_fp8_64x32"),             # 32 rows
+    ((1, 7168, 16384), "skinny_fp8_64x32"),
+    ((64, 32768, 7168), "skinny_fp8_64x32"),             # 256 strips: no split
+    ((64, 1000, 384), "skinny_fp8_64x32"),               # 3 blocks: too short to split
+    ((65, 7168, 7168), "tile_fp8_256x128"),
+    ((64, 100, 24), "generic_fp8_64x64"),
+]
+
+
+@pytest.mark.parametrize("case", FP8_WS_PLANS, ids=[f"{m}x{n}x{k}" for (m, n, k), _ in FP8_WS_PLANS])
+def test_fp8_workspace_plans(lib, case):
+    (M, N, K), want = case
+    args = (tg.OP_FP8, M, N, K, PA, K, 1, PB, 1, K, PC, N, 1)
+    need = _ws_bytes(tg.OP_FP8, M, N, K, 1, K)
+    plain = tg.tg_gemm_plan(*args)
+    assert (need > 0) == (want != plain)
+    assert tg.tg_gemm_plan_ws(*args, need) == want
+    assert tg.tg_gemm_plan_ws(*args, 1 << 40) == want
+    if need:
+        assert plain == "skinny_fp8_64x32"
+        assert tg.tg_gemm_plan_ws(*args, need - 1) == plain
+        assert tg.tg_gemm_plan_ws(*args, 0) == plain
+        strips, splits = -(-N // 128), int(want.rsplit("splitk", 1)[1])
+        assert need == 16384 + strips * splits * 64 * 128 * 4
+
+
 def test_workspace_sizes(lib):
     """The split plans' scratch: a 16 KiB counter area, then 4 bytes per
     element of each split's partial tile."""
@@ -427,7 +467,9 @@ def test_workspace_sizes(lib):
     assert _ws_bytes(tg.OP_F16, 1024, 1024, 4096, 1, 4096) == 16384 + 64 * 4 * 128 * 128 * 4
     assert _ws_bytes(tg.OP_BF16, 4352, 4096, 4096, 1, 4096) == 16384 + 67 * 3 * 256 * 224 * 4
     assert _ws_bytes(tg.OP_BF16, 4096, 7168, 16384, 1, 16384) == 0
+    assert _ws_bytes(tg.OP_FP8, 64, 7168, 16384, 1, 16384) == 16384 + 56 * 4 * 64 * 128 * 4
     assert _ws_bytes(tg.OP_FP8, 64, 7168, 7168, 1, 7168) == 0
+    assert _ws_bytes(tg.OP_FP8, 65, 7168, 7168, 1, 7168) == 0
     assert _ws_bytes(tg.OP_BF16, 0, 8, 8, 1, 8) == 0
     with pytest.raises(tg.TgError):
         _ws_bytes(tg.OP_BF16, -1, 8, 8, 1, 8)
@@ -446,6 +488,18 @@ def test_workspace_invalid(lib, name):
     args = (64, 7168, 7168, PA, 7168, 1, PB, 1, 7168, PC, 7168, 1)
     assert fn(*args, 0, 1 << 20, None) == tg.TG_ERR_INVALID_VALUE          # NULL workspace
     assert fn(*args, PS + 16, 1 << 20, None) == tg.TG_ERR_INVALID_VALUE    # not 256-byte aligned
+    bad = (-1,) + args[1:]
+    assert fn(*bad, PS, 1 << 20, None) == tg.TG_ERR_INVALID_VALUE
+    assert fn(0, *args[1:], PS, 1 << 20, None) == tg.TG_SUCCESS             # no-op
+
+
+def test_fp8_workspace_invalid(lib):
+    fn = lib.tg_gemm_fp8_blockscaled_ws
+    args = (64, 7168, 7168, PA, 7168, 1, PS, 56, 1, PB, 1, 7168, PS, 56, 1, PC, 7168, 1)
+    assert fn(*args, 0, 1 << 20, None) == tg.TG_ERR_INVALID_VALUE          # NULL workspace
+    assert fn(*args, PS + 16, 1 << 20, None) == tg.TG_ERR_INVALID_VALUE    # not 256-byte aligned
+    bad = args[:6] + (0,) + args[7:]                                         # NULL SA
+    assert fn(*bad, PS, 1 << 20, None) == tg.TG_ERR_INVALID_VALUE
     bad = (-1,) + args[1:]
     assert fn(*bad, PS, 1 << 20, None) == tg.TG_ERR_INVALID_VALUE
     assert fn(0, *args[1:], PS, 1 << 20, None) == tg.TG_SUCCESS             # no-op

@@ -214,11 +214,11 @@ def _fp8_inputs(M, N, K, seed, layout="nk", int_r=None, pow2_scales=False):
     return d
 
 
-def _check_fp8(M, N, K, d, rows=None, exact=False, what=""):
+def _check_fp8(M, N, K, d, rows=None, exact=False, what="", ws=None):
     nkb = d["SA"].shape[1]
     A, B, SA, SB = H.dev(d["A"]), H.dev(d["B"]), H.dev(d["SA"]), H.dev(d["SB"])
-    H.log(f"fp8 {what} M={M} N={N} K={K} layout={d['layout']}")
-    c, plan = H.run_fp8(M, N, K, A, K, 1, SA, nkb, 1, B, d["sbk"], d["sbn"], SB, nkb, 1)
+    H.log(f"fp8 {what} M={M} N={N} K={K} layout={d['layout']} ws={ws is not None}")
+    c, plan = H.run_fp8(M, N, K, A, K, 1, SA, nkb, 1, B, d["sbk"], d["sbn"], SB, nkb, 1, ws=ws)
     C_ref, S = oracle.gemm_fp8_blockscaled(M, N, K, d["A"], K, 1, d["SA"], nkb, 1, d["B"],
                                            d["sbk"], d["sbn"], d["SB"], nkb, 1, rows=rows)
     cc = c if rows is None else c[rows]
@@ -771,6 +771,62 @@ def test_fp8_skinny(case):
     plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 2000 + M + K, int_r=4, pow2_scales=True),
                       exact=True, what="skinny int pow2 scales")
     assert plan == "skinny_fp8_64x32", plan
+
+
+# The split plan of the fp8 decode product (a caller's workspace): 64 x 128
+# strips over ranges of the K blocks, partial tiles added in split order; it
+# runs for 33 .. 64 rows where the strip grid is not one nearly full round or
+# the splits are long.  Cases: a 64 x 7168 x 16384 down projection (4
+# splits); 64 x 16384 x 7168 (2 splits); a ragged last strip and a ragged
+# last K block in the last split (33 x 300 x 1040: 9 blocks in 2 splits); one
+# partial strip with 8 uneven splits (40 x 40 x 4112: 33 blocks); 16 splits,
+# summed four at a time (48 x 100 x 8192); 14 splits (64 x 2048 x 7168); a
+# 2-column strip in the second B scale block; 63 rows of a 16-column strip.
+FP8_SPLIT_CASES = [(64, 7168, 16384), (64, 16384, 7168), (33, 300, 1040), (40, 40, 4112),
+                   (48, 100, 8192), (64, 2048, 7168), (64, 130, 2048), (63, 16, 1024)]
+
+
+@pytest.mark.parametrize("case", FP8_SPLIT_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in FP8_SPLIT_CASES])
+def test_fp8_skinny_split(case):
+    M, N, K = case
+    for d, exact, what in (
+            (_fp8_inputs(M, N, K, 2200 + M + K), False, "split bound"),
+            (_fp8_inputs(M, N, K, 2300 + M + K, int_r=16), True, "split int unit scales"),
+            (_fp8_inputs(M, N, K, 2400 + M + K, int_r=4, pow2_scales=True), True,
+             "split int pow2 scales")):
+        plan = _check_fp8(M, N, K, d, exact=exact, what=what, ws=True)
+        assert plan.startswith("skinny_fp8_64x128_splitk"), plan
+
+
+def test_fp8_split_workspace_reuse():
+    """One workspace through three calls in a row -- a 64 x 7168 x 16384 down
+    projection, a smaller call (fewer strips and splits), the first again: each
+    leaves the counters zero and is bit-exact on integer inputs."""
+    M0, N0, K0 = big = (64, 7168, 16384)
+    ws = H.Workspace(H.tg.tg_gemm_workspace_size(H.tg.OP_FP8, M0, N0, K0, 0x100, K0, 1, 0x200, 1,
+                                                 K0, 0x300, N0, 1))
+    assert ws.nbytes == 16384 + 56 * 4 * 64 * 128 * 4
+    for i, (M, N, K) in enumerate((big, (33, 300, 1040), big)):
+        plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 2500 + i, int_r=16), exact=True,
+                          what=f"split reuse {i}", ws=ws)
+        assert plan.startswith("skinny_fp8_64x128_splitk"), plan
+
+
+def test_fp8_split_padded_c():
+    """The split plan storing into C rows padded by 40 elements, behind guard
+    bands, with B stored K x N-contiguous rows padded (sbn = K + 32)."""
+    M, N, K = 40, 300, 2048
+    d = _fp8_inputs(M, N, K, 2600, int_r=16)
+    assert (d["sbk"], d["sbn"]) == (1, K)
+    Bp = np.zeros((N, K + 32), np.uint8)
+    Bp[:, :K] = np.asarray(d["B"]).view(np.uint8).reshape(N, K)
+    nkb = d["SA"].shape[1]
+    c, plan = H.run_fp8(M, N, K, H.dev(d["A"]), K, 1, H.dev(d["SA"]), nkb, 1, H.dev(Bp),
+                        1, K + 32, H.dev(d["SB"]), nkb, 1, scm=N + 40, ws=True)
+    assert plan == "skinny_fp8_64x128_splitk4", plan
+    C_ref, _ = oracle.gemm_fp8_blockscaled(M, N, K, d["A"], K, 1, d["SA"], nkb, 1, Bp, 1, K + 32,
+                                           d["SB"], nkb, 1)
+    H.assert_bit_exact("bf16", c, C_ref, f"fp8 split, padded C [{plan}]")
 
 
 def test_fp8_skinny_padded_c():
