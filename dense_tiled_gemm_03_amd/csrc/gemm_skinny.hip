@@ -211,13 +211,15 @@ __global__ __launch_bounds__(256) void gemm16_skinny(GemmArgs a, int splits, flo
     // and read with device-coherent (sc1) accesses, and every wave waits for
     // its writes to complete before the barrier that precedes the counter
     // increment, so the last workgroup reads every tile whole.
+    // Only the rows of C are stored and read (row (256 e + t) >> 5 < M).
     const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
         part + (int64_t)strip * splits * SM * SN, (short)0, splits * SM * SN * 4, 0x00020000);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x[e]), rp,
-                                             (split * SM * SN + 4 * (256 * e + t)) * 4, 0,
-                                             kCoherent);
+      if (8 * e + (t >> 5) < a.M)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x[e]), rp,
+                                               (split * SM * SN + 4 * (256 * e + t)) * 4, 0,
+                                               kCoherent);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t == 0) last = atomicAdd(counters + strip, 1) == splits - 1;
@@ -232,8 +234,10 @@ __global__ __launch_bounds__(256) void gemm16_skinny(GemmArgs a, int splits, flo
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          y[j][e] = __builtin_amdgcn_raw_buffer_load_b128(
-              rp, ((sp0 + j) * SM * SN + 4 * (256 * e + t)) * 4, 0, kCoherent);
+          y[j][e] = 8 * e + (t >> 5) < a.M && sp0 + j < splits
+                        ? __builtin_amdgcn_raw_buffer_load_b128(
+                              rp, ((sp0 + j) * SM * SN + 4 * (256 * e + t)) * 4, 0, kCoherent)
+                        : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (sp0 + j < splits)
