@@ -25,7 +25,9 @@ EXPORTS = ("tg_status_string", "tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8_block
            "tg_gemm_quant_fp8_plan", "tg_gemm_f16_ws", "tg_gemm_bf16_ws", "tg_gemm_workspace_size",
            "tg_gemm_plan_ws", "tg_gemm_bf16_static_scratch", "tg_gemm_f16_swiglu_quant_fp8",
            "tg_gemm_bf16_swiglu_quant_fp8", "tg_gemm_swiglu_quant_fp8_plan",
-           "tg_gemm_fp8_blockscaled_ws")
+           "tg_gemm_fp8_blockscaled_ws", "tg_gemm_f16_swiglu_quant_fp8_ws",
+           "tg_gemm_bf16_swiglu_quant_fp8_ws", "tg_gemm_swiglu_quant_fp8_workspace_size",
+           "tg_gemm_swiglu_quant_fp8_plan_ws")
 
 
 class TgError(RuntimeError):
@@ -99,6 +101,14 @@ def load():
         getattr(lib, name).restype = c_int
     lib.tg_gemm_swiglu_quant_fp8_plan.argtypes = [c_int] + sigs
     lib.tg_gemm_swiglu_quant_fp8_plan.restype = ctypes.c_char_p
+    for name in ("tg_gemm_f16_swiglu_quant_fp8_ws", "tg_gemm_bf16_swiglu_quant_fp8_ws"):
+        getattr(lib, name).argtypes = sigs + [vp, ctypes.c_size_t, vp]
+        getattr(lib, name).restype = c_int
+    lib.tg_gemm_swiglu_quant_fp8_workspace_size.argtypes = (
+        [c_int] + sigs + [ctypes.POINTER(ctypes.c_size_t)])
+    lib.tg_gemm_swiglu_quant_fp8_workspace_size.restype = c_int
+    lib.tg_gemm_swiglu_quant_fp8_plan_ws.argtypes = [c_int] + sigs + [ctypes.c_size_t]
+    lib.tg_gemm_swiglu_quant_fp8_plan_ws.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -212,6 +222,37 @@ def tg_gemm_swiglu_quant_fp8_plan(op, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q,
                                   ssj):
     r = load().tg_gemm_swiglu_quant_fp8_plan(op, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm,
                                              S, ssm, ssj)
+    return None if r is None else r.decode()
+
+
+def tg_gemm_f16_swiglu_quant_fp8_ws(M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm, S, ssm, ssj,
+                                    workspace, workspace_bytes, stream=0):
+    return _check(load().tg_gemm_f16_swiglu_quant_fp8_ws(M, N, K, A, sam, sak, Bg, Bu, sbk, sbn,
+                                                         Q, sqm, S, ssm, ssj, workspace,
+                                                         workspace_bytes, stream))
+
+
+def tg_gemm_bf16_swiglu_quant_fp8_ws(M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm, S, ssm, ssj,
+                                     workspace, workspace_bytes, stream=0):
+    return _check(load().tg_gemm_bf16_swiglu_quant_fp8_ws(M, N, K, A, sam, sak, Bg, Bu, sbk, sbn,
+                                                          Q, sqm, S, ssm, ssj, workspace,
+                                                          workspace_bytes, stream))
+
+
+def tg_gemm_swiglu_quant_fp8_workspace_size(op, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm, S,
+                                            ssm, ssj):
+    """Workspace bytes of the fused SwiGLU call's split plan (0: none)."""
+    out = ctypes.c_size_t(0)
+    _check(load().tg_gemm_swiglu_quant_fp8_workspace_size(op, M, N, K, A, sam, sak, Bg, Bu, sbk,
+                                                          sbn, Q, sqm, S, ssm, ssj,
+                                                          ctypes.byref(out)))
+    return out.value
+
+
+def tg_gemm_swiglu_quant_fp8_plan_ws(op, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm, S, ssm,
+                                     ssj, workspace_bytes):
+    r = load().tg_gemm_swiglu_quant_fp8_plan_ws(op, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q,
+                                                sqm, S, ssm, ssj, workspace_bytes)
     return None if r is None else r.decode()
 
 

@@ -114,7 +114,8 @@ __global__ __launch_bounds__(256) void gemm16_generic_swiglu_q8(GemmArgs a, cons
 // bound by streaming the two weight matrices from HBM, which the 256-row tile
 // does with most of its rows empty.  One workgroup of 4 waves owns one
 // 128-column output slice (so the slice's row maxima stay in the workgroup)
-// over the whole of K:
+// over the whole of K -- or, with a caller's workspace, over one of `splits`
+// ranges of the K slices, so that there are about as many workgroups as CUs:
 //  - 64-wide K slices go HBM -> LDS by LDS-direct loads into a 4-stage ring;
 //    a stage holds the slice of A (64 rows), then the slice's 128 gate rows
 //    and its 128 up rows (40 KiB; the weights non-temporal, as they are read
@@ -124,6 +125,11 @@ __global__ __launch_bounds__(256) void gemm16_generic_swiglu_q8(GemmArgs a, cons
 //    32x32x16 MFMAs (rows 0-31, 32-63) of the gate and two of the up
 //    weights, so g and u of an element sit in the same lane and h = silu(g) u
 //    is formed in registers;
+//  - split: each workgroup writes its fp32 g and u partial tiles to the
+//    workspace in the accumulators' register layout (rows below M only);
+//    the last of a slice's workgroups to finish (a device-scope counter, the
+//    protocol of the skinny product) adds them in split order, so g and u
+//    are whole before the activation, and clears the counter;
 //  - the epilogue takes each row's maximum |h| over the wave's 32 columns by
 //    shuffles and over the four waves through LDS, then quantises as the
 //    fp8-output epilogue does.
@@ -142,10 +148,16 @@ constexpr int D_NLD = D_ALD + 2 * D_BLD;       // 10
 static_assert(D_ST * D_STAGE <= 160 * 1024, "the ring must fit the LDS");
 static_assert(D_ST * D_NLD <= 63, "loads in flight must fit the vmcnt counter");
 static_assert(4 * DM * 4 <= D_STAGE, "the row maxima fit the first stage");
+constexpr int D_PART = 256 * 64;               // floats of a split's g and u partial tiles
+constexpr int D_LAST = 4096;                   // LDS byte offset of the last-split flag
+static_assert(D_LAST >= 4 * DM * 4 && D_LAST + 4 <= D_STAGE, "the flag clears the row maxima");
+constexpr int kCoherent = 0x10;                // sc1: device-coherent buffer access
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __global__ __launch_bounds__(256) void gemm16_swiglu_skinny(GemmArgs a, const void* up,
-                                                            QuantOut qo) {
+                                                            QuantOut qo, int splits, float* part,
+                                                            int* counters) {
   typedef typename Elem<T>::x8 T8;
   typedef tile::Mfma32 MMA;
   __shared__ __attribute__((aligned(1024))) char lds[D_ST * D_STAGE];
@@ -154,7 +166,8 @@ __global__ __launch_bounds__(256) void gemm16_swiglu_skinny(GemmArgs a, const vo
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t strip = blockIdx.x, n0 = strip * DN;
+  const int64_t strip = blockIdx.x / splits, n0 = strip * DN;
+  const int split = blockIdx.x % splits;
   const int K = (int)a.K;
   const uint32_t lda = (uint32_t)a.sam, ldb = (uint32_t)a.sbn;
   const int rows_a = (int)a.M;  // <= 64
@@ -163,7 +176,11 @@ __global__ __launch_bounds__(256) void gemm16_swiglu_skinny(GemmArgs a, const vo
   const uint32_t b_range = (uint32_t)(((rows_b - 1) * ldb + K) * 2);
   const i32x4 rg = make_desc(static_cast<const T*>(a.B) + n0 * a.sbn, b_range);
   const i32x4 ru = make_desc(static_cast<const T*>(up) + n0 * a.sbn, b_range);
+  // This workgroup's slices [s_begin, s_end) of the nk 64-wide K slices.
   const int nk = (K + DK - 1) / DK;
+  const int s_begin = (int)((int64_t)split * nk / splits);
+  const int s_end = (int)((int64_t)(split + 1) * nk / splits);
+  const int count = s_end - s_begin;
 
   // Wave w's j-th load of a stage fills 8-row group G of the stage: A rows
   // 16w + 8j (G = 2w + j), gate rows 32w + 8j' (G = 8 + 4w + j'), up rows
@@ -172,7 +189,7 @@ __global__ __launch_bounds__(256) void gemm16_swiglu_skinny(GemmArgs a, const vo
   const uint32_t lrow = lane >> 3;
   const uint32_t lc0 = (lane & 7) ^ (lane >> 4), lc1 = (lane & 7) ^ (4 + (lane >> 4));
   auto load_slice = [&](int slot, int slice) {
-    if (slice >= nk) return;  // nothing past K (an empty load still costs an issue)
+    if (slice >= s_end) return;  // nothing past the range (an empty load still costs an issue)
     const int k0 = slice * DK;
     const uint32_t stage = lds32 + slot * D_STAGE;
 #pragma unroll
@@ -221,12 +238,12 @@ __global__ __launch_bounds__(256) void gemm16_swiglu_skinny(GemmArgs a, const vo
   // follow, every load) and every wave's reads of slice i are done; refill
   // slice i's slot with slice i + D_ST; read slice i + 1; multiply slice i.
   auto step = [&](int i, int cur) {
-    if (i + D_ST - 1 < nk)
+    if (i + D_ST - 1 < count)
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((D_ST - 2) * D_NLD) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     asm volatile("s_barrier" ::: "memory");
-    load_slice(i % D_ST, i + D_ST);
+    load_slice(i % D_ST, s_begin + i + D_ST);
     read_slice(cur ^ 1, (i + 1) % D_ST);
     __builtin_amdgcn_sched_barrier(0);  // reads ahead of the MFMAs
 #pragma unroll
@@ -239,23 +256,78 @@ __global__ __launch_bounds__(256) void gemm16_swiglu_skinny(GemmArgs a, const vo
     __builtin_amdgcn_sched_barrier(0);
   };
 #pragma unroll
-  for (int p = 0; p < D_ST; ++p) load_slice(p, p);
-  if (D_ST <= nk)
+  for (int p = 0; p < D_ST; ++p) load_slice(p, s_begin + p);
+  if (D_ST <= count)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((D_ST - 1) * D_NLD) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   asm volatile("s_barrier" ::: "memory");
   read_slice(0, 0);
   int i = 0;
-  for (; i + 1 < nk; i += 2) {
+  for (; i + 1 < count; i += 2) {
     step(i, 0);
     step(i + 1, 1);
   }
-  if (i < nk) step(i, 0);
+  if (i < count) step(i, 0);
   // every load has landed; once every wave is past its last reads the LDS
-  // holds the row maxima
+  // holds the flag and the row maxima
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+
+  if (splits > 1) {
+    // Thread t's float4 e (0 .. 15) of a split's partial tiles: acc_g[e / 4]
+    // (e < 8) or acc_u[e / 4 - 2], values 4 (e % 4) .. + 3, i.e. rows 32 b +
+    // 8 (e % 4) + 4 (l >> 5) .. + 3 (b = (e / 4) % 2) of column 32 w + (l & 31);
+    // float4s of rows past M are neither stored nor read.
+    const int t = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        part + strip * splits * D_PART, (short)0, splits * D_PART * 4, 0x00020000);
+    auto row0 = [&](int e) { return 32 * ((e >> 2) & 1) + 8 * (e & 3) + 4 * (lane >> 5); };
+    auto acc_of = [&](int e) -> f32x16& { return e < 8 ? acc_g[e >> 2] : acc_u[(e >> 2) - 2]; };
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (row0(e) < a.M) {
+        const f32x16& v = acc_of(e);
+        const int q = 4 * (e & 3);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, f32x4{v[q], v[q + 1], v[q + 2], v[q + 3]}), rp,
+            ((split * 16 + e) * 256 + t) * 16, 0, kCoherent);
+      }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int* last = reinterpret_cast<int*>(lds + D_LAST);
+    __syncthreads();
+    if (t == 0) *last = atomicAdd(counters + strip, 1) == splits - 1;
+    __syncthreads();
+    if (!*last) return;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc_g[b][v] = acc_u[b][v] = 0.0f;
+    // two splits' tiles in flight at a time, added in split order
+    for (int sp0 = 0; sp0 < splits; sp0 += 2) {
+      u32x4 y[2][16];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          y[j][e] = row0(e) < a.M && sp0 + j < splits
+                        ? __builtin_amdgcn_raw_buffer_load_b128(
+                              rp, (((sp0 + j) * 16 + e) * 256 + t) * 16, 0, kCoherent)
+                        : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (sp0 + j < splits)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            f32x16& v = acc_of(e);
+            const f32x4 x = __builtin_bit_cast(f32x4, y[j][e]);
+            const int q = 4 * (e & 3);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[q + r] += x[r];
+          }
+    }
+    if (t == 0) __hip_atomic_store(counters + strip, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // h = silu(g) u; lane l holds column 32w + (l & 31), rows 32i + out_row(l, v)
   f32x16 h[2];
@@ -345,12 +417,43 @@ int64_t grid_of(const Call& c, Path p) {
   }
 }
 
+// Splits of the skinny kernel's K slices with a workspace: about one
+// workgroup per CU, at least 8 slices and at most 8 splits (the last
+// workgroup of a slice reads every split's 64 KiB of partial tiles); 1: no
+// split plan.
+constexpr int kCus = 256;
+int choose_splits(const Call& c) {
+  const int64_t slices = cdiv(c.a.N, DN), nk = cdiv(c.a.K, DK);
+  int64_t sp = kCus / slices;
+  if (sp > nk / 8) sp = nk / 8;
+  if (sp > 8) sp = 8;
+  return sp < 2 ? 1 : (int)sp;
+}
+
+// Workspace of the split plan: a counter per slice in the fixed counter
+// area, then every split's g and u partial tiles (0: no split plan).
+size_t scratch_bytes(const Call& c) {
+  if (path_of(c) != Path::Skinny) return 0;
+  const int64_t slices = cdiv(c.a.N, DN);
+  const int splits = choose_splits(c);
+  if (splits == 1 || slices > kWorkspaceCounters) return 0;
+  return kWorkspaceCounterBytes + (size_t)slices * splits * D_PART * 4;
+}
+
 template <typename T>
-hipError_t launch_t(const Call& c, Path p, hipStream_t s) {
+hipError_t launch_t(const Call& c, Path p, const Scratch& ws, hipStream_t s) {
   const GemmArgs& a = c.a;
   const unsigned grid = (unsigned)grid_of(c, p);
   if (p == Path::Skinny) {
-    hipLaunchKernelGGL(gemm16_swiglu_skinny<T>, dim3(grid), dim3(256), 0, s, a, c.up, c.qo);
+    if (scratch_fits(ws, scratch_bytes(c))) {
+      const int splits = choose_splits(c);
+      hipLaunchKernelGGL(gemm16_swiglu_skinny<T>, dim3(grid * splits), dim3(256), 0, s, a, c.up,
+                         c.qo, splits, reinterpret_cast<float*>(ws.ptr + kWorkspaceCounterBytes),
+                         reinterpret_cast<int*>(ws.ptr));
+    } else {
+      hipLaunchKernelGGL(gemm16_swiglu_skinny<T>, dim3(grid), dim3(256), 0, s, a, c.up, c.qo, 1,
+                         nullptr, nullptr);
+    }
   } else if (p == Path::Generic) {
     hipLaunchKernelGGL(gemm16_generic_swiglu_q8<T>, dim3(grid), dim3(256), 0, s, a, c.up, c.qo,
                        cdiv(a.N, WTN));
@@ -363,15 +466,46 @@ hipError_t launch_t(const Call& c, Path p, hipStream_t s) {
   return hipGetLastError();
 }
 
-tg_status run(const Call& c, tg_stream_t stream) {
+tg_status run(const Call& c, const Scratch& ws, tg_stream_t stream) {
   tg_status st = validate(c);
   if (st != TG_SUCCESS) return st;
   if (c.a.M == 0 || c.a.N == 0) return TG_SUCCESS;
   const Path p = path_of(c);
   if (grid_of(c, p) >= (int64_t(1) << 31)) return TG_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = c.op == Op::BF16 ? launch_t<__bf16>(c, p, s) : launch_t<_Float16>(c, p, s);
+  const hipError_t e =
+      c.op == Op::BF16 ? launch_t<__bf16>(c, p, ws, s) : launch_t<_Float16>(c, p, ws, s);
   return e == hipSuccess ? TG_SUCCESS : TG_ERR_LAUNCH;
+}
+
+// The workspace entry points: a NULL or unaligned workspace of nonzero size
+// is rejected before anything runs.
+tg_status run_ws(const Call& c, void* workspace, size_t workspace_bytes, tg_stream_t stream) {
+  tg_status st = validate(c);
+  if (st != TG_SUCCESS) return st;
+  if (workspace_bytes > 0 &&
+      (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0))
+    return TG_ERR_INVALID_VALUE;
+  return run(c, Scratch{static_cast<char*>(workspace), workspace_bytes}, stream);
+}
+
+const char* const kSplitNames[] = {
+    "skinny_64x128_swiglu_q8",         "skinny_64x128_swiglu_q8",
+    "skinny_64x128_swiglu_q8_splitk2", "skinny_64x128_swiglu_q8_splitk3",
+    "skinny_64x128_swiglu_q8_splitk4", "skinny_64x128_swiglu_q8_splitk5",
+    "skinny_64x128_swiglu_q8_splitk6", "skinny_64x128_swiglu_q8_splitk7",
+    "skinny_64x128_swiglu_q8_splitk8"};
+
+const char* plan_name(const Call& c, size_t workspace_bytes) {
+  switch (path_of(c)) {
+    case Path::Skinny: {
+      const size_t need = scratch_bytes(c);
+      return need > 0 && workspace_bytes >= need ? kSplitNames[choose_splits(c)]
+                                                 : "skinny_64x128_swiglu_q8";
+    }
+    case Path::Tile: return "tile_nt_256x256_swiglu_q8";
+    default: return "generic16_32x128_swiglu_q8";
+  }
 }
 
 Call make(Op op, int64_t M, int64_t N, int64_t K, const void* A, int64_t sam, int64_t sak,
@@ -396,7 +530,7 @@ tg_status tg_gemm_f16_swiglu_quant_fp8(int64_t M, int64_t N, int64_t K, const vo
                                        int64_t ssm, int64_t ssj, tg_stream_t stream) {
   return tg::run(tg::make(tg::Op::F16, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm, S, ssm,
                           ssj),
-                 stream);
+                 tg::Scratch{nullptr, 0}, stream);
 }
 
 tg_status tg_gemm_bf16_swiglu_quant_fp8(int64_t M, int64_t N, int64_t K, const void* A,
@@ -405,7 +539,43 @@ tg_status tg_gemm_bf16_swiglu_quant_fp8(int64_t M, int64_t N, int64_t K, const v
                                         int64_t ssm, int64_t ssj, tg_stream_t stream) {
   return tg::run(tg::make(tg::Op::BF16, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm, S, ssm,
                           ssj),
-                 stream);
+                 tg::Scratch{nullptr, 0}, stream);
+}
+
+tg_status tg_gemm_f16_swiglu_quant_fp8_ws(int64_t M, int64_t N, int64_t K, const void* A,
+                                          int64_t sam, int64_t sak, const void* Bg,
+                                          const void* Bu, int64_t sbk, int64_t sbn, void* Q,
+                                          int64_t sqm, float* S, int64_t ssm, int64_t ssj,
+                                          void* workspace, size_t workspace_bytes,
+                                          tg_stream_t stream) {
+  return tg::run_ws(tg::make(tg::Op::F16, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm, S, ssm,
+                             ssj),
+                    workspace, workspace_bytes, stream);
+}
+
+tg_status tg_gemm_bf16_swiglu_quant_fp8_ws(int64_t M, int64_t N, int64_t K, const void* A,
+                                           int64_t sam, int64_t sak, const void* Bg,
+                                           const void* Bu, int64_t sbk, int64_t sbn, void* Q,
+                                           int64_t sqm, float* S, int64_t ssm, int64_t ssj,
+                                           void* workspace, size_t workspace_bytes,
+                                           tg_stream_t stream) {
+  return tg::run_ws(tg::make(tg::Op::BF16, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q, sqm, S,
+                             ssm, ssj),
+                    workspace, workspace_bytes, stream);
+}
+
+tg_status tg_gemm_swiglu_quant_fp8_workspace_size(int op, int64_t M, int64_t N, int64_t K,
+                                                  const void* A, int64_t sam, int64_t sak,
+                                                  const void* Bg, const void* Bu, int64_t sbk,
+                                                  int64_t sbn, void* Q, int64_t sqm, float* S,
+                                                  int64_t ssm, int64_t ssj, size_t* bytes) {
+  if (bytes == nullptr || (op != 0 && op != 1)) return TG_ERR_INVALID_VALUE;
+  const tg::Call c = tg::make(static_cast<tg::Op>(op), M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q,
+                              sqm, S, ssm, ssj);
+  const tg_status st = tg::validate(c);
+  if (st != TG_SUCCESS) return st;
+  *bytes = M == 0 || N == 0 ? 0 : tg::scratch_bytes(c);
+  return TG_SUCCESS;
 }
 
 const char* tg_gemm_swiglu_quant_fp8_plan(int op, int64_t M, int64_t N, int64_t K, const void* A,
@@ -417,11 +587,20 @@ const char* tg_gemm_swiglu_quant_fp8_plan(int op, int64_t M, int64_t N, int64_t 
                               sqm, S, ssm, ssj);
   if (tg::validate(c) != TG_SUCCESS) return nullptr;
   if (M == 0 || N == 0) return "none";
-  switch (tg::path_of(c)) {
-    case tg::Path::Skinny: return "skinny_64x128_swiglu_q8";
-    case tg::Path::Tile: return "tile_nt_256x256_swiglu_q8";
-    default: return "generic16_32x128_swiglu_q8";
-  }
+  return tg::plan_name(c, 0);
+}
+
+const char* tg_gemm_swiglu_quant_fp8_plan_ws(int op, int64_t M, int64_t N, int64_t K,
+                                             const void* A, int64_t sam, int64_t sak,
+                                             const void* Bg, const void* Bu, int64_t sbk,
+                                             int64_t sbn, void* Q, int64_t sqm, float* S,
+                                             int64_t ssm, int64_t ssj, size_t workspace_bytes) {
+  if (op != 0 && op != 1) return nullptr;
+  const tg::Call c = tg::make(static_cast<tg::Op>(op), M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, Q,
+                              sqm, S, ssm, ssj);
+  if (tg::validate(c) != TG_SUCCESS) return nullptr;
+  if (M == 0 || N == 0) return "none";
+  return tg::plan_name(c, workspace_bytes);
 }
 
 }  // extern "C"

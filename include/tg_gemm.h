@@ -362,17 +362,61 @@ tg_status tg_gemm_bf16_swiglu_quant_fp8(int64_t M, int64_t N, int64_t K,
                                         void* Q, int64_t sqm, float* S, int64_t ssm, int64_t ssj,
                                         tg_stream_t stream);
 
+/* The fused SwiGLU with a caller-owned workspace (contract of
+ * tg_gemm_f16_ws: 256-byte aligned, its first 16 KiB counters that must be
+ * zero before first use and are left zero, no sharing between calls that
+ * may overlap in time).  Its split plan is for M <= 64: the K slices of each
+ * 128-column output slice are split over several workgroups, so that there
+ * is about one workgroup per CU; the fp32 g and u partial sums are added in
+ * split order before the activation, so h, the scales and the codes are
+ * those of whole sums (bit for bit those of the call without a workspace
+ * when every fp32 partial sum is exact).  Without workspace (or too little)
+ * it runs exactly as tg_gemm_f16_swiglu_quant_fp8 / _bf16_.  Errors: those
+ * of the call without a workspace, plus TG_ERR_INVALID_VALUE for
+ * workspace_bytes > 0 with a NULL or not 256-byte aligned workspace.
+ * Nothing is allocated; asynchronous on `stream`. */
+tg_status tg_gemm_f16_swiglu_quant_fp8_ws(int64_t M, int64_t N, int64_t K,
+                                          const void* A, int64_t sam, int64_t sak,
+                                          const void* Bg, const void* Bu, int64_t sbk,
+                                          int64_t sbn, void* Q, int64_t sqm, float* S,
+                                          int64_t ssm, int64_t ssj, void* workspace,
+                                          size_t workspace_bytes, tg_stream_t stream);
+tg_status tg_gemm_bf16_swiglu_quant_fp8_ws(int64_t M, int64_t N, int64_t K,
+                                           const void* A, int64_t sam, int64_t sak,
+                                           const void* Bg, const void* Bu, int64_t sbk,
+                                           int64_t sbn, void* Q, int64_t sqm, float* S,
+                                           int64_t ssm, int64_t ssj, void* workspace,
+                                           size_t workspace_bytes, tg_stream_t stream);
+
+/* Workspace bytes the split plan of a fused SwiGLU call uses (0: no split
+ * plan, so a workspace changes nothing).  op: 0 = f16, 1 = bf16.  Host only.
+ * Errors: TG_ERR_INVALID_VALUE for a NULL `bytes`, an unknown op or
+ * arguments the call would reject. */
+tg_status tg_gemm_swiglu_quant_fp8_workspace_size(int op, int64_t M, int64_t N, int64_t K,
+                                                  const void* A, int64_t sam, int64_t sak,
+                                                  const void* Bg, const void* Bu, int64_t sbk,
+                                                  int64_t sbn, void* Q, int64_t sqm, float* S,
+                                                  int64_t ssm, int64_t ssj, size_t* bytes);
+
 /* How a fused SwiGLU call would run: "skinny_64x128_swiglu_q8" (M <= 64,
  * both weights stored N x K: one workgroup per 128-column slice over the
- * whole of K), "tile_nt_256x256_swiglu_q8" (larger M, both weights stored
- * N x K and accepted by the N x K tile kernel), "generic16_32x128_swiglu_q8"
- * (any other call), "none" (no-op) or NULL (invalid arguments).  op: 0 =
- * f16, 1 = bf16.  Host only. */
+ * whole of K), "skinny_64x128_swiglu_q8_splitkS" (the same with a workspace,
+ * K split S ways), "tile_nt_256x256_swiglu_q8" (larger M, both weights
+ * stored N x K and accepted by the N x K tile kernel),
+ * "generic16_32x128_swiglu_q8" (any other call), "none" (no-op) or NULL
+ * (invalid arguments).  op: 0 = f16, 1 = bf16.  tg_gemm_swiglu_quant_fp8_plan
+ * names the plan without a workspace, tg_gemm_swiglu_quant_fp8_plan_ws with
+ * one of workspace_bytes.  Host only. */
 const char* tg_gemm_swiglu_quant_fp8_plan(int op, int64_t M, int64_t N, int64_t K,
                                           const void* A, int64_t sam, int64_t sak,
                                           const void* Bg, const void* Bu, int64_t sbk,
                                           int64_t sbn, void* Q, int64_t sqm, float* S,
                                           int64_t ssm, int64_t ssj);
+const char* tg_gemm_swiglu_quant_fp8_plan_ws(int op, int64_t M, int64_t N, int64_t K,
+                                             const void* A, int64_t sam, int64_t sak,
+                                             const void* Bg, const void* Bu, int64_t sbk,
+                                             int64_t sbn, void* Q, int64_t sqm, float* S,
+                                             int64_t ssm, int64_t ssj, size_t workspace_bytes);
 
 /* Name of the kernel a call with these arguments would launch ("none" for a
  * no-op, NULL if the arguments are invalid); nothing is launched.  op: 0 =

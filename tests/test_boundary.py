@@ -183,6 +183,13 @@ def _callsw(lib, name, **kw):
     if name == "plan":
         r = lib.tg_gemm_swiglu_quant_fp8_plan(a.get("op", 1), *args)
         return None if r is None else r.decode()
+    if name == "plan_ws":
+        r = lib.tg_gemm_swiglu_quant_fp8_plan_ws(a.get("op", 1), *args, a.get("ws_bytes", 0))
+        return None if r is None else r.decode()
+    if name == "ws_size":
+        return tg.tg_gemm_swiglu_quant_fp8_workspace_size(a.get("op", 1), *args)
+    if name.endswith("_ws"):
+        return getattr(lib, name)(*args, a.get("ws", 0), a.get("ws_bytes", 0), None)
     return getattr(lib, name)(*args, None)
 
 
@@ -191,10 +198,72 @@ INVALIDSW = INVALIDQO[:9] + [dict(Bg=0), dict(Bu=0)] + INVALIDQO[10:]
 
 @pytest.mark.parametrize("kw", INVALIDSW, ids=[str(k) for k in INVALIDSW])
 @pytest.mark.parametrize("name", ["tg_gemm_f16_swiglu_quant_fp8", "tg_gemm_bf16_swiglu_quant_fp8",
-                                  "plan"])
+                                  "tg_gemm_f16_swiglu_quant_fp8_ws",
+                                  "tg_gemm_bf16_swiglu_quant_fp8_ws", "plan", "plan_ws", "ws_size"])
 def test_swiglu_invalid(lib, name, kw):
+    if name == "ws_size":
+        with pytest.raises(tg.TgError):
+            _callsw(lib, name, **kw)
+        return
     r = _callsw(lib, name, **kw)
-    assert (r is None) if name == "plan" else (r == tg.TG_ERR_INVALID_VALUE)
+    assert (r is None) if name.startswith("plan") else (r == tg.TG_ERR_INVALID_VALUE)
+
+
+# The fused SwiGLU's split plan (with a workspace): the K slices of each
+# 128-column output slice split so that slices x splits stays within 256
+# workgroups, with at least 8 slices per split and at most 8 splits;
+# 64 KiB of g and u partial tiles per slice and split after the 16 KiB of
+# counters.
+SWIGLU_WS_PLANS = [
+    ((64, 16384, 7168), 2),     # the decode shape: 128 slices
+    ((1, 7168, 7168), 4),       # 56 slices
+    ((64, 300, 2048), 4),       # 3 slices, 32 K slices
+    ((64, 256, 16384), 8),      # 2 slices, capped at 8 splits
+    ((33, 200, 1040), 2),       # 17 K slices
+    ((64, 32768, 7168), 1),     # 256 slices: no split
+    ((8, 300, 64), 1),          # one K slice
+]
+
+
+@pytest.mark.parametrize("case", SWIGLU_WS_PLANS, ids=[f"{m}x{n}x{k}" for (m, n, k), _ in SWIGLU_WS_PLANS])
+def test_swiglu_workspace_plans(lib, case):
+    (M, N, K), splits = case
+    kw = dict(M=M, N=N, K=K, sam=K, sbn=K, sqm=N, ssm=-(-N // 128))
+    need = _callsw(lib, "ws_size", **kw)
+    base = "skinny_64x128_swiglu_q8"
+    assert _callsw(lib, "plan", **kw) == base
+    if splits == 1:
+        assert need == 0
+        assert _callsw(lib, "plan_ws", ws_bytes=1 << 40, **kw) == base
+        return
+    assert need == 16384 + -(-N // 128) * splits * 64 * 1024
+    want = f"{base}_splitk{splits}"
+    assert _callsw(lib, "plan_ws", ws_bytes=need, **kw) == want
+    assert _callsw(lib, "plan_ws", ws_bytes=1 << 40, **kw) == want
+    assert _callsw(lib, "plan_ws", ws_bytes=need - 1, **kw) == base
+    assert _callsw(lib, "plan_ws", op=0, ws_bytes=need, **kw) == want
+
+
+def test_swiglu_workspace_other_paths_and_errors(lib):
+    # larger M (the tile kernel) and misaligned weights (the masked kernel): no split plan
+    kw = dict(M=4096, N=7168, K=7168, sam=7168, sbn=7168, sqm=7168, ssm=56)
+    assert _callsw(lib, "ws_size", **kw) == 0
+    assert _callsw(lib, "plan_ws", ws_bytes=1 << 40, **kw) == "tile_nt_256x256_swiglu_q8"
+    assert _callsw(lib, "ws_size", M=8, Bu=PB + 2) == 0
+    assert _callsw(lib, "plan_ws", M=8, Bu=PB + 2, ws_bytes=1 << 40) == \
+        "generic16_32x128_swiglu_q8"
+    assert _callsw(lib, "plan_ws", M=0, ws_bytes=1 << 20) == "none"
+    assert _callsw(lib, "ws_size", M=0) == 0
+    for name in ("tg_gemm_f16_swiglu_quant_fp8_ws", "tg_gemm_bf16_swiglu_quant_fp8_ws"):
+        assert _callsw(lib, name, ws=0, ws_bytes=1 << 20) == tg.TG_ERR_INVALID_VALUE
+        assert _callsw(lib, name, ws=PS + 16, ws_bytes=1 << 20) == tg.TG_ERR_INVALID_VALUE
+        assert _callsw(lib, name, M=0, A=0, Bg=0, Bu=0, Q=0, S=0, ws=PS, ws_bytes=1 << 20) == \
+            tg.TG_SUCCESS
+    assert lib.tg_gemm_swiglu_quant_fp8_workspace_size(1, 8, 300, 64, PA, 64, 1, PB, PB + 0x8000,
+                                                       1, 64, PC, 300, PS, 3, 1, None) == \
+        tg.TG_ERR_INVALID_VALUE
+    with pytest.raises(tg.TgError):
+        _callsw(lib, "ws_size", op=2)
 
 
 def test_swiglu_noop_and_plans(lib):

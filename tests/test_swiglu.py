@@ -14,7 +14,9 @@ an e4m3fn step allow.  The cases reach all three kernels, ragged edges, a grid o
 more than one round of workgroups, padded code and scale strides behind guard
 bytes, K = 0, weight rows closer than K apart, the 4096 x 16384 x 7168 shape on
 sampled rows, the 64 x 16384 x 7168 decode shape in full, and the output fed
-to tg_gemm_fp8_blockscaled as the down projection's A operand.
+to tg_gemm_fp8_blockscaled as the down projection's A operand; the workspace
+entry points' split plan on 2, 4 and 8 splits, workspace reuse and graph
+capture.
 """
 from __future__ import annotations
 
@@ -80,21 +82,40 @@ def _operands(fmt, M, N, K, layout, seed, exact):
     raise ValueError(layout)
 
 
-def _run(fmt, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, sqm=None, ssm=None, ssj=1):
+def _run(fmt, M, N, K, A, sam, sak, Bg, Bu, sbk, sbn, sqm=None, ssm=None, ssj=1, ws=None):
     """Run the fused SwiGLU on device operands; returns (codes M x N,
-    scales M x ceil(N/128), plan)."""
-    fn = tg.tg_gemm_bf16_swiglu_quant_fp8 if fmt == "bf16" else tg.tg_gemm_f16_swiglu_quant_fp8
+    scales M x ceil(N/128), plan).  ws=True: the workspace entry point with a
+    fresh zeroed workspace of the size its split plan asks for; ws=<Workspace>:
+    with that one (its counters must be zero again afterwards)."""
     op = 1 if fmt == "bf16" else 0
+    if ws is None:
+        fn = tg.tg_gemm_bf16_swiglu_quant_fp8 if fmt == "bf16" else tg.tg_gemm_f16_swiglu_quant_fp8
+    else:
+        fn = (tg.tg_gemm_bf16_swiglu_quant_fp8_ws if fmt == "bf16"
+              else tg.tg_gemm_f16_swiglu_quant_fp8_ws)
+    box = [ws]
 
     def launch(Q, sqm, S, ssm, ssj):
         args = (M, N, K, A.data_ptr(), sam, sak, Bg.data_ptr(), Bu.data_ptr(), sbk, sbn, Q, sqm,
                 S, ssm, ssj)
-        plan = tg.tg_gemm_swiglu_quant_fp8_plan(op, *args)
-        H.log(f"swiglu->fp8 {fmt} M={M} N={N} K={K} sqm={sqm} ssm={ssm} ssj={ssj} [{plan}]")
-        fn(*args, torch.cuda.current_stream().cuda_stream)
+        st = torch.cuda.current_stream().cuda_stream
+        if box[0] is None:
+            plan = tg.tg_gemm_swiglu_quant_fp8_plan(op, *args)
+            H.log(f"swiglu->fp8 {fmt} M={M} N={N} K={K} sqm={sqm} ssm={ssm} ssj={ssj} [{plan}]")
+            fn(*args, st)
+            return plan
+        if box[0] is True:
+            box[0] = H.Workspace(tg.tg_gemm_swiglu_quant_fp8_workspace_size(op, *args))
+        w = box[0]
+        plan = tg.tg_gemm_swiglu_quant_fp8_plan_ws(op, *args, w.nbytes)
+        H.log(f"swiglu->fp8 ws {fmt} M={M} N={N} K={K} bytes={w.nbytes} [{plan}]")
+        fn(*args, w.ptr, w.nbytes, st)
         return plan
 
-    return run_guarded(M, N, launch, sqm, ssm, ssj)
+    Q, S, plan = run_guarded(M, N, launch, sqm, ssm, ssj)
+    if ws is not None:
+        assert box[0].counters_zero(), "workspace counters left nonzero"
+    return Q, S, plan
 
 
 def _h_error(K, G, U, Sg, Su):
@@ -109,10 +130,10 @@ def _h_error(K, G, U, Sg, Su):
         + 2.0 ** -19 * (np.abs(G) + eg) * (np.abs(U) + eu)
 
 
-def _check(fmt, M, N, K, layout, seed, want=None):
-    for exact in (True, False):
+def _check(fmt, M, N, K, layout, seed, want=None, ws=None, modes=(True, False)):
+    for exact in modes:
         A, sam, sak, Bg, Bu, sbk, sbn = _operands(fmt, M, N, K, layout, seed, exact)
-        Q, S, plan = _run(fmt, M, N, K, H.dev(A), sam, sak, H.dev(Bg), H.dev(Bu), sbk, sbn)
+        Q, S, plan = _run(fmt, M, N, K, H.dev(A), sam, sak, H.dev(Bg), H.dev(Bu), sbk, sbn, ws=ws)
         if want:
             assert plan == want, plan
         Qo, So, Ho, G, U, Sg, Su = oracle.swiglu_quant_fp8(fmt, M, N, K, A, sam, sak, Bg, Bu, sbk,
@@ -298,4 +319,98 @@ def test_swiglu_graph_capture(M):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
+        assert torch.equal(Qg, Qe) and torch.equal(Sg.view(torch.int32), Se.view(torch.int32)), rep
+
+
+# The skinny kernel's split plan (the workspace entry points): K slices of
+# each output slice split over workgroups, the g and u partial sums added in
+# split order before the activation.  (M, N, K, layout, splits, modes): 2
+# splits with a ragged last output slice; a ragged last K slice in the last
+# split; one row, one column past the first slice, padded strides; 4 and 8
+# splits (normal inputs only: the exact recipe needs K <= 1024).
+SPLIT_CASES = [
+    (64, 300, 1024, "nk", 2, (True, False)),
+    (33, 1000, 1000, "nk", 2, (True, False)),
+    (1, 129, 1024, "padded", 2, (True, False)),
+    (64, 7168, 2048, "nk", 4, (False,)),
+    (48, 256, 16384, "nk", 8, (False,)),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}-{c[3]}" for c in SPLIT_CASES])
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_swiglu_split(fmt, case):
+    M, N, K, layout, splits, modes = case
+    _check(fmt, M, N, K, layout, 3900 + M + N + K, f"skinny_64x128_swiglu_q8_splitk{splits}",
+           ws=True, modes=modes)
+
+
+def test_swiglu_split_decode_shape():
+    """The 64 x 16384 x 7168 decode shape with a workspace (K split 2 ways,
+    256 workgroups), every row, within the bound."""
+    M, N, K = 64, 16384, 7168
+    d = configs.swiglu_inputs(M, N, K, 3710)
+    Q, S, plan = _run("bf16", M, N, K, H.dev(d["A"]), K, 1, H.dev(d["Bg"]), H.dev(d["Bu"]), 1, K,
+                      ws=True)
+    assert plan == "skinny_64x128_swiglu_q8_splitk2", plan
+    _, _, Ho, G, U, Sg, Su = oracle.swiglu_quant_fp8("bf16", M, N, K, d["A"], K, 1, d["Bg"],
+                                                     d["Bu"], 1, K)
+    assert_within_err(Q, S, Ho, _h_error(K, G, U, Sg, Su), "decode shape, split, normal")
+
+
+def test_swiglu_split_workspace_reuse():
+    """One workspace through three calls in a row: 2 splits over 56 output
+    slices, then 2 over 3 (a smaller call), then the first again; integer
+    inputs, bit for bit against the oracle, counters zero after each."""
+    fmt = "bf16"
+    big, small = (64, 7168, 1024), (40, 300, 1024)
+    ws = None
+    for i, (M, N, K) in enumerate((big, small, big)):
+        A, sam, sak, Bg, Bu, sbk, sbn = _operands(fmt, M, N, K, "nk", 4000 + i, True)
+        if ws is None:
+            nb = -(-N // 128)
+            ws = H.Workspace(tg.tg_gemm_swiglu_quant_fp8_workspace_size(
+                1, M, N, K, 0x100, sam, sak, 0x200, 0x300, sbk, sbn, 0x400, N, 0x500, nb, 1))
+            assert ws.nbytes == 16384 + 56 * 2 * 64 * 1024
+        Q, S, plan = _run(fmt, M, N, K, H.dev(A), sam, sak, H.dev(Bg), H.dev(Bu), sbk, sbn, ws=ws)
+        assert plan.startswith("skinny_64x128_swiglu_q8_splitk"), plan
+        Qo, So, Ho, G, U, _, _ = oracle.swiglu_quant_fp8(fmt, M, N, K, A, sam, sak, Bg, Bu, sbk,
+                                                         sbn)
+        assert G.min() >= GATE_MIN and np.abs(Ho).max() < 2.0 ** 24 and np.array_equal(Ho, G * U)
+        assert_exact(Q, S, Qo, So, f"workspace reuse {i} [{plan}]")
+
+
+def test_swiglu_split_graph_capture():
+    """The split plan under graph capture: the kernel clears its own counters,
+    so replays (with eager calls on the same workspace in between) give the
+    eager codes and scales bit for bit."""
+    M, N, K = 48, 512, 2048
+    A, sam, sak, Bg, Bu, sbk, sbn = _operands("bf16", M, N, K, "nk", 4100, False)
+    Ad, Bgd, Bud = H.dev(A), H.dev(Bg), H.dev(Bu)
+    nb = -(-N // 128)
+    Q = torch.zeros((M, N), dtype=torch.uint8, device="cuda")
+    S = torch.zeros((M, nb), dtype=torch.float32, device="cuda")
+    args = lambda q, s: (M, N, K, Ad.data_ptr(), sam, sak, Bgd.data_ptr(), Bud.data_ptr(),  # noqa
+                         sbk, sbn, q.data_ptr(), N, s.data_ptr(), nb, 1)
+    ws = H.Workspace(tg.tg_gemm_swiglu_quant_fp8_workspace_size(1, *args(Q, S)))
+    plan = tg.tg_gemm_swiglu_quant_fp8_plan_ws(1, *args(Q, S), ws.nbytes)
+    assert plan == "skinny_64x128_swiglu_q8_splitk4", plan
+    H.log(f"swiglu split graph capture M={M} N={N} K={K} [{plan}]")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        tg.tg_gemm_bf16_swiglu_quant_fp8_ws(*args(Q, S), ws.ptr, ws.nbytes, stream.cuda_stream)
+    stream.synchronize()
+    Qe, Se = Q.clone(), S.clone()
+    Qg, Sg = torch.zeros_like(Q), torch.zeros_like(S)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        tg.tg_gemm_bf16_swiglu_quant_fp8_ws(*args(Qg, Sg), ws.ptr, ws.nbytes, stream.cuda_stream)
+    for rep in range(3):
+        Qg.fill_(0x5A)
+        Sg.fill_(-7.0)
+        _run("bf16", M, N, K, Ad, sam, sak, Bgd, Bud, sbk, sbn, ws=ws)  # eager work in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert ws.counters_zero(), rep
         assert torch.equal(Qg, Qe) and torch.equal(Sg.view(torch.int32), Se.view(torch.int32)), rep
