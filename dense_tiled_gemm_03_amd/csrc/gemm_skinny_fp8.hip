@@ -524,13 +524,14 @@ __global__ __launch_bounds__(256) void gemm_fp8_skinny_split(GemmArgs a, int spl
 // Splits of the K blocks: about one workgroup per CU, each with at least
 // kMinBlocks blocks; 1 (no split plan) where the strip kernel is as fast.
 // Both kernels stream the same B bytes per CU; the split saves A bytes and
-// fills the CUs when the strip grid does not, but pays the combine of the
-// partial tiles.  It is taken for more than 32 rows (with fewer, A is
-// small and the strip kernel keeps more of B in flight) when the strip grid
-// is not one nearly full round (kStripRoundMin .. 256 workgroups) or each
-// split has at least kAmortBlocks blocks to amortise the combine.
-constexpr int kStripRoundMin = 192;
-constexpr int kAmortBlocks = 24;
+// fills the CUs when the strip grid does not, but pays a fixed cost for the
+// combine of the partial tiles that grows with the splits.  It is taken, as
+// measured, for more than 32 rows (with fewer, A is small and the strip
+// kernel keeps more of B in flight) when each strip workgroup has a long
+// run of K blocks (strip rounds x blocks >= kLongBlocks), or when the strip
+// grid fills at most half the CUs and K has at least kHalfGridBlocks blocks.
+constexpr int kLongBlocks = 96;
+constexpr int kHalfGridBlocks = 56;
 int choose_splits(const GemmArgs& a) {
   if (a.M <= 32) return 1;
   const int64_t strips = cdiv(a.N, XN), nkb = cdiv(a.K, FK);
@@ -538,9 +539,9 @@ int choose_splits(const GemmArgs& a) {
   if (sp > nkb / kMinBlocks) sp = nkb / kMinBlocks;
   if (sp < 2) return 1;
   const int64_t strip_wgs = cdiv(a.N, FN_);
-  const bool full_round = strip_wgs >= kStripRoundMin && strip_wgs <= kCus;
-  if (full_round && nkb / sp < kAmortBlocks) return 1;
-  return (int)sp;
+  const bool long_strips = cdiv(strip_wgs, kCus) * nkb >= kLongBlocks;
+  const bool half_grid = strip_wgs <= kCus / 2 && nkb >= kHalfGridBlocks;
+  return long_strips || half_grid ? (int)sp : 1;
 }
 
 // The split plan's scratch: a counter per strip in the fixed counter area,

@@ -490,18 +490,21 @@ def test_fp8_tile_plans(lib, case):
 
 # The fp8 decode product with a workspace: 64 x 128 strips, the K blocks
 # split so that strips x splits stays within 256 workgroups, with at least 4
-# blocks per split -- for more than 32 rows, where the strip grid is not one
-# nearly full round (192 .. 256 workgroups of 32 columns) or each split gets
-# at least 24 blocks.  Otherwise (and for M > 64, or K not a multiple of 16)
-# the plan without workspace.
+# blocks per split -- for more than 32 rows, where the strip grid's rounds
+# times the K blocks reach 96, or the strip grid (32-column strips) fills at
+# most half the CUs and K has at least 56 blocks.  Otherwise (and for M > 64,
+# or K not a multiple of 16) the plan without workspace.
 FP8_WS_PLANS = [
-    ((64, 7168, 16384), "skinny_fp8_64x128_splitk4"),    # 224 strip workgroups, 32 blocks per split
-    ((33, 7168, 18432), "skinny_fp8_64x128_splitk4"),    # 36 blocks per split
-    ((64, 16384, 7168), "skinny_fp8_64x128_splitk2"),    # 512 strip workgroups: 2 rounds
-    ((40, 1000, 4096), "skinny_fp8_64x128_splitk8"),     # 32 strip workgroups; 8 strips, 32 blocks
-    ((64, 2048, 2048), "skinny_fp8_64x128_splitk4"),     # 16 strips, 16 blocks
-    ((48, 300, 1024), "skinny_fp8_64x128_splitk2"),      # 3 strips, 8 blocks
-    ((64, 7168, 7168), "skinny_fp8_64x32"),              # one full round, 14 blocks per split
+    ((64, 7168, 16384), "skinny_fp8_64x128_splitk4"),    # 1 round x 128 blocks
+    ((33, 7168, 18432), "skinny_fp8_64x128_splitk4"),    # 1 round x 144 blocks
+    ((64, 16384, 7168), "skinny_fp8_64x128_splitk2"),    # 2 rounds x 56 blocks
+    ((48, 8192, 12288), "skinny_fp8_64x128_splitk4"),    # 1 round x 96 blocks
+    ((40, 4096, 7168), "skinny_fp8_64x128_splitk8"),     # 128 strip workgroups, 56 blocks
+    ((64, 2048, 7168), "skinny_fp8_64x128_splitk"),      # 64 strip workgroups: 14 splits
+    ((64, 4096, 6144), "skinny_fp8_64x32"),              # half grid, but 48 blocks
+    ((64, 7168, 7168), "skinny_fp8_64x32"),              # 1 round x 56 blocks
+    ((64, 4096, 4096), "skinny_fp8_64x32"),              # half grid, but 32 blocks
+    ((64, 1024, 4096), "skinny_fp8_64x32"),
     ((32, 16384, 7168), "skinny_fp8_64x32"),             # 32 rows
     ((1, 7168, 16384), "skinny_fp8_64x32"),
     ((64, 32768, 7168), "skinny_fp8_64x32"),             # 256 strips: no split
@@ -524,7 +527,8 @@ def test_fp8_workspace_plans(lib, case):
         assert plain == "skinny_fp8_64x32"
         assert tg.tg_gemm_plan_ws(*args, need - 1) == plain
         assert tg.tg_gemm_plan_ws(*args, 0) == plain
-        strips, splits = -(-N // 128), int(want.rsplit("splitk", 1)[1])
+        strips = -(-N // 128)
+        splits = int(want.rsplit("splitk", 1)[1] or 14)    # the names go to splitk8
         assert need == 16384 + strips * splits * 64 * 128 * 4
 
 

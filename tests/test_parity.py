@@ -775,15 +775,16 @@ def test_fp8_skinny(case):
 
 # The split plan of the fp8 decode product (a caller's workspace): 64 x 128
 # strips over ranges of the K blocks, partial tiles added in split order; it
-# runs for 33 .. 64 rows where the strip grid is not one nearly full round or
-# the splits are long.  Cases: a 64 x 7168 x 16384 down projection (4
-# splits); 64 x 16384 x 7168 (2 splits); a ragged last strip and a ragged
-# last K block in the last split (33 x 300 x 1040: 9 blocks in 2 splits); one
-# partial strip with 8 uneven splits (40 x 40 x 4112: 33 blocks); 16 splits,
-# summed four at a time (48 x 100 x 8192); 14 splits (64 x 2048 x 7168); a
-# 2-column strip in the second B scale block; 63 rows of a 16-column strip.
-FP8_SPLIT_CASES = [(64, 7168, 16384), (64, 16384, 7168), (33, 300, 1040), (40, 40, 4112),
-                   (48, 100, 8192), (64, 2048, 7168), (64, 130, 2048), (63, 16, 1024)]
+# runs for 33 .. 64 rows with long strips or half-empty strip grids.  Cases:
+# a 64 x 7168 x 16384 down projection (4 splits); 64 x 16384 x 7168 (2
+# splits); 8 splits (40 x 4096 x 7168); a ragged last strip and a ragged
+# last K block in the last of 14 splits (33 x 300 x 7184: 57 blocks); one
+# partial strip with 14 splits; 16 splits, summed four at a time (48 x 100 x
+# 8192); 14 splits over 16 strips (64 x 2048 x 7168); a 2-column strip in
+# the second B scale block; 63 rows of a 16-column strip.
+FP8_SPLIT_CASES = [(64, 7168, 16384), (64, 16384, 7168), (40, 4096, 7168), (33, 300, 7184),
+                   (40, 40, 7184), (48, 100, 8192), (64, 2048, 7168), (64, 130, 7168),
+                   (63, 16, 7168)]
 
 
 @pytest.mark.parametrize("case", FP8_SPLIT_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in FP8_SPLIT_CASES])
@@ -806,7 +807,7 @@ def test_fp8_split_workspace_reuse():
     ws = H.Workspace(H.tg.tg_gemm_workspace_size(H.tg.OP_FP8, M0, N0, K0, 0x100, K0, 1, 0x200, 1,
                                                  K0, 0x300, N0, 1))
     assert ws.nbytes == 16384 + 56 * 4 * 64 * 128 * 4
-    for i, (M, N, K) in enumerate((big, (33, 300, 1040), big)):
+    for i, (M, N, K) in enumerate((big, (33, 300, 7184), big)):
         plan = _check_fp8(M, N, K, _fp8_inputs(M, N, K, 2500 + i, int_r=16), exact=True,
                           what=f"split reuse {i}", ws=ws)
         assert plan.startswith("skinny_fp8_64x128_splitk"), plan
@@ -815,7 +816,7 @@ def test_fp8_split_workspace_reuse():
 def test_fp8_split_padded_c():
     """The split plan storing into C rows padded by 40 elements, behind guard
     bands, with B stored K x N-contiguous rows padded (sbn = K + 32)."""
-    M, N, K = 40, 300, 2048
+    M, N, K = 40, 300, 7168
     d = _fp8_inputs(M, N, K, 2600, int_r=16)
     assert (d["sbk"], d["sbn"]) == (1, K)
     Bp = np.zeros((N, K + 32), np.uint8)
@@ -823,7 +824,7 @@ def test_fp8_split_padded_c():
     nkb = d["SA"].shape[1]
     c, plan = H.run_fp8(M, N, K, H.dev(d["A"]), K, 1, H.dev(d["SA"]), nkb, 1, H.dev(Bp),
                         1, K + 32, H.dev(d["SB"]), nkb, 1, scm=N + 40, ws=True)
-    assert plan == "skinny_fp8_64x128_splitk4", plan
+    assert plan == "skinny_fp8_64x128_splitk", plan     # 14 splits
     C_ref, _ = oracle.gemm_fp8_blockscaled(M, N, K, d["A"], K, 1, d["SA"], nkb, 1, Bp, 1, K + 32,
                                            d["SB"], nkb, 1)
     H.assert_bit_exact("bf16", c, C_ref, f"fp8 split, padded C [{plan}]")
