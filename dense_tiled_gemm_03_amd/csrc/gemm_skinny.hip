@@ -510,24 +510,37 @@ int choose_splits(const GemmArgs& a) {
   return s < 1 ? 1 : (int)s;
 }
 
+// Whether the split plan beats the 32-column strips over all of K (both
+// stream the same B bytes per CU; the split saves A bytes and fills the CUs
+// when the strip grid does not, but pays a fixed cost for the combine).  As
+// measured: when each strip workgroup has a long run of K slices (strip
+// rounds x slices >= 96), or when the strip grid fills at most half the
+// CUs.  Short K on a full strip grid (64 x 7168 x 2048: 15.8 us split
+// against 11.1) stays on the strips.
+constexpr int kLongSlices = 96;
+bool split_pays(const GemmArgs& a) {
+  const int64_t strip_wgs = cdiv(a.N, WN), nk = cdiv(a.K, SK);
+  return cdiv(strip_wgs, kCus) * nk >= kLongSlices || strip_wgs <= kCus / 2;
+}
+
 // Scratch of the split plan: one counter per strip in the fixed counter
 // area, then each split's 64 x 128 fp32 partial tile (0: no split).
 size_t scratch_bytes(const GemmArgs& a) {
   const int64_t strips = cdiv(a.N, SN);
   const int splits = choose_splits(a);
-  if (splits == 1 || strips > kWorkspaceCounters) return 0;
+  if (splits == 1 || !split_pays(a) || strips > kWorkspaceCounters) return 0;
   return kWorkspaceCounterBytes + (size_t)strips * splits * SM * SN * 4;
 }
 
-// Plans: with scratch for the split, 64 x 128 strips split K across
-// workgroups; without it, 32-column strips over all of K (waves split each
-// slice); when no split is wanted (short K, or enough strips), 64 x 128
-// strips unsplit.
+// Plans: with scratch for the split where it pays, 64 x 128 strips split K
+// across workgroups; otherwise 32-column strips over all of K (waves split
+// each slice); when K is too short to split or the strips alone fill the
+// CUs, 64 x 128 strips unsplit.
 enum class Skinny { Strip128, Split128, Strip32 };
 Skinny choose(const GemmArgs& a, const Scratch& ws, int& splits) {
   splits = choose_splits(a);
   if (splits == 1) return Skinny::Strip128;
-  if (scratch_fits(ws, scratch_bytes(a))) return Skinny::Split128;
+  if (split_pays(a) && scratch_fits(ws, scratch_bytes(a))) return Skinny::Split128;
   splits = 1;
   return Skinny::Strip32;
 }

@@ -532,6 +532,36 @@ def test_fp8_workspace_plans(lib, case):
         assert need == 16384 + strips * splits * 64 * 128 * 4
 
 
+# The 16-bit skinny product with a workspace: its split plan where it pays --
+# the strip grid's rounds times the K slices (64 wide) reach 96, or the
+# strip grid (32-column strips) fills at most half the CUs; otherwise the
+# allocation-free 32-column strips.
+BF16_WS_PLANS = [
+    ((64, 7168, 7168), "skinny_64x128_splitk4"),     # 1 round x 112 slices
+    ((1, 7168, 7168), "skinny_64x128_splitk4"),
+    ((64, 16384, 7168), "skinny_64x128_splitk2"),    # 2 rounds x 112
+    ((64, 7168, 16384), "skinny_64x128_splitk4"),
+    ((64, 4096, 4096), "skinny_64x128_splitk8"),     # 128 strip workgroups
+    ((64, 1024, 4096), "skinny_64x128_splitk8"),
+    ((64, 7168, 4096), "skinny_64x32"),              # 1 round x 64 slices
+    ((64, 7168, 2048), "skinny_64x32"),              # 1 round x 32 slices
+    ((40, 7168, 1024), "skinny_64x32"),
+    ((64, 7168, 520), "skinny_64x128"),              # 9 slices: too short to split
+]
+
+
+@pytest.mark.parametrize("case", BF16_WS_PLANS, ids=[f"{m}x{n}x{k}" for (m, n, k), _ in BF16_WS_PLANS])
+def test_bf16_skinny_workspace_plans(lib, case):
+    (M, N, K), want = case
+    args = (tg.OP_BF16, M, N, K, PA, K, 1, PB, 1, K, PC, N, 1)
+    need = _ws_bytes(tg.OP_BF16, M, N, K, 1, K)
+    assert tg.tg_gemm_plan_ws(*args, 1 << 40) == want
+    assert (need > 0) == ("splitk" in want)
+    if need:
+        assert tg.tg_gemm_plan_ws(*args, need) == want
+        assert tg.tg_gemm_plan_ws(*args, need - 1) == tg.tg_gemm_plan(*args) == "skinny_64x32"
+
+
 def test_workspace_sizes(lib):
     """The split plans' scratch: a 16 KiB counter area, then 4 bytes per
     element of each split's partial tile."""
