@@ -420,14 +420,17 @@ int64_t grid_of(const Call& c, Path p) {
 // Splits of the skinny kernel's K slices with a workspace: about one
 // workgroup per CU, at least 8 slices and at most 8 splits (the last
 // workgroup of a slice reads every split's 64 KiB of partial tiles); 1: no
-// split plan.
+// split plan.  When the output slices already fill half the CUs and a split
+// would get fewer than 16 K slices, the combine costs more than the second
+// half of the CUs gains (64 x 16384 x 1024: 33.3 us split against 30.1).
 constexpr int kCus = 256;
 int choose_splits(const Call& c) {
   const int64_t slices = cdiv(c.a.N, DN), nk = cdiv(c.a.K, DK);
   int64_t sp = kCus / slices;
   if (sp > nk / 8) sp = nk / 8;
   if (sp > 8) sp = 8;
-  return sp < 2 ? 1 : (int)sp;
+  if (sp < 2 || (slices > kCus / 4 && nk / sp < 16)) return 1;
+  return (int)sp;
 }
 
 // Workspace of the split plan: a counter per slice in the fixed counter

@@ -211,7 +211,8 @@ def test_swiglu_invalid(lib, name, kw):
 
 # The fused SwiGLU's split plan (with a workspace): the K slices of each
 # 128-column output slice split so that slices x splits stays within 256
-# workgroups, with at least 8 slices per split and at most 8 splits;
+# workgroups, with at least 8 slices per split and at most 8 splits, and
+# none for more than 64 output slices with fewer than 16 K slices per split;
 # 64 KiB of g and u partial tiles per slice and split after the 16 KiB of
 # counters.
 SWIGLU_WS_PLANS = [
@@ -221,6 +222,9 @@ SWIGLU_WS_PLANS = [
     ((64, 256, 16384), 8),      # 2 slices, capped at 8 splits
     ((33, 200, 1040), 2),       # 17 K slices
     ((64, 32768, 7168), 1),     # 256 slices: no split
+    ((64, 16384, 1024), 1),     # 128 slices, 2 splits would get 8 K slices each
+    ((64, 16384, 2048), 2),     # 16 K slices per split
+    ((16, 7168, 2048), 4),      # 56 slices
     ((8, 300, 64), 1),          # one K slice
 ]
 
