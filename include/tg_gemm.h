@@ -113,7 +113,9 @@ tg_status tg_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
 /* The same products with a caller-owned workspace, for the plans that split
  * K across the workgroups of an output tile and add their fp32 partial
  * tiles in split order (deterministic): products with M <= 64 (64 x 128
- * strips of C, K split so that there is about one workgroup per CU), grids
+ * strips of C, K split so that there is about one workgroup per CU -- where
+ * that beats 32-column strips over all of K: a long K run per strip, or a
+ * strip grid that fills at most half the CUs), grids
  * of output tiles that would fill at most half the CUs (one GPU's share of
  * a larger product, e.g. 4096 x 896 x 16384: 256 x 224 tiles, K split 4
  * ways), and grids of one whole wave of 256 x 224 tiles and a partial one
@@ -155,7 +157,9 @@ tg_status tg_gemm_bf16_ws(int64_t M, int64_t N, int64_t K,
  * step over fp8 weights): 64 x 128 strips of C, the K blocks split so that
  * there is about one workgroup per CU, each split's block sums folded in
  * with SA * SB as in tg_gemm_fp8_blockscaled and the fp32 partial tiles
- * added in split order.  Without workspace (or too little) it runs exactly
+ * added in split order.  It runs for M > 32 where it beats the strips (a
+ * long K run per strip, or a strip grid of at most half the CUs with K of at
+ * least 56 blocks); tg_gemm_workspace_size is 0 elsewhere.  Without workspace (or too little) it runs exactly
  * as tg_gemm_fp8_blockscaled.  Results: within the same bound, bit for bit
  * equal when every fp32 partial sum is exact.  Errors: those of
  * tg_gemm_fp8_blockscaled, plus TG_ERR_INVALID_VALUE for workspace_bytes > 0
